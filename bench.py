@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged FP8-e4m3 KV-cache decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the batched page-tag
+check, then for each layer the quantize-on-append of every request's new
+token and split-K paged decode attention (dequantize on read, online softmax,
+cross-partition reduction). Inputs are seeded synthetic tensors already
+resident in HBM when the timed region starts.
+
+Default workload (the headline point): batch 64, contexts 8192 + U{0..1000}
+tokens, 64 query / 8 KV heads, head_dim 128, page 16, 8 layers each with its
+own pool, FP8 e4m3 cache, tag check on every step.
+
+Prints ONE JSON line. ``value`` is the algorithmic HBM throughput of the
+whole step in GB/s; ``seq_steps_per_s`` is batch * steps / time. The
+``roofline`` object is the attention kernel measured alone with HIP events
+on its launch stream; ``cpu_baseline`` is the CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4", choices=["c3", "c4", "c5"])
+    ap.add_argument("--cache", default="fp8", choices=["fp8", "bf16"])
+    ap.add_argument("--verify", default="on", choices=["on", "off"])
+    ap.add_argument("--partition-tokens", type=int, default=-1,
+                    help="split-K partition size; -1 = the workload's own (0 = automatic)")
+    ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle sample")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (what the method must move), per step
+# ---------------------------------------------------------------------------
+def step_bytes(wl, seq_lens, cache, verify):
+    """Bytes one step must read or write, split by operation."""
+    import numpy as np
+    B, Hq, Hkv, D, P = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size
+    esz = 1 if cache == "fp8" else 2
+    L = seq_lens.astype(np.int64)
+    pages = -(-L // P)
+    kv_read = int(L.sum()) * 2 * Hkv * D * esz                 # K and V of every token
+    attn_io = B * Hq * D * 2 + B * Hq * D * 4 + int(pages.sum()) * 4 + B * 4
+    append = B * Hkv * D * 2 * 2 + B * Hkv * D * 2 * esz + B * 12
+    check = int(pages.sum()) * 12 + B * 5 if verify else 0
+    per_layer_attn = kv_read + attn_io
+    total = check + wl.num_layers * (per_layer_attn + append)
+    return dict(total=total, attn_per_layer=per_layer_attn, kv_per_layer=kv_read,
+                append_per_layer=append, check=check)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle leg (bounded sample)
+# ---------------------------------------------------------------------------
+def cpu_baseline(args, wl, scales, step_index):
+    """Time the oracle's step work (tag check, append, attention) for a few
+    requests of layer 0 on this host; scale to sequence-steps per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import e4m3, paged
+
+    P = wl.page_size
+    ks, vs = scales
+    order = np.argsort(wl.seq_lens0)[::-1]          # longest first, then shortest
+    sample_reqs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    prepared = []
+    for b in sample_reqs:
+        L0 = int(wl.seq_lens0[b]) + step_index          # tokens already in the pool
+        L = L0 + 1
+        n = -(-L // P)
+        k = e4m3.quantize(wl.kv_bits(0, "k", b, 0, L0), ks[None, :, None])
+        v = e4m3.quantize(wl.kv_bits(0, "v", b, 0, L0), vs[None, :, None])
+        kp = np.zeros((n, wl.num_kv_heads, P, wl.head_dim), np.uint8)
+        vp = np.zeros_like(kp)
+        for j in range(n):
+            m = max(0, min(P, L0 - j * P))
+            kp[j, :, :m] = k[j * P:j * P + m].transpose(1, 0, 2)
+            vp[j, :, :m] = v[j * P:j * P + m].transpose(1, 0, 2)
+        bt = np.arange(n, dtype=np.int32)[None, :]
+        tags = np.arange(n, dtype=np.uint32)
+        q = wl.q_bits(0, step_index)[b:b + 1]
+        kn = wl.kv_bits(0, "k", b, L0, L)
+        vn = wl.kv_bits(0, "v", b, L0, L)
+        prepared.append((b, L, kp, vp, bt, tags, q, kn, vn))
+    sm = 1.0 / math.sqrt(wl.head_dim)
+    done, t_total, per_req = 0, 0.0, []
+    with threadpool_limits(limits=1):
+        while t_total < args.cpu_seconds and done < 64:
+            for (b, L, kp, vp, bt, tags, q, kn, vn) in prepared:
+                kp2, vp2 = kp.copy(), vp.copy()
+                t0 = time.perf_counter()
+                ab = paged.verify_tags(tags, bt, tags[None, :], np.array([L]), P)
+                paged.append_fp8(kp2, vp2, kn, vn, np.array([0]), np.array([L - 1]), bt, ks,
+                                 vs, ab)
+                paged.decode_attn(q, kp2, vp2, ks, vs, bt, np.array([L], np.int32), sm,
+                                  "fp8", ab)
+                dt = time.perf_counter() - t0
+                t_total += dt
+                per_req.append((L, dt))
+                done += 1
+    tok = sum(L for L, _ in per_req)
+    sec = sum(dt for _, dt in per_req)
+    # one sequence-step = every layer of one request; scale by mean context
+    mean_L = float(wl.seq_lens0.mean()) + step_index + 1
+    sec_per_seq_step = wl.num_layers * (sec / tok) * mean_L
+    return {
+        "value": 1.0 / sec_per_seq_step,
+        "unit": "seq-steps/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} oracle (tag check + append + attention) runs of layer 0 for "
+                   f"requests {sample_reqs} (lengths {sorted(set(L for L, _ in per_req))}), "
+                   f"{sec:.1f} s of CPU on 1 thread (host has {os.cpu_count()} cpus); "
+                   f"scaled by {wl.num_layers} layers and mean context {mean_L:.0f}"),
+        "effective_GBps": None,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_e4m3_paged_amd as kv
+    import synth
+    from synth import device as sd
+
+    kv.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    total_steps = args.warmup + args.steps
+    make = {"c3": synth.c3_uniform, "c4": synth.c4_headline, "c5": synth.c5_skewed}[args.config]
+    wl = make(max_steps=total_steps)
+    pt = wl.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
+    verify = args.verify == "on"
+    cache = args.cache
+    fp8 = cache == "fp8"
+    log(args, f"workload {wl.name}: B={wl.batch} layers={wl.num_layers} pages={wl.num_pages} "
+              f"mean L0={wl.seq_lens0.mean():.0f} cache={cache} verify={verify}")
+
+    t0 = time.time()
+    st = sd.DeviceState(wl, kv, cache=cache, device=dev)
+    torch.cuda.synchronize()
+    log(args, f"pools filled in {time.time() - t0:.1f} s")
+
+    # per-step inputs, made on the device before timing
+    seq_lens = [st.seq_lens(s).contiguous() for s in range(total_steps)]
+    tok_pos = [st.tok_pos(s).contiguous() for s in range(total_steps)]
+    inputs = []
+    for s in range(total_steps):
+        per = []
+        for layer in range(wl.num_layers):
+            per.append((sd.q_bits_device(wl, layer, s, dev),
+                        sd.new_token_bits_device(wl, layer, "k", s, dev),
+                        sd.new_token_bits_device(wl, layer, "v", s, dev)))
+        inputs.append(per)
+    outs = [torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+            for _ in range(wl.num_layers)]
+    max_len = wl.max_seq_len
+    pt_eff = kv.paged_decode_attn_partition_tokens(wl.batch, wl.num_kv_heads, max_len, pt)
+    ws_n = kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads,
+                                                max_len, pt)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+    cd = kv.KV_CACHE_FP8_E4M3 if fp8 else kv.KV_CACHE_BF16
+    sm = 1.0 / math.sqrt(wl.head_dim)
+    stream = torch.cuda.current_stream()
+    abort = st.abort if verify else None
+
+    ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps * wl.num_layers)]
+
+    def run_step(s, timed_slot=None):
+        if verify:
+            kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens[s],
+                              st.abort, stream=stream)
+        for layer in range(wl.num_layers):
+            q, kn, vn = inputs[s][layer]
+            if fp8:
+                kv.kv_append_quant(kn, vn, st.tok_seq, tok_pos[s], st.block_table,
+                                   st.k_scale[layer], st.v_scale[layer], st.k_pool[layer],
+                                   st.v_pool[layer], abort=abort, stream=stream)
+            else:
+                kv.kv_append_bf16(kn, vn, st.tok_seq, tok_pos[s], st.block_table,
+                                  st.k_pool[layer], st.v_pool[layer], abort=abort, stream=stream)
+            if timed_slot is not None:
+                ev_attn[timed_slot + layer][0].record(stream)
+            kv.paged_decode_attn(q, st.k_pool[layer], st.v_pool[layer], st.k_scale[layer],
+                                 st.v_scale[layer], st.block_table, seq_lens[s], max_len,
+                                 outs[layer], sm, workspace=ws, abort=abort,
+                                 partition_tokens=pt, cache_dtype=cd, stream=stream)
+            if timed_slot is not None:
+                ev_attn[timed_slot + layer][1].record(stream)
+
+    for s in range(args.warmup):
+        run_step(s)
+    torch.cuda.synchronize()
+    if verify:
+        assert int(st.abort.sum().item()) == 0, "no request of this workload may abort"
+    log(args, f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        run_step(args.warmup + i, timed_slot=i * wl.num_layers)
+    end.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(end)
+    ms_per_step = elapsed_ms / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev_attn]
+    attn_avg_ms = float(np.mean(attn_ms))
+
+    by = [step_bytes(wl, wl.seq_lens_at(args.warmup + i), cache, verify)
+          for i in range(args.steps)]
+    total_bytes = sum(b["total"] for b in by)
+    gbs = total_bytes / (elapsed_ms * 1e-3) / 1e9
+    attn_bytes = float(np.mean([b["attn_per_layer"] for b in by]))
+    attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    seq_steps = wl.batch * args.steps / (elapsed_ms * 1e-3)
+    log(args, f"{ms_per_step:.3f} ms/step, {gbs:.0f} GB/s, attention call {attn_avg_ms*1e3:.1f} us "
+              f"= {attn_gbs:.0f} GB/s")
+
+    cpu = None
+    if args.cpu_baseline == "on" and fp8:
+        log(args, "timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(args, wl, (st.k_scale_host[0], st.v_scale_host[0]), args.warmup)
+        sec_per_seq_step = 1.0 / cpu["value"]
+        mean_bytes_per_seq_step = total_bytes / args.steps / wl.batch
+        cpu["effective_GBps"] = mean_bytes_per_seq_step / sec_per_seq_step / 1e9
+
+    result = {
+        "metric": "paged FP8-KV decode attn: achieved HBM GB/s + seq-steps/s at B=64, ctx=8k",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "seq_steps_per_s": round(seq_steps, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: batch {wl.batch}, ctx 8192+U[0,1000]"
+                         if wl.name == "c4_headline" else wl.name),
+            "batch": wl.batch, "layers": wl.num_layers, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "page_size": wl.page_size, "mean_ctx": round(float(wl.seq_lens0.mean()) + 1, 1),
+            "cache": cache, "verify": verify, "partition_tokens": pt_eff,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_attn (partition kernel + cross-partition reduce)",
+            "achieved": round(attn_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(attn_avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(attn_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,270 @@
+"""Python binding of libkvfp8.so: paged FP8-e4m3 KV-cache decode on MI355X.
+
+A thin ctypes layer over the C ABI declared in include/kvfp8.h. Each function
+takes torch tensors that already live on the GPU, checks their dtypes and
+shapes, and passes raw device pointers plus the current HIP stream of torch.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback: if the shared library is not built, importing this package still
+works but the first call raises ``KvLibraryMissing``.
+
+Entry points (same names as the C ABI):
+    kv_verify_tags, kv_append_quant, kv_append_bf16, paged_decode_attn,
+    paged_decode_attn_workspace_bytes, paged_decode_attn_partition_tokens,
+    kv_status_str
+plus ``decode_step``, which enqueues one decode step (tag check, then per
+layer append and attention) in the order the operations require.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "KV_CACHE_FP8_E4M3", "KV_CACHE_BF16", "KvError", "KvLibraryMissing", "lib_path",
+    "load", "kv_status_str", "kv_verify_tags", "kv_append_quant", "kv_append_bf16",
+    "paged_decode_attn", "paged_decode_attn_workspace_bytes",
+    "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
+]
+
+KV_CACHE_FP8_E4M3 = 0
+KV_CACHE_BF16 = 1
+PAGE_SIZE = 16
+HEAD_DIM = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class KvError(RuntimeError):
+    """A C-ABI call returned a negative kv_status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {kv_status_str(status)} ({status})")
+
+
+class KvLibraryMissing(RuntimeError):
+    """libkvfp8.so has not been built (python -m fp8_e4m3_paged_amd.build)."""
+
+
+def lib_path() -> str:
+    return os.environ.get("KVFP8_LIB", os.path.join(_HERE, "libkvfp8.so"))
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "kv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "kv_verify_tags": (ctypes.c_int, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P]),
+    "kv_append_quant": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _I,
+                                       _I, _I, _I, _P, _P]),
+    "kv_append_bf16": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I,
+                                      _I, _P, _P]),
+    "paged_decode_attn_partition_tokens": (ctypes.c_int32, [_I, _I, _I, _I]),
+    "paged_decode_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "paged_decode_attn": (ctypes.c_int, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P,
+                                         ctypes.c_float, _I, _I, _I, _I, _I, _I, _I, _P,
+                                         ctypes.c_size_t, _P]),
+}
+
+
+def load():
+    """Load libkvfp8.so once and declare the C signatures."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise KvLibraryMissing(
+                f"{path} not found; build it with `python -m fp8_e4m3_paged_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def kv_status_str(status: int) -> str:
+    return load().kv_status_str(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t, name, dtypes=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise KvError(fn, status)
+
+
+def _dt():
+    import torch
+    return dict(
+        i32=(torch.int32,), u32=(torch.int32, torch.uint32), u8=(torch.uint8,),
+        bf16=(torch.bfloat16, torch.int16, torch.uint16), f32=(torch.float32,),
+        pool=(torch.uint8, torch.int16, torch.bfloat16, torch.uint16),
+    )
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def kv_verify_tags(pool_tags, block_table, expected_tags, seq_lens, abort_out,
+                   page_size=PAGE_SIZE, stream=None):
+    """abort_out[b] = 1 iff request b's recorded (page, tag) pairs disagree with the pool."""
+    d = _dt()
+    batch = seq_lens.numel()
+    if block_table.dim() != 2 or expected_tags.shape != block_table.shape:
+        raise ValueError("block_table / expected_tags must be [batch][bt_stride] alike")
+    if block_table.shape[0] != batch or abort_out.numel() != batch:
+        raise ValueError("batch mismatch")
+    st = load().kv_verify_tags(_ptr(pool_tags, "pool_tags", d["u32"]), pool_tags.numel(),
+                               _ptr(block_table, "block_table", d["i32"]),
+                               _ptr(expected_tags, "expected_tags", d["u32"]),
+                               block_table.shape[1], _ptr(seq_lens, "seq_lens", d["i32"]),
+                               batch, page_size, _ptr(abort_out, "abort_out", d["u8"]),
+                               _stream(stream))
+    _check("kv_verify_tags", st)
+
+
+def _append(fp8, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool, v_pool,
+            abort=None, batch=None, page_size=PAGE_SIZE, stream=None):
+    d = _dt()
+    n_tok = tok_seq.numel()
+    if tok_pos.numel() != n_tok:
+        raise ValueError("tok_seq / tok_pos length mismatch")
+    if k_new.dim() != 3 or k_new.shape != v_new.shape or k_new.shape[0] != n_tok:
+        raise ValueError("k_new / v_new must be [n_tok][num_kv_heads][head_dim]")
+    hkv, hd = k_new.shape[1], k_new.shape[2]
+    if k_pool.shape[:2] != v_pool.shape[:2] or k_pool.shape[1] != hkv:
+        raise ValueError("pools must be [num_pages][num_kv_heads][...]")
+    num_pages = k_pool.shape[0]
+    if batch is None:
+        batch = block_table.shape[0]
+    lib = load()
+    if fp8:
+        st = lib.kv_append_quant(
+            _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
+            _ptr(tok_seq, "tok_seq", d["i32"]), _ptr(tok_pos, "tok_pos", d["i32"]), n_tok,
+            _ptr(block_table, "block_table", d["i32"]), block_table.shape[1], batch,
+            _ptr(k_scale, "k_scale", d["f32"]), _ptr(v_scale, "v_scale", d["f32"]),
+            _ptr(k_pool, "k_pool", d["u8"]), _ptr(v_pool, "v_pool", d["u8"]), num_pages, hkv,
+            hd, page_size, _ptr(abort, "abort", d["u8"], allow_none=True), _stream(stream))
+        _check("kv_append_quant", st)
+    else:
+        st = lib.kv_append_bf16(
+            _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
+            _ptr(tok_seq, "tok_seq", d["i32"]), _ptr(tok_pos, "tok_pos", d["i32"]), n_tok,
+            _ptr(block_table, "block_table", d["i32"]), block_table.shape[1], batch,
+            _ptr(k_pool, "k_pool", d["pool"]), _ptr(v_pool, "v_pool", d["pool"]), num_pages,
+            hkv, hd, page_size, _ptr(abort, "abort", d["u8"], allow_none=True),
+            _stream(stream))
+        _check("kv_append_bf16", st)
+
+
+def kv_append_quant(k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool,
+                    v_pool, abort=None, batch=None, page_size=PAGE_SIZE, stream=None):
+    """Quantize new K/V rows to E4M3 with per-KV-head scales and write them into pool pages."""
+    _append(True, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool,
+            v_pool, abort, batch, page_size, stream)
+
+
+def kv_append_bf16(k_new, v_new, tok_seq, tok_pos, block_table, k_pool, v_pool, abort=None,
+                   batch=None, page_size=PAGE_SIZE, stream=None):
+    """Write new bf16 K/V rows unchanged into BF16 pool pages."""
+    _append(False, k_new, v_new, tok_seq, tok_pos, block_table, None, None, k_pool, v_pool,
+            abort, batch, page_size, stream)
+
+
+def paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len, partition_tokens=0):
+    v = load().paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
+                                                  partition_tokens)
+    if v < 0:
+        raise KvError("paged_decode_attn_partition_tokens", v)
+    return v
+
+
+def paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len,
+                                      partition_tokens=0, head_dim=HEAD_DIM):
+    return int(load().paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
+                                                        head_dim, max_seq_len,
+                                                        partition_tokens))
+
+
+def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                      out, sm_scale, workspace=None, abort=None, partition_tokens=0,
+                      cache_dtype=KV_CACHE_FP8_E4M3, page_size=PAGE_SIZE, stream=None):
+    """out[b][h] = softmax attention of q[b][h] over request b's cached tokens."""
+    d = _dt()
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
+    batch, hq, hd = q.shape
+    hkv = k_pool.shape[1]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
+    st = load().paged_decode_attn(
+        _ptr(q, "q", d["bf16"]), int(cache_dtype),
+        _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
+        _ptr(v_pool, "v_pool", d["u8"] if fp8 else d["pool"]),
+        _ptr(k_scale, "k_scale", d["f32"], allow_none=not fp8),
+        _ptr(v_scale, "v_scale", d["f32"], allow_none=not fp8),
+        _ptr(block_table, "block_table", d["i32"]), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", d["i32"]), int(max_seq_len),
+        _ptr(abort, "abort", d["u8"], allow_none=True), _ptr(out, "out", d["f32"]),
+        float(sm_scale), batch, hq, hkv, hd, page_size, k_pool.shape[0], int(partition_tokens),
+        ws_ptr, ws_bytes, _stream(stream))
+    _check("paged_decode_attn", st)
+
+
+def decode_step(layers, block_table, seq_lens, tok_pos, tok_seq, max_seq_len, sm_scale,
+                pool_tags=None, expected_tags=None, abort=None, cache_dtype=KV_CACHE_FP8_E4M3,
+                workspace=None, partition_tokens=0, stream=None):
+    """Enqueue one decode step: tag check (if pool_tags is given), then for
+    each layer the append of the new token and attention over the pages.
+
+    ``layers`` is a sequence of dicts with keys q, k_new, v_new, k_pool, v_pool,
+    k_scale, v_scale, out. With pool_tags=None no check runs and abort=None is
+    passed on (the no-op tracker).
+    """
+    if pool_tags is not None:
+        kv_verify_tags(pool_tags, block_table, expected_tags, seq_lens, abort, stream=stream)
+    else:
+        abort = None
+    for ly in layers:
+        if cache_dtype == KV_CACHE_FP8_E4M3:
+            kv_append_quant(ly["k_new"], ly["v_new"], tok_seq, tok_pos, block_table,
+                            ly["k_scale"], ly["v_scale"], ly["k_pool"], ly["v_pool"],
+                            abort=abort, stream=stream)
+        else:
+            kv_append_bf16(ly["k_new"], ly["v_new"], tok_seq, tok_pos, block_table,
+                           ly["k_pool"], ly["v_pool"], abort=abort, stream=stream)
+        paged_decode_attn(ly["q"], ly["k_pool"], ly["v_pool"], ly.get("k_scale"),
+                          ly.get("v_scale"), block_table, seq_lens, max_seq_len, ly["out"],
+                          sm_scale, workspace=workspace, abort=abort,
+                          partition_tokens=partition_tokens, cache_dtype=cache_dtype,
+                          stream=stream)

@@ -1,0 +1,417 @@
+// Split-K paged decode attention over an FP8 e4m3 (or BF16) KV cache.
+//
+// What it computes is standard softmax attention of one decode token per
+// query head over the request's cached tokens; the FP8 values are converted
+// when the kernel reads them (remio.ai/it "Il serving di modelli più piccoli
+// di Cloudflare ...", section "Perché le cache più piccole di Cloudflare
+// battono la velocità pura": the conversion work sits in the attention
+// kernel's reads). Decode is memory-bound (same page, same section), so the
+// kernel is built to stream the cache at HBM speed:
+//
+//  * one 256-thread workgroup per (partition p, request b, KV head g); its
+//    4 wavefronts take the partition's page *pairs* round-robin and keep the
+//    next pair's loads in flight while computing the current one;
+//  * a (page, head) tile is 2 KiB (FP8) and is read with 16-byte-per-lane
+//    loads that cover it contiguously; the tile layout puts every byte in
+//    the lane that needs it for the matrix-core step, so nothing is staged;
+//  * QK^T of the GQA group runs on v_mfma_f32_16x16x32_bf16: A = 16 tokens x
+//    32 dims of K (e4m3 -> bf16 is exact), B = 32 dims x 16 query columns of
+//    Q (bf16, exact); the G <= 16 query heads of the group fill the columns;
+//  * the online softmax works on the 16x16 score tile in the accumulator
+//    layout (lane = query column, 4 token rows per lane): max and sum are a
+//    4-value in-lane reduction plus two cross-lane xor steps;
+//  * P.V runs on v_mfma_f32_16x16x32_f16 over the pair's 32 tokens: A = V^T
+//    (e4m3 -> f16 is exact), B = P^T taken straight from the score registers
+//    and rounded to f16 (nearest-even). BF16 caches use the bf16 instruction
+//    with P split into a bf16 high and low part (two products) instead;
+//  * the 4 wavefronts merge their (max, sum, output) in LDS; with one
+//    partition the workgroup writes the final output, otherwise a partial
+//    that reduce_partials_kernel combines across partitions.
+#include "kv_device.h"
+#include "kv_launch.h"
+
+namespace kvfp8 {
+
+constexpr int kAttnThreads = 256;
+constexpr int kWaves = kAttnThreads / 64;
+constexpr int kAccStride = kDim + 4;           // padded LDS row (floats)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Raw registers of one page pair: K and V tiles of pages a and b.
+template <bool FP8>
+struct PairTiles {
+    static constexpr int N = FP8 ? 2 : 4;     // 16-byte loads per lane per tile
+    u32x4 ka[N], kb[N], va[N], vb[N];
+};
+
+template <bool FP8>
+__device__ inline void load_pair(PairTiles<FP8>& r, const uint8_t* __restrict__ k_pool,
+                                 const uint8_t* __restrict__ v_pool, size_t tile_a,
+                                 size_t tile_b, int lane) {
+    constexpr int T = FP8 ? kTileFp8 : kTileBf16;
+    const uint8_t* ka = k_pool + tile_a * T + 16 * lane;
+    const uint8_t* kb = k_pool + tile_b * T + 16 * lane;
+    const uint8_t* va = v_pool + tile_a * T + 16 * lane;
+    const uint8_t* vb = v_pool + tile_b * T + 16 * lane;
+#pragma unroll
+    for (int h = 0; h < PairTiles<FP8>::N; ++h) {
+        r.ka[h] = *reinterpret_cast<const u32x4*>(ka + 1024 * h);
+        r.kb[h] = *reinterpret_cast<const u32x4*>(kb + 1024 * h);
+        r.va[h] = *reinterpret_cast<const u32x4*>(va + 1024 * h);
+        r.vb[h] = *reinterpret_cast<const u32x4*>(vb + 1024 * h);
+    }
+}
+
+// S^T (16 tokens x 16 query columns) of one page: 4 MFMAs over head_dim.
+template <bool FP8>
+__device__ inline f32x4 qk_page(const u32x4 (&k)[PairTiles<FP8>::N], const bf16x8 (&qop)[4]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        bf16x8 a;
+        if constexpr (FP8) {
+            // slot i of MFMA c <- dim 32j + 8c + i = bytes 8(c%2)..+7 of load c/2
+            const uint32_t w0 = k[c / 2][2 * (c % 2)];
+            const uint32_t w1 = k[c / 2][2 * (c % 2) + 1];
+            bf16x2 p0, p1, p2, p3;
+            decode4_bf16(w0, p0, p1);
+            decode4_bf16(w1, p2, p3);
+            a = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        } else {
+            a = __builtin_bit_cast(bf16x8, k[c]);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[c], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Zero the bytes of tokens >= valid in a lane's 4-token groups (FP8: 1 byte
+// per token per dword; BF16: 2 bytes per token, two dwords per group).
+__device__ inline uint32_t token_mask_fp8(int valid) {
+    return valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
+}
+__device__ inline uint64_t token_mask_bf16(int valid) {
+    return valid >= 4 ? ~0ull : (valid <= 0 ? 0ull : ((1ull << (16 * valid)) - 1ull));
+}
+
+template <bool FP8>
+__device__ inline void mask_v(u32x4 (&v)[PairTiles<FP8>::N], int valid) {
+    if constexpr (FP8) {
+        const uint32_t m = token_mask_fp8(valid);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[h][e] &= m;
+    } else {
+        const uint64_t m = token_mask_bf16(valid);
+        const uint32_t lo = static_cast<uint32_t>(m), hi = static_cast<uint32_t>(m >> 32);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            v[h][0] &= lo;
+            v[h][1] &= hi;
+            v[h][2] &= lo;
+            v[h][3] &= hi;
+        }
+    }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int32_t bt_stride,
+    const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const uint8_t* __restrict__ abort,
+    float* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_acc,
+    float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv, int32_t num_pages,
+    int32_t part_tokens, int32_t n_parts) {
+    extern __shared__ float smem[];
+    const int group = hq / hkv;
+    // LDS: [wave][16] max, [wave][16] sum, [wave][group][kAccStride] output,
+    // and the partition's page ids (aliasing nothing used at the same time).
+    float* sm_m = smem;
+    float* sm_l = sm_m + kWaves * 16;
+    float* sm_acc = sm_l + kWaves * 16;
+    int32_t* sm_ids = reinterpret_cast<int32_t*>(sm_acc + kWaves * group * kAccStride);
+
+    const int bid = blockIdx.x;
+    const int g = bid % hkv;
+    const int b = (bid / hkv) % batch;
+    const int p = bid / (hkv * batch);
+    const int tid = threadIdx.x;
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    const int col = lane % 16;       // query column of the MFMA tiles
+    const int jgrp = lane / 16;      // k-group of the operands / row group of the result
+
+    const int L = seq_lens[b];
+    const bool aborted = abort != nullptr && abort[b] != 0;
+    const bool valid_req = !aborted && L >= 1 && L <= max_seq_len &&
+                           (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
+    const int t_begin = p * part_tokens;
+    if (!valid_req || t_begin >= L) {
+        // Only the single-partition case owns the final output here; with
+        // several partitions the reduction writes zeros for such requests.
+        if (n_parts == 1) {
+            for (int i = tid; i < group * kDim; i += kAttnThreads)
+                out[(static_cast<size_t>(b) * hq + g * group) * kDim + i] = 0.f;
+        }
+        return;
+    }
+    const int t_end = min(L, t_begin + part_tokens);
+    const int pg0 = t_begin / kPage;
+    const int npg = (t_end + kPage - 1) / kPage - pg0;
+    const int npairs = (npg + 1) / 2;
+
+    // Page ids of the partition -> LDS; any id outside the pool poisons the
+    // request (its output becomes zero and no page of it is read).
+    int bad = 0;
+    const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
+    for (int k = tid; k < npg; k += kAttnThreads) {
+        const int32_t id = bt_row[k];
+        bad |= (id < 0 || id >= num_pages);
+        sm_ids[k] = id;
+    }
+    bad = __syncthreads_or(bad);
+
+    const size_t q_row = static_cast<size_t>(b) * hq + g * group;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4 acc_o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc_o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (!bad) {
+        // B operand of QK^T: column = query head g*G + col, slots = dims
+        // 32*jgrp + 8c + i. Columns past the group stay zero.
+        bf16x8 qop[4];
+        if (col < group) {
+            const u32x4* qp = reinterpret_cast<const u32x4*>(q + (q_row + col) * kDim + 32 * jgrp);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, qp[c]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        }
+        const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
+
+        const auto tile_of = [&](int page_idx) -> size_t {
+            const int id = __builtin_amdgcn_readfirstlane(sm_ids[page_idx]);
+            return static_cast<size_t>(id) * hkv + g;
+        };
+
+        int pr = wave;
+        PairTiles<FP8> cur;
+        if (pr < npairs) {
+            const int ia = 2 * pr, ib = min(2 * pr + 1, npg - 1);
+            load_pair<FP8>(cur, k_pool, v_pool, tile_of(ia), tile_of(ib), lane);
+        }
+        for (; pr < npairs; pr += kWaves) {
+            // Prefetch the wave's next pair (or re-read the current one at the
+            // end, which hits in cache) before touching the current registers.
+            PairTiles<FP8> nxt;
+            {
+                const int pn = (pr + kWaves < npairs) ? pr + kWaves : pr;
+                const int ia = 2 * pn, ib = min(2 * pn + 1, npg - 1);
+                load_pair<FP8>(nxt, k_pool, v_pool, tile_of(ia), tile_of(ib), lane);
+            }
+            const int tok_a = (pg0 + 2 * pr) * kPage;       // first token of page a
+            const int tok_b = tok_a + kPage;
+            // Tokens past t_end (the tail of the last page, or a missing page b)
+            // must not contribute: mask their scores and zero their V bytes
+            // (the slots may hold stale codes, NaN included).
+            if (tok_b + kPage > t_end) {
+                mask_v<FP8>(cur.va, t_end - (tok_a + 4 * jgrp));
+                mask_v<FP8>(cur.vb, t_end - (tok_b + 4 * jgrp));
+            }
+            const f32x4 sa = qk_page<FP8>(cur.ka, qop);
+            const f32x4 sb = qk_page<FP8>(cur.kb, qop);
+            float s[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[r] = (tok_a + 4 * jgrp + r < t_end) ? sa[r] * s_scale : -INFINITY;
+                s[4 + r] = (tok_b + 4 * jgrp + r < t_end) ? sb[r] * s_scale : -INFINITY;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2f(m_run - m_use);
+            float pv[8];
+            float psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                pv[r] = exp2f(s[r] - m_use);
+                psum += pv[r];
+            }
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc_o[c] *= alpha;
+
+            if constexpr (FP8) {
+                // B = P^T: slots 0..3 = page a tokens 4j..4j+3, 4..7 = page b.
+                f16x8 P;
+#pragma unroll
+                for (int r = 0; r < 8; r += 2) {
+                    const f16x2 h2 = __builtin_convertvector((f32x2{pv[r], pv[r + 1]}), f16x2);
+                    P[r] = h2[0];
+                    P[r + 1] = h2[1];
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    // A = V^T: row = dim 16c + col, slots = tokens 4j..4j+3 of
+                    // page a then of page b (dword c%4 of load c/4).
+                    f16x2 a0, a1, b0, b1;
+                    decode4_f16(cur.va[c / 4][c % 4], a0, a1);
+                    decode4_f16(cur.vb[c / 4][c % 4], b0, b1);
+                    const f16x8 A = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+                    acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, P, acc_o[c], 0, 0, 0);
+                }
+            } else {
+                // P = hi + lo, both bf16: hi = RNE(p), lo = RNE(p - hi).
+                bf16x8 Ph, Pl;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const __bf16 h = static_cast<__bf16>(pv[r]);
+                    Ph[r] = h;
+                    Pl[r] = static_cast<__bf16>(pv[r] - static_cast<float>(h));
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const u32x4 w = {cur.va[c / 2][2 * (c % 2)], cur.va[c / 2][2 * (c % 2) + 1],
+                                     cur.vb[c / 2][2 * (c % 2)], cur.vb[c / 2][2 * (c % 2) + 1]};
+                    const bf16x8 A = __builtin_bit_cast(bf16x8, w);
+                    acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Ph, acc_o[c], 0, 0, 0);
+                    acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pl, acc_o[c], 0, 0, 0);
+                }
+            }
+            cur = nxt;
+        }
+    }
+
+    // ---- merge the 4 wavefronts ------------------------------------------
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    __syncthreads();   // sm_ids is no longer read; LDS is reused below
+    if (jgrp == 0) {
+        sm_m[wave * 16 + col] = m_run;
+        sm_l[wave * 16 + col] = l_tot;
+    }
+    if (col < group) {
+        float* row = sm_acc + (wave * group + col) * kAccStride;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            *reinterpret_cast<f32x4*>(row + 16 * c + 4 * jgrp) = acc_o[c];
+    }
+    __syncthreads();
+
+    const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
+    for (int it = tid; it < group * (kDim / 4); it += kAttnThreads) {
+        const int qh = it / (kDim / 4);
+        const int d = (it % (kDim / 4)) * 4;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float lt = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = exp2f(sm_m[w * 16 + qh] - M_use);
+            lt += f * sm_l[w * 16 + qh];
+            o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
+        }
+        if (n_parts == 1) {
+            f32x4 r = {0.f, 0.f, 0.f, 0.f};
+            if (!bad && lt > 0.f) r = o * (vs / lt);
+            *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
+        } else {
+            const size_t slot = (q_row + qh) * n_parts + p;
+            *reinterpret_cast<f32x4*>(part_acc + slot * kDim + d) = o;
+            if (d == 0) {
+                part_ml[2 * slot] = M;
+                part_ml[2 * slot + 1] = bad ? -1.f : lt;
+            }
+        }
+    }
+}
+
+// Combine the partitions of each (request, query head):
+//   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p acc_p / sum_p w_p l_p
+// Requests that are aborted, empty, too long, or that a partition marked as
+// mapped to an invalid page (l_p < 0) get zeros.
+__global__ __launch_bounds__(kDim) void reduce_partials_kernel(
+    const float* __restrict__ part_ml, const float* __restrict__ part_acc,
+    const int32_t* __restrict__ seq_lens, int32_t max_seq_len, int32_t bt_stride,
+    const uint8_t* __restrict__ abort, const float* __restrict__ v_scale,
+    float* __restrict__ out, int32_t hq, int32_t hkv, int32_t part_tokens, int32_t n_parts) {
+    const int bh = blockIdx.x;
+    const int b = bh / hq;
+    const int h = bh % hq;
+    const int d = threadIdx.x;
+    const int L = seq_lens[b];
+    const bool aborted = abort != nullptr && abort[b] != 0;
+    const bool valid_req = !aborted && L >= 1 && L <= max_seq_len &&
+                           (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
+    float* o = out + static_cast<size_t>(bh) * kDim + d;
+    if (!valid_req) {
+        *o = 0.f;
+        return;
+    }
+    const int np = (L + part_tokens - 1) / part_tokens;
+    const float* ml = part_ml + static_cast<size_t>(bh) * n_parts * 2;
+    const float* acc = part_acc + static_cast<size_t>(bh) * n_parts * kDim + d;
+    float M = -INFINITY;
+    bool bad = false;
+    for (int i = 0; i < np; ++i) {
+        M = fmaxf(M, ml[2 * i]);
+        bad |= ml[2 * i + 1] < 0.f;
+    }
+    if (bad) {
+        *o = 0.f;
+        return;
+    }
+    float lt = 0.f, num = 0.f;
+    for (int i = 0; i < np; ++i) {
+        const float w = exp2f(ml[2 * i] - M);
+        lt += w * ml[2 * i + 1];
+        num += w * acc[static_cast<size_t>(i) * kDim];
+    }
+    const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
+    *o = lt > 0.f ? num * (vs / lt) : 0.f;
+}
+
+hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
+    const int group = a.num_q_heads / a.num_kv_heads;
+    const size_t lds = sizeof(float) * (2 * kWaves * 16 + kWaves * group * kAccStride) +
+                       sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage);
+    const dim3 grid(static_cast<uint32_t>(a.num_partitions) * a.batch * a.num_kv_heads);
+    const float sm_log2 = a.sm_scale * kLog2e;
+    if (fp8) {
+        hipLaunchKernelGGL(attn_partition_kernel<true>, grid, dim3(kAttnThreads), lds, stream,
+                           a.q, static_cast<const uint8_t*>(a.k_pool),
+                           static_cast<const uint8_t*>(a.v_pool), a.k_scale, a.v_scale,
+                           a.block_table, a.bt_stride, a.seq_lens, a.max_seq_len, a.abort, a.out,
+                           a.part_ml, a.part_acc, sm_log2, a.batch, a.num_q_heads,
+                           a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions);
+    } else {
+        hipLaunchKernelGGL(attn_partition_kernel<false>, grid, dim3(kAttnThreads), lds, stream,
+                           a.q, static_cast<const uint8_t*>(a.k_pool),
+                           static_cast<const uint8_t*>(a.v_pool), nullptr, nullptr,
+                           a.block_table, a.bt_stride, a.seq_lens, a.max_seq_len, a.abort, a.out,
+                           a.part_ml, a.part_acc, sm_log2, a.batch, a.num_q_heads,
+                           a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.num_partitions == 1) return e;
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(a.batch * a.num_q_heads), dim3(kDim), 0,
+                       stream, a.part_ml, a.part_acc, a.seq_lens, a.max_seq_len, a.bt_stride,
+                       a.abort, fp8 ? a.v_scale : nullptr, a.out, a.num_q_heads, a.num_kv_heads,
+                       a.partition_tokens, a.num_partitions);
+    return hipGetLastError();
+}
+
+}  // namespace kvfp8

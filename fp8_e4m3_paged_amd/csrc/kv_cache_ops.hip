@@ -1,0 +1,173 @@
+// Page-tag verification and append (quantize-on-append / bf16 copy) kernels.
+//
+// Tag check: the pages describe a separate batched check that compares each
+// request's recorded (page, tag) pairs with the pool's current tags before
+// supported decode operations read, aborting just the mismatching request
+// (remio.ai/it "Il serving di modelli più piccoli di Cloudflare ...", sections
+// "Cosa ha cambiato Cloudflare per Kimi e GLM" and "La sicurezza della cache
+// KV condivisa diventa una questione di produzione").
+//
+// Append: the cache is stored as FP8 e4m3 instead of BF16 (same page, section
+// "Cosa ha cambiato ..."); each new token's K/V row is divided by its
+// (layer, KV head) scale and rounded to e4m3 on the way into its page slot.
+#include "kv_device.h"
+#include "kv_launch.h"
+
+namespace kvfp8 {
+
+// ---------------------------------------------------------------------------
+// kv_verify_tags: one 256-thread workgroup per request. Each thread checks up
+// to 4 logical pages per sweep; loads of a sweep are independent so their
+// latencies overlap. The workgroup ORs the per-thread verdicts and one thread
+// writes the request's flag.
+// ---------------------------------------------------------------------------
+constexpr int kVerifyThreads = 256;
+constexpr int kVerifyUnroll = 4;
+
+__global__ __launch_bounds__(kVerifyThreads) void verify_tags_kernel(
+    const uint32_t* __restrict__ pool_tags, int32_t num_pages,
+    const int32_t* __restrict__ block_table, const uint32_t* __restrict__ expected_tags,
+    int32_t bt_stride, const int32_t* __restrict__ seq_lens, uint8_t* __restrict__ abort_out) {
+    const int b = blockIdx.x;
+    const int L = seq_lens[b];
+    int bad = 0;
+    int64_t npages = 0;
+    if (L < 0) {
+        bad = 1;
+    } else {
+        npages = (static_cast<int64_t>(L) + kPage - 1) / kPage;
+        if (npages > bt_stride) bad = 1;
+    }
+    if (!bad) {
+        const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride;
+        const uint32_t* ex_row = expected_tags + static_cast<size_t>(b) * bt_stride;
+        for (int64_t base = 0; base < npages; base += kVerifyThreads * kVerifyUnroll) {
+            int32_t page[kVerifyUnroll];
+            uint32_t want[kVerifyUnroll];
+#pragma unroll
+            for (int u = 0; u < kVerifyUnroll; ++u) {
+                const int64_t j = base + u * kVerifyThreads + threadIdx.x;
+                page[u] = 0;
+                want[u] = 0;
+                if (j < npages) {
+                    page[u] = bt_row[j];
+                    want[u] = ex_row[j];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kVerifyUnroll; ++u) {
+                const int64_t j = base + u * kVerifyThreads + threadIdx.x;
+                if (j < npages) {
+                    const int32_t p = page[u];
+                    if (p < 0 || p >= num_pages || pool_tags[p] != want[u]) bad = 1;
+                }
+            }
+        }
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) abort_out[b] = bad ? 1 : 0;
+}
+
+hipError_t launch_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
+                              const int32_t* block_table, const uint32_t* expected_tags,
+                              int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                              uint8_t* abort_out, hipStream_t stream) {
+    hipLaunchKernelGGL(verify_tags_kernel, dim3(batch), dim3(kVerifyThreads), 0, stream,
+                       pool_tags, num_pages, block_table, expected_tags, bt_stride, seq_lens,
+                       abort_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Append. Grid: x = token n, y = slice of the token's (K|V, head, 4-dim group)
+// work items; each thread handles 4 consecutive dims of one head of K or V.
+// FP8: x / s in correctly rounded fp32 (the default HIP division), clamp to
+// +-448, hardware round-to-nearest-even convert. BF16: stored as is.
+// ---------------------------------------------------------------------------
+constexpr int kAppendThreads = 256;
+
+template <bool FP8>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ tok_seq, const int32_t* __restrict__ tok_pos,
+    const int32_t* __restrict__ block_table, int32_t bt_stride, int32_t batch,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int32_t num_pages,
+    int32_t num_kv_heads, const uint8_t* __restrict__ abort) {
+    const int n = blockIdx.x;
+    const int items_per_kind = num_kv_heads * (kDim / 4);
+    const int item = blockIdx.y * kAppendThreads + threadIdx.x;
+    if (item >= 2 * items_per_kind) return;
+    const int b = tok_seq[n];
+    const int t = tok_pos[n];
+    if (b < 0 || b >= batch || t < 0) return;
+    if (abort != nullptr && abort[b] != 0) return;
+    const int j = t / kPage;
+    if (j >= bt_stride) return;
+    const int page = block_table[static_cast<size_t>(b) * bt_stride + j];
+    if (page < 0 || page >= num_pages) return;
+
+    const bool is_v = item >= items_per_kind;
+    const int rem = is_v ? item - items_per_kind : item;
+    const int g = rem / (kDim / 4);
+    const int d = (rem % (kDim / 4)) * 4;
+    const int slot = t % kPage;
+    const uint16_t* src = (is_v ? v_new : k_new) +
+                          (static_cast<size_t>(n) * num_kv_heads + g) * kDim + d;
+    const u32x2 raw = *reinterpret_cast<const u32x2*>(src);
+    const size_t tile = static_cast<size_t>(page) * num_kv_heads + g;
+
+    if constexpr (FP8) {
+        const float s = (is_v ? v_scale : k_scale)[g];
+        const float y0 = bf16_bits_to_float(raw.x & 0xFFFF) / s;
+        const float y1 = bf16_bits_to_float(raw.x >> 16) / s;
+        const float y2 = bf16_bits_to_float(raw.y & 0xFFFF) / s;
+        const float y3 = bf16_bits_to_float(raw.y >> 16) / s;
+        const uint32_t codes = encode4_e4m3(y0, y1, y2, y3);
+        uint8_t* base = (is_v ? v_pool : k_pool) + tile * kTileFp8;
+        if (!is_v) {
+            // 4 consecutive dims are 4 consecutive bytes in the K tile.
+            *reinterpret_cast<uint32_t*>(base + off_k_fp8(slot, d)) = codes;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) base[off_v_fp8(slot, d + i)] = (codes >> (8 * i)) & 0xFF;
+        }
+    } else {
+        uint8_t* base = (is_v ? v_pool : k_pool) + tile * kTileBf16;
+        if (!is_v) {
+            *reinterpret_cast<u32x2*>(base + off_k_bf16(slot, d)) = raw;
+        } else {
+            const uint16_t h[4] = {static_cast<uint16_t>(raw.x & 0xFFFF),
+                                   static_cast<uint16_t>(raw.x >> 16),
+                                   static_cast<uint16_t>(raw.y & 0xFFFF),
+                                   static_cast<uint16_t>(raw.y >> 16)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint16_t*>(base + off_v_bf16(slot, d + i)) = h[i];
+        }
+    }
+}
+
+hipError_t launch_append(bool fp8, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok,
+                         const int32_t* block_table, int32_t bt_stride, int32_t batch,
+                         const float* k_scale, const float* v_scale, void* k_pool,
+                         void* v_pool, int32_t num_pages, int32_t num_kv_heads,
+                         const uint8_t* abort, hipStream_t stream) {
+    const int items = 2 * num_kv_heads * (kDim / 4);
+    const dim3 grid(n_tok, (items + kAppendThreads - 1) / kAppendThreads);
+    if (fp8) {
+        hipLaunchKernelGGL(append_kernel<true>, grid, dim3(kAppendThreads), 0, stream, k_new,
+                           v_new, tok_seq, tok_pos, block_table, bt_stride, batch, k_scale,
+                           v_scale, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                           num_pages, num_kv_heads, abort);
+    } else {
+        hipLaunchKernelGGL(append_kernel<false>, grid, dim3(kAppendThreads), 0, stream, k_new,
+                           v_new, tok_seq, tok_pos, block_table, bt_stride, batch, k_scale,
+                           v_scale, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                           num_pages, num_kv_heads, abort);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvfp8

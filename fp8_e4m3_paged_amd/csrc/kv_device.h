@@ -1,0 +1,88 @@
+// Device-side helpers shared by the kernels: vector types, tile layouts and
+// the gfx950 FP8 conversions. gfx950 only; no other target is built.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp8 {
+
+constexpr int kPage = 16;          // tokens per page
+constexpr int kDim = 128;          // head_dim
+constexpr int kTileFp8 = kPage * kDim;        // 2048 bytes
+constexpr int kTileBf16 = kPage * kDim * 2;   // 4096 bytes
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Byte offset of element (token t, dim d) inside one (page, head) tile.
+// These are the layouts documented in kvfp8.h; the append kernels write
+// through them and the attention kernel's loads are their inverse.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int off_k_fp8(int t, int d) {
+    return 1024 * ((d % 32) / 16) + 256 * (d / 32) + 16 * t + (d % 16);
+}
+__host__ __device__ inline int off_v_fp8(int t, int d) {
+    return 1024 * (d / 64) + 256 * (t / 4) + 16 * (d % 16) + 4 * ((d / 16) % 4) + (t % 4);
+}
+__host__ __device__ inline int off_k_bf16(int t, int d) {
+    return 1024 * ((d % 32) / 8) + 256 * (d / 32) + 16 * t + 2 * (d % 8);
+}
+__host__ __device__ inline int off_v_bf16(int t, int d) {
+    return 1024 * (d / 32) + 256 * (t / 4) + 16 * (d % 16) + 8 * ((d / 16) % 2) + 2 * (t % 4);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 e4m3 (OCP) conversions on gfx950.
+// ---------------------------------------------------------------------------
+
+// Encode two floats already divided by the scale. Finite values and
+// infinities are clamped to +-448 first, so the hardware's round-to-nearest-
+// even conversion never sees an overflow; NaN gets the NaN code with its sign.
+__device__ inline uint32_t sat_e4m3_byte_fixup(float y, uint32_t code) {
+    if (y != y) return (__float_as_uint(y) >> 24 & 0x80u) | 0x7Fu;
+    return code;
+}
+
+__device__ inline float clamp448(float y) {
+    // fminf/fmaxf would turn NaN into +-448; NaN is fixed up after the convert.
+    return (y != y) ? 0.0f : fminf(fmaxf(y, -448.0f), 448.0f);
+}
+
+// Four floats (already x / s) -> four e4m3 codes packed little-endian.
+__device__ inline uint32_t encode4_e4m3(float y0, float y1, float y2, float y3) {
+    uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y0), clamp448(y1), 0u, false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y2), clamp448(y3), pk, true);
+    uint32_t b0 = sat_e4m3_byte_fixup(y0, pk & 0xFFu);
+    uint32_t b1 = sat_e4m3_byte_fixup(y1, (pk >> 8) & 0xFFu);
+    uint32_t b2 = sat_e4m3_byte_fixup(y2, (pk >> 16) & 0xFFu);
+    uint32_t b3 = sat_e4m3_byte_fixup(y3, (pk >> 24) & 0xFFu);
+    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// Decode the 4 e4m3 codes of one dword into 4 bf16 (exact: 4 significant
+// bits fit bf16's 8). Scale operand 1.0 keeps the conversion a pure decode.
+__device__ inline void decode4_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
+    lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+}
+
+// Decode the 4 e4m3 codes of one dword into 4 f16 (exact: every e4m3 value,
+// subnormals included, is an f16 normal).
+__device__ inline void decode4_f16(uint32_t w, f16x2& lo, f16x2& hi) {
+    lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+}
+
+__device__ inline float bf16_bits_to_float(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+}  // namespace kvfp8

@@ -1,0 +1,48 @@
+// Internal host-side launchers. Arguments are already validated by the C-ABI
+// layer (kvfp8_api.hip); each launcher only enqueues its kernels on `stream`
+// and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp8 {
+
+hipError_t launch_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
+                              const int32_t* block_table, const uint32_t* expected_tags,
+                              int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                              uint8_t* abort_out, hipStream_t stream);
+
+hipError_t launch_append(bool fp8, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok,
+                         const int32_t* block_table, int32_t bt_stride, int32_t batch,
+                         const float* k_scale, const float* v_scale, void* k_pool,
+                         void* v_pool, int32_t num_pages, int32_t num_kv_heads,
+                         const uint8_t* abort, hipStream_t stream);
+
+struct AttnArgs {
+    const uint16_t* q;
+    const void* k_pool;
+    const void* v_pool;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_table;
+    int32_t bt_stride;
+    const int32_t* seq_lens;
+    int32_t max_seq_len;
+    const uint8_t* abort;
+    float* out;
+    float sm_scale;
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_pages;
+    int32_t partition_tokens;   // resolved, > 0
+    int32_t num_partitions;     // ceil(max_seq_len / partition_tokens), >= 1
+    float* part_ml;             // [batch][Hq][num_partitions][2], or null if 1 partition
+    float* part_acc;            // [batch][Hq][num_partitions][128]
+};
+
+hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream);
+
+}  // namespace kvfp8

@@ -1,0 +1,212 @@
+// C-ABI entry points: argument validation, partition sizing and dispatch to
+// the kernel launchers. Validation happens before any HIP call, so invalid
+// arguments return a negative status and enqueue nothing.
+#include "../../include/kvfp8.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kv_launch.h"
+
+namespace {
+
+inline bool misaligned(const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_LAUNCH; }
+
+int check_append_common(const void* k_new, const void* v_new, const int32_t* tok_seq,
+                        const int32_t* tok_pos, int32_t n_tok, const int32_t* block_table,
+                        int32_t bt_stride, int32_t batch, const void* k_pool, const void* v_pool,
+                        int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t page_size, const uint8_t* /*abort*/) {
+    if (n_tok < 0 || bt_stride < 0 || batch < 0 || num_pages < 0 || num_kv_heads <= 0)
+        return KV_ERR_SHAPE;
+    if (head_dim != KV_HEAD_DIM || page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
+    if (n_tok == 0) return KV_OK;
+    if (!k_new || !v_new || !tok_seq || !tok_pos || !block_table || !k_pool || !v_pool)
+        return KV_ERR_NULL;
+    if (misaligned(k_new, 16) || misaligned(v_new, 16) || misaligned(k_pool, 16) ||
+        misaligned(v_pool, 16) || misaligned(tok_seq, 4) || misaligned(tok_pos, 4) ||
+        misaligned(block_table, 4))
+        return KV_ERR_ALIGN;
+    return KV_OK;
+}
+
+// Automatic split-K size: enough (partition, request, KV head) workgroups to
+// keep every compute unit streaming (at least ~4 per CU of the 256), but no
+// partition shorter than 1024 tokens so that the partial traffic (520 B per
+// query head and partition) stays small next to the KV bytes, and none longer
+// than the maximum the kernel's LDS page list holds.
+int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+    const int64_t items = static_cast<int64_t>(batch) * num_kv_heads;
+    const int64_t target = 1024;
+    int64_t parts = items >= target ? 1 : (target + items - 1) / items;
+    int64_t tokens = (static_cast<int64_t>(max_seq_len) + parts - 1) / parts;
+    tokens = ((tokens + 255) / 256) * 256;
+    if (tokens < 1024) tokens = 1024;
+    if (tokens > KV_MAX_PARTITION_TOKENS) tokens = KV_MAX_PARTITION_TOKENS;
+    return static_cast<int32_t>(tokens);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_status_str(int status) {
+    switch (status) {
+        case KV_OK: return "KV_OK";
+        case KV_ERR_NULL: return "KV_ERR_NULL: a required pointer is NULL";
+        case KV_ERR_SHAPE: return "KV_ERR_SHAPE: a size is negative or inconsistent";
+        case KV_ERR_UNSUPPORTED:
+            return "KV_ERR_UNSUPPORTED: head_dim/page_size/group size/partition not supported";
+        case KV_ERR_WORKSPACE: return "KV_ERR_WORKSPACE: workspace missing or too small";
+        case KV_ERR_LAUNCH: return "KV_ERR_LAUNCH: HIP reported an error when enqueueing";
+        case KV_ERR_ALIGN: return "KV_ERR_ALIGN: a pointer is not aligned as required";
+        default: return "unknown kv_status";
+    }
+}
+
+int kv_verify_tags(const uint32_t* pool_tags, int32_t num_pages, const int32_t* block_table,
+                   const uint32_t* expected_tags, int32_t bt_stride, const int32_t* seq_lens,
+                   int32_t batch, int32_t page_size, uint8_t* abort_out, void* stream) {
+    if (batch < 0 || num_pages < 0 || bt_stride < 0) return KV_ERR_SHAPE;
+    if (page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
+    if (batch == 0) return KV_OK;
+    if (!block_table || !expected_tags || !seq_lens || !abort_out) return KV_ERR_NULL;
+    if (!pool_tags && num_pages > 0) return KV_ERR_NULL;
+    if (misaligned(pool_tags, 4) || misaligned(block_table, 4) || misaligned(expected_tags, 4) ||
+        misaligned(seq_lens, 4))
+        return KV_ERR_ALIGN;
+    return launch_status(kvfp8::launch_verify_tags(pool_tags, num_pages, block_table,
+                                                   expected_tags, bt_stride, seq_lens, batch,
+                                                   abort_out, static_cast<hipStream_t>(stream)));
+}
+
+int kv_append_quant(const void* k_new, const void* v_new, const int32_t* tok_seq,
+                    const int32_t* tok_pos, int32_t n_tok, const int32_t* block_table,
+                    int32_t bt_stride, int32_t batch, const float* k_scale, const float* v_scale,
+                    uint8_t* k_pool, uint8_t* v_pool, int32_t num_pages, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, const uint8_t* abort, void* stream) {
+    int st = check_append_common(k_new, v_new, tok_seq, tok_pos, n_tok, block_table, bt_stride,
+                                 batch, k_pool, v_pool, num_pages, num_kv_heads, head_dim,
+                                 page_size, abort);
+    if (st != KV_OK || n_tok == 0) return st;
+    if (!k_scale || !v_scale) return KV_ERR_NULL;
+    if (misaligned(k_scale, 4) || misaligned(v_scale, 4)) return KV_ERR_ALIGN;
+    return launch_status(kvfp8::launch_append(
+        true, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), tok_seq,
+        tok_pos, n_tok, block_table, bt_stride, batch, k_scale, v_scale, k_pool, v_pool,
+        num_pages, num_kv_heads, abort, static_cast<hipStream_t>(stream)));
+}
+
+int kv_append_bf16(const void* k_new, const void* v_new, const int32_t* tok_seq,
+                   const int32_t* tok_pos, int32_t n_tok, const int32_t* block_table,
+                   int32_t bt_stride, int32_t batch, void* k_pool, void* v_pool,
+                   int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                   const uint8_t* abort, void* stream) {
+    int st = check_append_common(k_new, v_new, tok_seq, tok_pos, n_tok, block_table, bt_stride,
+                                 batch, k_pool, v_pool, num_pages, num_kv_heads, head_dim,
+                                 page_size, abort);
+    if (st != KV_OK || n_tok == 0) return st;
+    return launch_status(kvfp8::launch_append(
+        false, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), tok_seq,
+        tok_pos, n_tok, block_table, bt_stride, batch, nullptr, nullptr, k_pool, v_pool,
+        num_pages, num_kv_heads, abort, static_cast<hipStream_t>(stream)));
+}
+
+int32_t paged_decode_attn_partition_tokens(int32_t batch, int32_t num_kv_heads,
+                                           int32_t max_seq_len, int32_t partition_tokens) {
+    if (partition_tokens < 0) return KV_ERR_UNSUPPORTED;
+    if (partition_tokens > 0) {
+        if (partition_tokens % KV_PAGE_SIZE != 0 || partition_tokens > KV_MAX_PARTITION_TOKENS)
+            return KV_ERR_UNSUPPORTED;
+        return partition_tokens;
+    }
+    if (batch <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return 1024;
+    return auto_partition(batch, num_kv_heads, max_seq_len);
+}
+
+size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_seq_len, int32_t partition_tokens) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+        head_dim != KV_HEAD_DIM)
+        return 0;
+    const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
+                                                          partition_tokens);
+    if (pt <= 0) return 0;
+    const int64_t parts = (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
+    if (parts <= 1) return 0;
+    const size_t slots = static_cast<size_t>(batch) * num_q_heads * parts;
+    // [slots][2] (max, sum) then [slots][head_dim] outputs, 256-byte aligned
+    const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
+    return ml + slots * head_dim * sizeof(float);
+}
+
+int paged_decode_attn(const void* q, int32_t cache_dtype, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                      const uint8_t* abort, float* out, float sm_scale, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t page_size, int32_t num_pages, int32_t partition_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || bt_stride < 0 || num_pages < 0 ||
+        max_seq_len < 0)
+        return KV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return KV_ERR_SHAPE;
+    if (head_dim != KV_HEAD_DIM || page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > KV_MAX_GROUP) return KV_ERR_UNSUPPORTED;
+    if (cache_dtype != KV_CACHE_FP8_E4M3 && cache_dtype != KV_CACHE_BF16)
+        return KV_ERR_UNSUPPORTED;
+    const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
+                                                          partition_tokens);
+    if (pt <= 0) return KV_ERR_UNSUPPORTED;
+    if (batch == 0) return KV_OK;
+    const bool fp8 = cache_dtype == KV_CACHE_FP8_E4M3;
+    if (!q || !out || !seq_lens || !block_table || !k_pool || !v_pool) return KV_ERR_NULL;
+    if (fp8 && (!k_scale || !v_scale)) return KV_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(out, 16) || misaligned(k_pool, 16) ||
+        misaligned(v_pool, 16) || misaligned(seq_lens, 4) || misaligned(block_table, 4) ||
+        (k_scale && misaligned(k_scale, 4)) || (v_scale && misaligned(v_scale, 4)))
+        return KV_ERR_ALIGN;
+    const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
+    if (parts64 > (1 << 20)) return KV_ERR_SHAPE;
+    const int32_t parts = static_cast<int32_t>(parts64);
+    const int64_t blocks = parts64 * batch * num_kv_heads;
+    if (blocks > 0x7FFFFFFFLL) return KV_ERR_SHAPE;
+    const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
+                                                          head_dim, max_seq_len, pt);
+    if (parts > 1) {
+        if (!workspace || workspace_bytes < need) return KV_ERR_WORKSPACE;
+        if (misaligned(workspace, 16)) return KV_ERR_ALIGN;
+    }
+    kvfp8::AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.seq_lens = seq_lens;
+    a.max_seq_len = max_seq_len;
+    a.abort = abort;
+    a.out = out;
+    a.sm_scale = sm_scale;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.num_pages = num_pages;
+    a.partition_tokens = pt;
+    a.num_partitions = parts;
+    if (parts > 1) {
+        const size_t slots = static_cast<size_t>(batch) * num_q_heads * parts;
+        const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
+        a.part_ml = static_cast<float*>(workspace);
+        a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+    }
+    return launch_status(kvfp8::launch_decode_attn(fp8, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+/*
+ * kvfp8.h -- C ABI of a paged FP8-e4m3 KV-cache decode library for AMD
+ * MI355X (gfx950 / CDNA4).
+ *
+ * The operations follow the problem statement of the five web reports of
+ * Cloudflare's post on serving Kimi and GLM (remio.ai it/pt/ko pages titled
+ * "Il serving di modelli più piccoli di Cloudflare riduce la memoria, ma la
+ * sicurezza diventa la prova decisiva" and translations; iitog.ru "Cloudflare
+ * ускорила Kimi на 41% сжатием KV-кеша ..."; manulx.blog "CloudflareのKimiと
+ * GLMを提供するためのレシピ ..."):
+ *
+ *   - the KV cache is stored in FP8 e4m3 instead of BF16, halving its size
+ *     (remio.ai/it, section "Cosa ha cambiato Cloudflare per Kimi e GLM");
+ *   - the attention kernel converts the cached values when it reads them
+ *     (section "Perché le cache più piccole di Cloudflare battono la velocità
+ *     pura");
+ *   - every physical cache page carries a tag that changes whenever the page
+ *     is reallocated; the server records the pages and tags each request
+ *     expects, and before supported decode operations read those pages the
+ *     mappings are verified, a mismatch aborting the affected request; the
+ *     check is a separate batched operation, not fused into attention, and a
+ *     no-op tracker exists where the check is disabled (sections "Cosa ha
+ *     cambiato ..." and "La sicurezza della cache KV condivisa diventa una
+ *     questione di produzione"; iitog.ru, paragraph on tags; manulx.blog,
+ *     "共有キャッシュの保護").
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers, allocated and owned by the
+ *     caller. The library allocates nothing, keeps no state and no handles,
+ *     and is safe to call from several host threads.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; nothing synchronises the host.
+ *   - Arguments are validated before anything is enqueued. On invalid
+ *     arguments a negative kv_status is returned and nothing is launched.
+ *     KV_ERR_LAUNCH reports a HIP launch error seen right after enqueueing.
+ *   - Data-plane outcomes are never errors: a tag mismatch or a bad page id
+ *     only raises a request's abort flag / zeroes its output. The kernels
+ *     never touch memory outside [0, num_pages) pages, whatever the tables
+ *     hold.
+ *   - Supported shapes: head_dim == 128, page_size == 16, num_q_heads a
+ *     multiple of num_kv_heads with group size num_q_heads/num_kv_heads in
+ *     [1, 16]. bf16 / FP8 arrays must be 16-byte aligned, int32/uint32/float
+ *     arrays 4-byte aligned.
+ *
+ * Number format. FP8 codes are OCP 8-bit floating point E4M3 ("e4m3fn"):
+ * sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN =
+ * S.1111.111, largest finite 448. Stored code = round-to-nearest-even of
+ * x / s with saturation to +-448 (+-inf included), NaN -> 0x7F/0xFF keeping
+ * the sign, and the sign kept on zero; x / s is the correctly rounded fp32
+ * quotient, which gives the same code as rounding the exact quotient. The
+ * value read back is code * s. s is one fp32 scale per (layer, KV head) for
+ * K and one for V, supplied by the caller (positive and finite).
+ *
+ * Pool layout. Each layer has a K pool and a V pool, each an array of
+ * [num_pages][num_kv_heads] tiles; a tile holds page_size (16) tokens x
+ * head_dim (128) elements of one KV head: 2048 bytes for FP8, 4096 bytes for
+ * BF16. Tile (page p, head g) starts at byte (p * num_kv_heads + g) * tile.
+ * Inside a tile the element of token t (0..15) and dimension d (0..127) is at
+ * byte offset
+ *
+ *   FP8  K: 1024*((d%32)/16) + 256*(d/32) + 16*t + (d%16)
+ *   FP8  V: 1024*(d/64) + 256*(t/4) + 16*(d%16) + 4*((d/16)%4) + (t%4)
+ *   BF16 K: 1024*((d%32)/8)  + 256*(d/32) + 16*t + 2*(d%8)
+ *   BF16 V: 1024*(d/32) + 256*(t/4) + 16*(d%16) + 8*((d/16)%2) + 2*(t%4)
+ *
+ * (integer division). These are permutations of the tile chosen so that a
+ * wavefront reads a tile with fully contiguous 16-byte-per-lane loads that
+ * land directly in the register layout of the gfx950 16x16x32 matrix-core
+ * instructions: K rows feed the QK^T product, V is stored token-minor so the
+ * P.V product needs no transpose. Pools should be written only through the
+ * append entry points.
+ *
+ * Request tables (shared by all layers):
+ *   block_table   int32 [batch][bt_stride]  logical page j -> physical page id
+ *   expected_tags uint32[batch][bt_stride]  tag the request recorded for page j
+ *   pool_tags     uint32[num_pages]         current tag of each physical page
+ *   seq_lens      int32 [batch]             tokens attended, INCLUDING the token
+ *                                           appended this step
+ * Token t of request b lives in page block_table[b][t/16], slot t%16. Only
+ * entries j < ceil(seq_lens[b]/16) are ever read.
+ */
+#ifndef KVFP8_H
+#define KVFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KV_OK = 0,
+    KV_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    KV_ERR_SHAPE = -2,       /* a size is negative or inconsistent                  */
+    KV_ERR_UNSUPPORTED = -3, /* head_dim/page_size/group size/partition not handled */
+    KV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required             */
+    KV_ERR_LAUNCH = -5,      /* HIP reported an error when enqueueing               */
+    KV_ERR_ALIGN = -6        /* a pointer is not aligned as required                */
+} kv_status;
+
+typedef enum { KV_CACHE_FP8_E4M3 = 0, KV_CACHE_BF16 = 1 } kv_cache_dtype;
+
+#define KV_PAGE_SIZE 16
+#define KV_HEAD_DIM 128
+#define KV_MAX_GROUP 16
+#define KV_MAX_PARTITION_TOKENS 16384
+
+/*
+ * Batched page-tag check (the separate batch operation the pages describe).
+ *
+ * For every request b < batch writes abort_out[b] = 1 if
+ *   seq_lens[b] < 0, or ceil(seq_lens[b]/page_size) > bt_stride, or
+ *   some j < ceil(seq_lens[b]/page_size) has block_table[b][j] outside
+ *   [0, num_pages) or pool_tags[block_table[b][j]] != expected_tags[b][j];
+ * else abort_out[b] = 0. abort_out is overwritten, never accumulated.
+ * Run it before the append and attention calls of the step, on the same
+ * stream, and pass abort_out to them. Skipping it and passing abort = NULL to
+ * the other calls is the no-op tracker.
+ *
+ * pool_tags [num_pages], block_table/expected_tags [batch][bt_stride],
+ * seq_lens [batch]: read. abort_out uint8 [batch]: written.
+ * Errors: KV_ERR_NULL (any pointer NULL while batch > 0), KV_ERR_SHAPE
+ * (batch, num_pages or bt_stride negative), KV_ERR_UNSUPPORTED (page_size
+ * != 16), KV_ERR_ALIGN. batch == 0 enqueues nothing.
+ */
+int kv_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
+                   const int32_t* block_table, const uint32_t* expected_tags,
+                   int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                   int32_t page_size, uint8_t* abort_out, void* stream);
+
+/*
+ * Quantize-on-append into an FP8 e4m3 pool (the FP8 cache write).
+ *
+ * For each new token n < n_tok, request b = tok_seq[n], position t =
+ * tok_pos[n]: if 0 <= b < batch, abort (if non-NULL) has abort[b] == 0,
+ * 0 <= t, t/16 < bt_stride and page = block_table[b][t/16] is in
+ * [0, num_pages), then for every KV head g and dimension d
+ *     K tile (page, g)[t%16][d] = E4M3(k_new[n][g][d] / k_scale[g])
+ *     V tile (page, g)[t%16][d] = E4M3(v_new[n][g][d] / v_scale[g])
+ * and otherwise nothing is written. Decode appends one token per request
+ * (tok_seq = 0..batch-1, tok_pos = seq_lens - 1); bulk mode (prefill
+ * ingest) passes any number of (request, position) pairs, distinct targets.
+ *
+ * k_new, v_new: bf16 [n_tok][num_kv_heads][head_dim], read.
+ * k_scale, v_scale: fp32 [num_kv_heads] of this layer, read.
+ * k_pool, v_pool: this layer's FP8 pools (layout above), written at targets.
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED (head_dim != 128,
+ * page_size != 16), KV_ERR_ALIGN. n_tok == 0 enqueues nothing.
+ */
+int kv_append_quant(const void* k_new, const void* v_new,
+                    const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok,
+                    const int32_t* block_table, int32_t bt_stride, int32_t batch,
+                    const float* k_scale, const float* v_scale,
+                    uint8_t* k_pool, uint8_t* v_pool, int32_t num_pages,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                    const uint8_t* abort, void* stream);
+
+/*
+ * BF16-cache append: same addressing and skipping rules as kv_append_quant,
+ * the bf16 value stored unchanged (the comparison format kept where compute
+ * dominates, remio.ai/it section "Cosa ha cambiato ...").
+ */
+int kv_append_bf16(const void* k_new, const void* v_new,
+                   const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok,
+                   const int32_t* block_table, int32_t bt_stride, int32_t batch,
+                   void* k_pool, void* v_pool, int32_t num_pages,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                   const uint8_t* abort, void* stream);
+
+/*
+ * Split-K partition size (tokens) that paged_decode_attn will use for these
+ * sizes. partition_tokens > 0 is returned unchanged if it is a multiple of
+ * 16 and at most KV_MAX_PARTITION_TOKENS, else KV_ERR_UNSUPPORTED;
+ * partition_tokens == 0 picks one (a pure function of the arguments).
+ */
+int32_t paged_decode_attn_partition_tokens(int32_t batch, int32_t num_kv_heads,
+                                           int32_t max_seq_len, int32_t partition_tokens);
+
+/*
+ * Bytes of device workspace paged_decode_attn needs for these sizes (0 when a
+ * single partition covers max_seq_len). The workspace holds per-partition
+ * softmax partials (running max, normaliser, unnormalised output) that the
+ * cross-partition reduction combines. Returns 0 for unsupported arguments.
+ */
+size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_seq_len, int32_t partition_tokens);
+
+/*
+ * Decode-step attention over the paged cache, dequantizing on read.
+ *
+ * For each request b with abort[b] == 0 (or abort == NULL) and
+ * 1 <= L = seq_lens[b] <= max_seq_len whose pages j < ceil(L/16) are all
+ * valid ids, and each query head h with KV head g = h / (Hq/Hkv):
+ *     K_j = code_K(token j, g) * k_scale[g],  V_j likewise with v_scale
+ *          (BF16 cache: the stored bf16 values, scales ignored)
+ *     s_j = sm_scale * (q[b][h] . K_j),  p = softmax_j(s),
+ *     out[b][h][:] = sum_j p_j V_j
+ * and out[b][h][:] = 0 for every other request (aborted, empty, too long,
+ * or mapped to an invalid page). The sequence is split into partitions of
+ * partition_tokens tokens (0 = automatic); each is reduced with an online
+ * softmax and the partials are merged by a second kernel when there is more
+ * than one partition.
+ *
+ * q: bf16 [batch][num_q_heads][head_dim]. out: fp32 [batch][num_q_heads]
+ * [head_dim], fully written. k_scale/v_scale: fp32 [num_kv_heads] (may be
+ * NULL for the BF16 cache). workspace: device memory of at least
+ * paged_decode_attn_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE,
+ * KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ */
+int paged_decode_attn(const void* q, int32_t cache_dtype,
+                      const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* block_table, int32_t bt_stride,
+                      const int32_t* seq_lens, int32_t max_seq_len,
+                      const uint8_t* abort, float* out, float sm_scale,
+                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, int32_t num_pages,
+                      int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Human-readable name of a kv_status value (static string, never NULL). */
+const char* kv_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVFP8_H */

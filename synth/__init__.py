@@ -32,28 +32,21 @@ _C2 = 0xC2B2AE35
 
 
 # --------------------------------------------------------------------------
-# counter-based hash (numpy, uint64 lanes holding 32-bit values)
+# counter-based hash (numpy uint32)
 # --------------------------------------------------------------------------
-def _mul32(h, c):
-    """(h * c) mod 2^32 for uint64 arrays h < 2^32, with no 64-bit overflow."""
-    lo = np.uint64(c & 0xFFFF)
-    hi = np.uint64(c >> 16)
-    return (h * lo + (((h * hi) & np.uint64(0xFFFF)) << np.uint64(16))) & np.uint64(M32)
-
-
 def fmix32(h):
-    """MurmurHash3's 32-bit finaliser on a uint64 array of 32-bit values."""
-    h = np.asarray(h, dtype=np.uint64)
-    h = h ^ (h >> np.uint64(16))
-    h = _mul32(h, _C1)
-    h = h ^ (h >> np.uint64(13))
-    h = _mul32(h, _C2)
-    h = h ^ (h >> np.uint64(16))
+    """MurmurHash3's 32-bit finaliser; numpy uint32 products wrap mod 2^32."""
+    h = np.asarray(h, dtype=np.uint32)
+    h = h ^ (h >> np.uint32(16))
+    h = h * np.uint32(_C1)
+    h = h ^ (h >> np.uint32(13))
+    h = h * np.uint32(_C2)
+    h = h ^ (h >> np.uint32(16))
     return h
 
 
 def _fmix32_int(x: int) -> int:
-    return int(fmix32(np.array([x & M32], dtype=np.uint64))[0])
+    return int(fmix32(np.array([x & M32], dtype=np.uint32))[0])
 
 
 def stream_key(seed: int, *parts: int) -> tuple[int, int]:
@@ -65,11 +58,11 @@ def stream_key(seed: int, *parts: int) -> tuple[int, int]:
 
 
 def table_index(key: tuple[int, int], ctr) -> np.ndarray:
-    """16-bit table index for each counter value (uint64 array < 2^32)."""
+    """16-bit table index for each counter value (counters < 2^32)."""
     k1, k2 = key
-    h = fmix32(np.asarray(ctr, dtype=np.uint64) ^ np.uint64(k1))
-    h = fmix32((h + np.uint64(k2)) & np.uint64(M32))
-    return (h >> np.uint64(16)).astype(np.int64)
+    h = fmix32(np.asarray(ctr, dtype=np.uint32) ^ np.uint32(k1))
+    h = fmix32(h + np.uint32(k2))
+    return (h >> np.uint32(16)).astype(np.int64)
 
 
 # --------------------------------------------------------------------------
@@ -165,10 +158,10 @@ class Workload:
     def kv_bits(self, layer: int, kind: str, b: int, t0: int, t1: int) -> np.ndarray:
         """bf16 bits [t1 - t0][Hkv][D] of tokens t0..t1-1 of request b."""
         hkv, d = self.num_kv_heads, self.head_dim
-        t = np.arange(t0, t1, dtype=np.uint64)[:, None, None]
-        g = np.arange(hkv, dtype=np.uint64)[None, :, None]
-        j = np.arange(d, dtype=np.uint64)[None, None, :]
-        ctr = (t * np.uint64(hkv) + g) * np.uint64(d) + j
+        t = np.arange(t0, t1, dtype=np.uint32)[:, None, None]
+        g = np.arange(hkv, dtype=np.uint32)[None, :, None]
+        j = np.arange(d, dtype=np.uint32)[None, None, :]
+        ctr = (t * np.uint32(hkv) + g) * np.uint32(d) + j
         return normal_bf16(self._kv_key(layer, kind, b), ctr, self.kv_sigma(kind))
 
     def new_token_bits(self, layer: int, kind: str, step: int) -> np.ndarray:
@@ -182,7 +175,7 @@ class Workload:
     def q_bits(self, layer: int, step: int) -> np.ndarray:
         """bf16 bits [B][Hq][D] of the decode queries of one layer and step."""
         hq, d = self.num_q_heads, self.head_dim
-        ctr = np.arange(self.batch * hq * d, dtype=np.uint64).reshape(self.batch, hq, d)
+        ctr = np.arange(self.batch * hq * d, dtype=np.uint32).reshape(self.batch, hq, d)
         return normal_bf16(stream_key(self.seed, T_Q, layer, step), ctr, self.q_sigma)
 
     def initial_scales(self, layer: int) -> tuple[np.ndarray, np.ndarray]:

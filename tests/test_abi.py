@@ -1,0 +1,163 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before enqueuing anything (no GPU needed: validation
+precedes every HIP call). Also the header's tile layouts and the device twin
+of the input hash."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import device as sd
+from tests.helpers import OFFSETS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfp8.h")
+LIB = os.path.join(ROOT, "fp8_e4m3_paged_amd", "libkvfp8.so")
+
+OK, NULL, SHAPE, UNSUP, WORKSPACE, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libkvfp8.so not built: run python -m fp8_e4m3_paged_amd.build")
+    import fp8_e4m3_paged_amd as k
+    return k.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["kv_verify_tags", "kv_append_quant", "kv_append_bf16", "paged_decode_attn",
+              "paged_decode_attn_workspace_bytes", "paged_decode_attn_partition_tokens",
+              "kv_status_str"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    import fp8_e4m3_paged_amd as k
+    for s in (OK, NULL, SHAPE, UNSUP, WORKSPACE, LAUNCH, ALIGN):
+        assert k.kv_status_str(s).startswith("KV_")
+    assert "unknown" in k.kv_status_str(42)
+
+
+A = 1 << 20        # a fake, 16-byte aligned "device" address (never dereferenced)
+
+
+def verify(lib, **kw):
+    args = dict(pool_tags=A, num_pages=10, block_table=A, expected_tags=A, bt_stride=4,
+                seq_lens=A, batch=2, page_size=16, abort_out=A, stream=None)
+    args.update(kw)
+    return lib.kv_verify_tags(*args.values())
+
+
+def test_verify_rejects_bad_arguments(lib):
+    assert verify(lib, page_size=8) == UNSUP
+    assert verify(lib, batch=-1) == SHAPE
+    assert verify(lib, bt_stride=-1) == SHAPE
+    assert verify(lib, block_table=None) == NULL
+    assert verify(lib, abort_out=None) == NULL
+    assert verify(lib, seq_lens=A + 2) == ALIGN
+    assert verify(lib, batch=0, block_table=None) == OK       # nothing to do
+
+
+def append(lib, fp8=True, **kw):
+    args = dict(k_new=A, v_new=A, tok_seq=A, tok_pos=A, n_tok=3, block_table=A, bt_stride=4,
+                batch=2)
+    if fp8:
+        args.update(k_scale=A, v_scale=A)
+    args.update(k_pool=A, v_pool=A, num_pages=10, num_kv_heads=8, head_dim=128, page_size=16,
+                abort=None, stream=None)
+    args.update(kw)
+    fn = lib.kv_append_quant if fp8 else lib.kv_append_bf16
+    return fn(*args.values())
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_append_rejects_bad_arguments(lib, fp8):
+    assert append(lib, fp8, head_dim=64) == UNSUP
+    assert append(lib, fp8, page_size=32) == UNSUP
+    assert append(lib, fp8, n_tok=-1) == SHAPE
+    assert append(lib, fp8, num_kv_heads=0) == SHAPE
+    assert append(lib, fp8, k_pool=None) == NULL
+    assert append(lib, fp8, tok_pos=None) == NULL
+    assert append(lib, fp8, v_new=A + 8) == ALIGN
+    assert append(lib, fp8, n_tok=0, k_new=None) == OK
+    if fp8:
+        assert append(lib, fp8, k_scale=None) == NULL
+
+
+def attn(lib, **kw):
+    args = dict(q=A, cache_dtype=0, k_pool=A, v_pool=A, k_scale=A, v_scale=A, block_table=A,
+                bt_stride=600, seq_lens=A, max_seq_len=9000, abort=None, out=A, sm_scale=0.088,
+                batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=16,
+                num_pages=40000, partition_tokens=0, workspace=A, workspace_bytes=1 << 40,
+                stream=None)
+    args.update(kw)
+    return lib.paged_decode_attn(*args.values())
+
+
+def test_attention_rejects_bad_arguments(lib):
+    assert attn(lib, head_dim=64) == UNSUP
+    assert attn(lib, page_size=8) == UNSUP
+    assert attn(lib, num_q_heads=60) == SHAPE                 # not a multiple of 8
+    assert attn(lib, num_q_heads=8 * 17) == UNSUP             # group of 17 > 16
+    assert attn(lib, cache_dtype=7) == UNSUP
+    assert attn(lib, partition_tokens=100) == UNSUP           # not a multiple of 16
+    assert attn(lib, partition_tokens=32768) == UNSUP         # above the maximum
+    assert attn(lib, batch=-2) == SHAPE
+    assert attn(lib, q=None) == NULL
+    assert attn(lib, k_scale=None) == NULL                    # FP8 needs scales
+    assert attn(lib, out=A + 4) == ALIGN
+    assert attn(lib, workspace=None, partition_tokens=512) == WORKSPACE
+    assert attn(lib, workspace_bytes=16, partition_tokens=512) == WORKSPACE
+    assert attn(lib, batch=0, q=None) == OK
+
+
+def test_workspace_and_partition_sizing(lib):
+    import fp8_e4m3_paged_amd as k
+    # one partition covers everything: no workspace
+    assert k.paged_decode_attn_workspace_bytes(64, 64, 8, 8000, 8192) == 0
+    # C5-like: 16 requests, 64 heads, 131073 tokens at 512 -> 257 partitions
+    n = 16 * 64 * 257
+    ml = -(-(n * 2 * 4) // 256) * 256
+    assert k.paged_decode_attn_workspace_bytes(16, 64, 8, 131073, 512) == ml + n * 128 * 4
+    for b, h, L in [(64, 8, 9193), (1, 1, 256), (16, 8, 131073), (8, 8, 8192)]:
+        pt = k.paged_decode_attn_partition_tokens(b, h, L, 0)
+        assert pt % 16 == 0 and 16 <= pt <= 16384
+    assert k.paged_decode_attn_partition_tokens(64, 8, 9193, 512) == 512
+    with pytest.raises(k.KvError):
+        k.paged_decode_attn_partition_tokens(64, 8, 9193, 24)
+
+
+@pytest.mark.parametrize("key", sorted(OFFSETS))
+def test_tile_layouts_are_permutations(key):
+    off = OFFSETS[key]
+    assert sorted(off.ravel().tolist()) == list(range(16 * 128))
+
+
+def test_device_hash_twin_matches_host_on_cpu_torch():
+    wl = synth.c2_mixed()
+    seq = torch.tensor([0, 3, 3, 7], dtype=torch.int32)
+    pos = torch.tensor([0, 5, 1500, int(wl.seq_lens0[7])], dtype=torch.int32)
+    for kind in ("k", "v"):
+        got = sd.kv_bits_tokens(wl, 0, kind, seq, pos).numpy().view(np.uint16)
+        for i in range(4):
+            b, t = int(seq[i]), int(pos[i])
+            assert np.array_equal(got[i], wl.kv_bits(0, kind, b, t, t + 1)[0])

@@ -1,0 +1,324 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: E4M3 codes and abort masks bit-exact; attention within rel-L2 <= 1e-3
+and max |err| <= 5e-3 on identical dequantized inputs (the pools are checked
+bit-exact first); aborted / empty / unmapped requests exactly zero.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import e4m3, paged
+from synth.device import DeviceState
+from tests import helpers
+from tests.gpu_harness import (DEV, OracleRun, device_pool_logical, gpu_step, oracle_request,
+                               say, sm_scale_for, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import fp8_e4m3_paged_amd as k
+    k.load()            # fails loudly if the library was not built
+    return k
+
+
+# ---------------------------------------------------------------------------
+# exhaustive encode: every bf16 bit pattern through the bulk append
+# ---------------------------------------------------------------------------
+def _encode_scales():
+    rng = np.random.default_rng(2024)
+    fixed = [1.0, 0.5, 2.0, 8.0, 2.0 ** -7, 2.0 ** -20, 2.0 ** 20, 448.0 / 448.0]
+    rnd = np.exp(rng.uniform(np.log(1e-4), np.log(30.0), 104))
+    return np.array(fixed + list(rnd), dtype=np.float32)
+
+
+def test_append_quant_every_bf16_value_many_scales(kv):
+    hkv, ntok = 4, 128                     # 128 tokens x 4 heads x 128 dims = 65536 values
+    say("exhaustive encode: 112 scales x 65536 bf16 patterns, K and V")
+    vals = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(ntok, hkv, 128)
+    vvals = vals[::-1].copy()
+    bt = torch.arange(8, dtype=torch.int32, device=DEV).view(1, 8)
+    seq = torch.zeros(ntok, dtype=torch.int32, device=DEV)
+    pos = torch.arange(ntok, dtype=torch.int32, device=DEV)
+    kn = torch.from_numpy(vals.view(np.int16)).to(DEV)
+    vn = torch.from_numpy(vvals.view(np.int16)).to(DEV)
+    scales = _encode_scales()
+    for i in range(0, len(scales), hkv):
+        ks = scales[i:i + hkv]
+        vs = scales[::-1][i:i + hkv]
+        kp = torch.zeros((8, hkv, 2048), dtype=torch.uint8, device=DEV)
+        vp = torch.zeros((8, hkv, 2048), dtype=torch.uint8, device=DEV)
+        kv.kv_append_quant(kn, vn, seq, pos, bt, torch.from_numpy(ks).to(DEV),
+                           torch.from_numpy(vs.copy()).to(DEV), kp, vp)
+        torch.cuda.synchronize()
+        klog = helpers.tiles_to_logical(kp.cpu().numpy(), "k", "fp8")     # [page][g][16][128]
+        vlog = helpers.tiles_to_logical(vp.cpu().numpy(), "v", "fp8")
+        kgot = klog.transpose(0, 2, 1, 3).reshape(ntok, hkv, 128)
+        vgot = vlog.transpose(0, 2, 1, 3).reshape(ntok, hkv, 128)
+        kwant = e4m3.quantize(vals, ks[None, :, None])
+        vwant = e4m3.quantize(vvals, vs[None, :, None])
+        bad = np.argwhere(kgot != kwant)
+        assert bad.size == 0, (f"K scale set {ks}: {len(bad)} codes differ, first "
+                               f"x=0x{int(vals[tuple(bad[0])]):04x} got 0x{int(kgot[tuple(bad[0])]):02x}"
+                               f" want 0x{int(kwant[tuple(bad[0])]):02x}")
+        assert np.array_equal(vgot, vwant), f"V scale set {vs}"
+
+
+def test_append_bf16_is_a_copy(kv):
+    hkv, ntok = 4, 128
+    vals = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(ntok, hkv, 128)
+    bt = torch.arange(8, dtype=torch.int32, device=DEV).view(1, 8)
+    seq = torch.zeros(ntok, dtype=torch.int32, device=DEV)
+    pos = torch.arange(ntok, dtype=torch.int32, device=DEV)
+    kn = torch.from_numpy(vals.view(np.int16)).to(DEV)
+    kp = torch.zeros((8, hkv, 2048), dtype=torch.int16, device=DEV)
+    vp = torch.zeros((8, hkv, 2048), dtype=torch.int16, device=DEV)
+    kv.kv_append_bf16(kn, kn, seq, pos, bt, kp, vp)
+    torch.cuda.synchronize()
+    for pool, kind in ((kp, "k"), (vp, "v")):
+        lg = helpers.tiles_to_logical(pool.cpu().numpy().view(np.uint16), kind, "bf16")
+        assert np.array_equal(lg.transpose(0, 2, 1, 3).reshape(ntok, hkv, 128), vals)
+
+
+# ---------------------------------------------------------------------------
+# whole decode steps on the small configurations, everything compared
+# ---------------------------------------------------------------------------
+def _full_step_check(kv, wl, cache="fp8", partition_tokens=0, label=""):
+    say(f"{label}: build device state ({wl.name}, {cache})")
+    st = DeviceState(wl, kv, cache=cache, device=DEV)
+    orc = OracleRun(st)
+    for layer in st.layers:
+        kd, vd = device_pool_logical(st, layer)
+        assert np.array_equal(kd, orc.kp[layer]), f"{label}: K pool after fill, layer {layer}"
+        assert np.array_equal(vd, orc.vp[layer]), f"{label}: V pool after fill, layer {layer}"
+    say(f"{label}: step 0")
+    ab, outs, inputs = gpu_step(st, 0, partition_tokens=partition_tokens)
+    ab_o, outs_o = orc.step(0, inputs)
+    assert np.array_equal(ab, ab_o), f"{label}: abort {ab} vs oracle {ab_o}"
+    for layer in st.layers:
+        kd, vd = device_pool_logical(st, layer)
+        assert np.array_equal(kd, orc.kp[layer]), f"{label}: K pool after append"
+        assert np.array_equal(vd, orc.vp[layer]), f"{label}: V pool after append"
+        rel, mx = helpers.check_attention(outs[layer], outs_o[layer],
+                                          zero_rows=np.flatnonzero(ab), label=label)
+        say(f"{label}: layer {layer} rel_l2={rel:.2e} max_abs={mx:.2e}")
+    return st, orc, ab
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_c1_tiny_step(kv, cache):
+    st, _, ab = _full_step_check(kv, synth.c1_tiny(), cache, label=f"c1/{cache}")
+    assert not ab.any()
+
+
+@pytest.mark.parametrize("partition_tokens", [0, 512])
+def test_c2_mixed_step_with_stale_tag(kv, partition_tokens):
+    wl = synth.c2_mixed()
+    _, _, ab = _full_step_check(kv, wl, "fp8", partition_tokens, label=f"c2/p{partition_tokens}")
+    assert np.flatnonzero(ab).tolist() == list(wl.stale)
+
+
+def test_c2_bf16_step(kv):
+    wl = synth.c2_mixed()
+    _, _, ab = _full_step_check(kv, wl, "bf16", 1024, label="c2/bf16")
+    assert np.flatnonzero(ab).tolist() == list(wl.stale)
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------
+def _attn(kv, st, layer, step, partition_tokens=0, sm=None, block_table=None, k_pool=None,
+          v_pool=None, abort=None, max_seq_len=None):
+    wl = st.wl
+    q, _, _ = st.step_layer_inputs(layer, step)
+    msl = max_seq_len or wl.max_seq_len
+    out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"), device=DEV)
+    kv.paged_decode_attn(q, st.k_pool[layer] if k_pool is None else k_pool,
+                         st.v_pool[layer] if v_pool is None else v_pool, st.k_scale[layer],
+                         st.v_scale[layer], st.block_table if block_table is None else block_table,
+                         st.seq_lens(step) - 1, msl, out,
+                         sm_scale_for(wl) if sm is None else sm,
+                         workspace=workspace(wl, partition_tokens, msl), abort=abort,
+                         partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), q
+
+
+def test_partition_size_independence_and_page_permutation(kv):
+    wl = synth.c2_mixed()
+    st = DeviceState(wl, kv, device=DEV)
+    base, _ = _attn(kv, st, 0, 0, partition_tokens=16384)
+    for pt in (16, 32, 48, 512, 1024, 4096, 0):
+        out, _ = _attn(kv, st, 0, 0, partition_tokens=pt)
+        helpers.check_attention(out, base, label=f"partition {pt} vs one partition")
+    # move every physical page to a new place: the output must not change at all
+    perm = np.random.default_rng(5).permutation(wl.num_pages)
+    inv = torch.from_numpy(np.argsort(perm).astype(np.int32)).to(DEV)
+    permt = torch.from_numpy(perm.astype(np.int64)).to(DEV)
+    kp2 = st.k_pool[0][permt].contiguous()
+    vp2 = st.v_pool[0][permt].contiguous()
+    bt2 = st.block_table.clone()
+    m = (bt2 >= 0) & (bt2 < wl.num_pages)
+    bt2[m] = inv[bt2[m].long()]
+    for pt in (0, 512):
+        a, _ = _attn(kv, st, 0, 0, partition_tokens=pt)
+        b, _ = _attn(kv, st, 0, 0, partition_tokens=pt, block_table=bt2, k_pool=kp2, v_pool=vp2)
+        assert np.array_equal(a, b)
+
+
+def test_zero_temperature_is_mean_of_v(kv):
+    wl = synth.c2_mixed()
+    st = DeviceState(wl, kv, device=DEV)
+    out, _ = _attn(kv, st, 0, 0, sm=0.0, partition_tokens=1024)
+    vlog = device_pool_logical(st, 0)[1]
+    for b in range(wl.batch):
+        L = int(wl.seq_lens0[b])
+        V = paged.dequant_request(vlog, wl.block_table[b], L, 16, st.v_scale_host[0], "fp8")
+        want = np.repeat(V.mean(axis=1), wl.num_q_heads // wl.num_kv_heads, axis=0)
+        helpers.check_attention(out[b:b + 1], want[None], label=f"mean V, request {b}")
+
+
+# ---------------------------------------------------------------------------
+# edge cases on a hand-made state
+# ---------------------------------------------------------------------------
+def _edge_state(kv, cache, hq, hkv, lens, pool_pages=40, nan_fill=True):
+    """Pool pages pre-filled with stale bytes (NaN codes included) before the
+    requests' tokens are appended, so unwritten slots hold garbage."""
+    rng = np.random.default_rng(99)
+    batch = len(lens)
+    need = [max(1, -(-L // 16)) for L in lens]
+    perm = rng.permutation(pool_pages).astype(np.int32)
+    bt = np.full((batch, max(need) + 1), -1, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        bt[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    dt = torch.uint8 if cache == "fp8" else torch.int16
+    if cache == "fp8":
+        junk = rng.integers(0, 256, (pool_pages, hkv, 2048)).astype(np.uint8)
+        if nan_fill:
+            junk[:, :, ::7] = 0x7F
+        kp = torch.from_numpy(junk).to(DEV)
+        vp = torch.from_numpy(junk[::-1].copy()).to(DEV)
+    else:
+        junk = rng.integers(0, 65536, (pool_pages, hkv, 2048)).astype(np.uint16)
+        if nan_fill:
+            junk[:, :, ::7] = 0x7FC0
+        kp = torch.from_numpy(junk.view(np.int16)).to(DEV)
+        vp = torch.from_numpy(junk[::-1].copy().view(np.int16)).to(DEV)
+    assert kp.dtype == dt
+    # append real tokens for every position < L
+    seqs = np.concatenate([np.full(L, b, np.int32) for b, L in enumerate(lens)] + [np.zeros(0, np.int32)])
+    poss = np.concatenate([np.arange(L, dtype=np.int32) for L in lens] + [np.zeros(0, np.int32)])
+    kvals = synth._f32_to_bf16_bits(rng.normal(0, 1, (len(seqs), hkv, 128)).astype(np.float32))
+    vvals = synth._f32_to_bf16_bits(rng.normal(0, 0.5, (len(seqs), hkv, 128)).astype(np.float32))
+    ks = np.full(hkv, 4.3 / 448, dtype=np.float32) * (1 + np.arange(hkv, dtype=np.float32) / 8)
+    vs = np.full(hkv, 2.2 / 448, dtype=np.float32)
+    btt = torch.from_numpy(bt).to(DEV)
+    kst, vst = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    if len(seqs):
+        args = (torch.from_numpy(kvals.view(np.int16)).to(DEV),
+                torch.from_numpy(vvals.view(np.int16)).to(DEV),
+                torch.from_numpy(seqs).to(DEV), torch.from_numpy(poss).to(DEV), btt)
+        if cache == "fp8":
+            kv.kv_append_quant(*args, kst, vst, kp, vp)
+        else:
+            kv.kv_append_bf16(*args, kp, vp)
+    q = synth._f32_to_bf16_bits(rng.normal(0, 1, (batch, hq, 128)).astype(np.float32))
+    torch.cuda.synchronize()
+    return dict(bt=bt, btt=btt, kp=kp, vp=vp, ks=ks, vs=vs, kst=kst, vst=vst, q=q,
+                lens=np.array(lens, np.int32))
+
+
+def _edge_run(kv, e, cache, lens=None, abort=None, max_seq_len=None, partition_tokens=0,
+              bt=None):
+    lens = e["lens"] if lens is None else np.asarray(lens, np.int32)
+    batch, hq, _ = e["q"].shape
+    msl = int(lens.max()) if max_seq_len is None else max_seq_len
+    out = torch.full((batch, hq, 128), float("nan"), device=DEV)
+    n = kv.paged_decode_attn_workspace_bytes(batch, hq, e["kp"].shape[1], msl, partition_tokens)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV)
+    btt = e["btt"] if bt is None else torch.from_numpy(bt).to(DEV)
+    kv.paged_decode_attn(torch.from_numpy(e["q"].view(np.int16)).to(DEV), e["kp"], e["vp"],
+                         e["kst"] if cache == "fp8" else None,
+                         e["vst"] if cache == "fp8" else None, btt,
+                         torch.from_numpy(lens).to(DEV), msl, out, 0.0883883,
+                         workspace=ws,
+                         abort=None if abort is None else torch.from_numpy(
+                             np.asarray(abort, np.uint8)).to(DEV),
+                         partition_tokens=partition_tokens,
+                         cache_dtype=0 if cache == "fp8" else 1)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _edge_oracle(e, cache, lens, abort=None, bt=None):
+    kt = e["kp"].cpu().numpy()
+    vt = e["vp"].cpu().numpy()
+    if cache == "bf16":
+        kt, vt = kt.view(np.uint16), vt.view(np.uint16)
+    kl = helpers.tiles_to_logical(kt, "k", cache)
+    vl = helpers.tiles_to_logical(vt, "v", cache)
+    return paged.decode_attn(e["q"], kl, vl, e["ks"], e["vs"], e["bt"] if bt is None else bt,
+                             np.asarray(lens, np.int32), 0.0883883, cache, abort)
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2), (4, 4), (32, 2)])
+def test_edge_lengths_groups_and_garbage_slots(kv, cache, hq, hkv):
+    lens = [1, 2, 15, 16, 17, 31, 33, 100, 0, 47]
+    e = _edge_state(kv, cache, hq, hkv, lens)
+    for pt in (0, 16, 32, 64):
+        got = _edge_run(kv, e, cache, partition_tokens=pt)
+        want = _edge_oracle(e, cache, lens)
+        helpers.check_attention(got, want, zero_rows=[8], label=f"edge {cache} G={hq//hkv} p{pt}")
+        # one token: exactly V0 (dequantized), the first check of the decode path
+        assert np.allclose(got[0], want[0], rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_edge_abort_bad_ids_and_overlong(kv, cache):
+    lens = [20, 40, 5, 64, 16]
+    e = _edge_state(kv, cache, 8, 1, lens)
+    bt = e["bt"].copy()
+    bt[1, 1] = 10 ** 6          # request 1 reads an out-of-pool page
+    bt[3, 0] = -5               # request 3 too
+    abort = [0, 0, 1, 0, 0]     # request 2 aborted by the tag check
+    for pt in (0, 16):
+        got = _edge_run(kv, e, cache, abort=abort, partition_tokens=pt, bt=bt)
+        want = _edge_oracle(e, cache, lens, abort=np.array(abort, np.uint8), bt=bt)
+        helpers.check_attention(got, want, zero_rows=[1, 2, 3], label=f"abort/bad {cache} p{pt}")
+    # a length above max_seq_len, or beyond the table row, is refused (zeros)
+    got = _edge_run(kv, e, cache, lens=[20, 40, 5, 64, 16], max_seq_len=39)
+    assert np.all(got[1] == 0) and np.all(got[3] == 0) and np.any(got[0] != 0)
+    got = _edge_run(kv, e, cache, lens=[20, 40, 5, 16 * e["bt"].shape[1] + 1, 16])
+    assert np.all(got[3] == 0)
+
+
+def test_verify_tags_cases(kv):
+    rng = np.random.default_rng(17)
+    num_pages, batch, width = 300, 9, 40
+    tags = rng.integers(0, 2 ** 32, num_pages, dtype=np.uint64).astype(np.uint32)
+    bt = rng.integers(0, num_pages, (batch, width)).astype(np.int32)
+    exp = tags[bt].copy()
+    lens = np.array([0, 1, 16, 17, 640, 641, -3, 300, 200], np.int32)
+    bt[2, 1] = -1                      # past request 2's pages: ignored
+    bt[3, 1] = -1                      # request 3 reads it: abort
+    exp[4, 39] ^= 1                    # last page of request 4: abort
+    exp[7, 19] ^= 1 << 31              # request 7 (300 tokens = 19 pages): page 19 not read
+    exp[8, 12] ^= 1                    # request 8: abort
+    assert paged.verify_tags(tags, bt, exp, lens, 16).tolist() == [0, 0, 0, 1, 1, 1, 1, 0, 1]
+    cases = [lens, np.full(batch, 0, np.int32), np.full(batch, 640, np.int32)]
+    for ls in cases:
+        want = paged.verify_tags(tags, bt, exp, ls, 16)
+        ab = torch.full((batch,), 7, dtype=torch.uint8, device=DEV)
+        kv.kv_verify_tags(torch.from_numpy(tags.view(np.int32)).to(DEV),
+                          torch.from_numpy(bt).to(DEV),
+                          torch.from_numpy(exp.view(np.int32)).to(DEV),
+                          torch.from_numpy(ls).to(DEV), ab)
+        torch.cuda.synchronize()
+        assert np.array_equal(ab.cpu().numpy(), want), (ls, ab.cpu().numpy(), want)

@@ -15,7 +15,7 @@ def test_fmix32_known_values():
         h = (h * 0xC2B2AE35) & 0xFFFFFFFF
         h ^= h >> 16
         return h
-    xs = np.array([0, 1, 2, 12345, 0xFFFFFFFF, 0x80000000, 0xDEADBEEF], dtype=np.uint64)
+    xs = np.array([0, 1, 2, 12345, 0xFFFFFFFF, 0x80000000, 0xDEADBEEF], dtype=np.uint32)
     assert synth.fmix32(xs).tolist() == [ref(int(x)) for x in xs]
 
 
