@@ -81,8 +81,10 @@ hipError_t launch_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
 // ---------------------------------------------------------------------------
 // Append. Grid: x = token n, y = slice of the token's (K|V, head, 4-dim group)
 // work items; each thread handles 4 consecutive dims of one head of K or V.
-// FP8: x / s in correctly rounded fp32 (the default HIP division), clamp to
-// +-448, hardware round-to-nearest-even convert. BF16: stored as is.
+// FP8: x / s rounded to fp32 with round-to-odd (correctly rounded division
+// plus the sign of the exact fma remainder), clamp to +-448, then the
+// hardware round-to-nearest-even convert; together this is round-to-nearest-
+// even of the exact quotient. BF16: stored as is.
 // ---------------------------------------------------------------------------
 constexpr int kAppendThreads = 256;
 
@@ -119,10 +121,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 
     if constexpr (FP8) {
         const float s = (is_v ? v_scale : k_scale)[g];
-        const float y0 = bf16_bits_to_float(raw.x & 0xFFFF) / s;
-        const float y1 = bf16_bits_to_float(raw.x >> 16) / s;
-        const float y2 = bf16_bits_to_float(raw.y & 0xFFFF) / s;
-        const float y3 = bf16_bits_to_float(raw.y >> 16) / s;
+        const float y0 = div_round_odd(bf16_bits_to_float(raw.x & 0xFFFF), s);
+        const float y1 = div_round_odd(bf16_bits_to_float(raw.x >> 16), s);
+        const float y2 = div_round_odd(bf16_bits_to_float(raw.y & 0xFFFF), s);
+        const float y3 = div_round_odd(bf16_bits_to_float(raw.y >> 16), s);
         const uint32_t codes = encode4_e4m3(y0, y1, y2, y3);
         uint8_t* base = (is_v ? v_pool : k_pool) + tile * kTileFp8;
         if (!is_v) {

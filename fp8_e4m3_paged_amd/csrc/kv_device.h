@@ -56,7 +56,26 @@ __device__ inline float clamp448(float y) {
     return (y != y) ? 0.0f : fminf(fmaxf(y, -448.0f), 448.0f);
 }
 
-// Four floats (already x / s) -> four e4m3 codes packed little-endian.
+// x / s rounded to fp32 with round-to-odd. The correctly rounded quotient y
+// alone is not enough: with bf16 x and s = amax / 448 the exact quotient is
+// often a hair away from an e4m3 midpoint, y then lands exactly on the
+// midpoint and the final round-half-even picks the wrong side. The fma
+// remainder r = x - y*s is exact, so the sign of r/s says on which side of y
+// the exact quotient lies; truncating toward zero and forcing the last bit to
+// 1 when inexact gives round-to-odd, and a round-to-odd value with >= 4 + 2
+// significand bits rounds to E4M3 exactly as the exact quotient would.
+__device__ inline float div_round_odd(float x, float s) {
+    const float y = x / s;                       // correctly rounded (IEEE) division
+    if (!(fabsf(y) < INFINITY) || y == 0.0f) return y;
+    const float r = fmaf(-y, s, x);
+    if (r == 0.0f) return y;                     // exact quotient
+    uint32_t u = __float_as_uint(y);
+    const bool toward_zero = ((r < 0.0f) != (s < 0.0f)) != (y < 0.0f);
+    if (toward_zero) u -= 1u;                    // |y| - 1 ulp: the truncated quotient
+    return __uint_as_float(u | 1u);
+}
+
+// Four floats (already x / s, round-to-odd) -> four e4m3 codes, little-endian.
 __device__ inline uint32_t encode4_e4m3(float y0, float y1, float y2, float y3) {
     uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y0), clamp448(y1), 0u, false);
     pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y2), clamp448(y3), pk, true);

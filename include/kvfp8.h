@@ -46,9 +46,11 @@
  * sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN =
  * S.1111.111, largest finite 448. Stored code = round-to-nearest-even of
  * x / s with saturation to +-448 (+-inf included), NaN -> 0x7F/0xFF keeping
- * the sign, and the sign kept on zero; x / s is the correctly rounded fp32
- * quotient, which gives the same code as rounding the exact quotient. The
- * value read back is code * s. s is one fp32 scale per (layer, KV head) for
+ * the sign, and the sign kept on zero, where x / s is the EXACT quotient
+ * (the kernels round it to fp32 with round-to-odd first, from the correctly
+ * rounded quotient and its exact fma remainder, so the second rounding cannot
+ * be misled by a quotient that lands on an e4m3 midpoint). The value read
+ * back is code * s. s is one fp32 scale per (layer, KV head) for
  * K and one for V, supplied by the caller (positive and finite).
  *
  * Pool layout. Each layer has a K pool and a V pool, each an array of

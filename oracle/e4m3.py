@@ -148,10 +148,16 @@ def quantize(x_bf16_bits, scale) -> np.ndarray:
     """Codes for bf16 values x stored with fp32 scale s: ENC(x / s).
 
     The quotient is formed in float64 from the exact bf16 and fp32 operands
-    (one rounding at 53 bits) and then rounded to E4M3. Because 53 >= 2*4 + 2,
-    rounding twice gives the same code as rounding the exact rational x/s
-    once (the double-rounding condition for division, Figueroa 1995), so
-    this is round-to-nearest-even of x/s itself.
+    (one rounding at 53 bits) and then rounded to E4M3; this equals rounding
+    the exact rational x/s once. Rounding to 53 bits is monotone, so the two
+    can only differ if the float64 quotient lands exactly on an E4M3 midpoint
+    M (5 significant bits) while x/s != M. Write x = X 2^a (X an integer of at
+    most 8 bits), s = S 2^b (at most 24 bits) and M = m 2^c (at most 5 bits).
+    Then X 2^n and m S (n = a - b - c, moving the power of two to whichever
+    side keeps both integral) are integers whose difference is at most
+    2^(8+5+24) 2^-53 < 1 in magnitude, hence zero: x/s would be M exactly.
+    (With only 24 bits, as in a plain fp32 division, the bound is 2^13 and
+    the midpoint trap is real; see the tests.)
     """
     x = bf16_bits_to_f64(x_bf16_bits)
     s = np.asarray(scale, dtype=np.float32).astype(np.float64)

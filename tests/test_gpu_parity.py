@@ -30,15 +30,22 @@ def kv():
 # exhaustive encode: every bf16 bit pattern through the bulk append
 # ---------------------------------------------------------------------------
 def _encode_scales():
+    """Powers of two, random fp32 scales, and fp32(amax / 448) for bf16 amax
+    values: the last kind puts many exact quotients a hair off an E4M3
+    midpoint, where rounding the fp32 quotient alone would go wrong."""
     rng = np.random.default_rng(2024)
     fixed = [1.0, 0.5, 2.0, 8.0, 2.0 ** -7, 2.0 ** -20, 2.0 ** 20, 448.0 / 448.0]
-    rnd = np.exp(rng.uniform(np.log(1e-4), np.log(30.0), 104))
-    return np.array(fixed + list(rnd), dtype=np.float32)
+    rnd = np.exp(rng.uniform(np.log(1e-4), np.log(30.0), 100))
+    allv = e4m3.bf16_bits_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    cand = np.unique(np.abs(allv[np.isfinite(allv) & (np.abs(allv) > 1e-3) & (np.abs(allv) < 1e3)]))
+    amax = rng.choice(cand, size=100, replace=False).astype(np.float32) / np.float32(448)
+    tiny = [float(np.float32(a) / np.float32(448)) for a in (4.0625, 2.15625, 4.3125, 2.1875)]
+    return np.array(fixed + list(rnd) + list(amax) + tiny, dtype=np.float32)
 
 
 def test_append_quant_every_bf16_value_many_scales(kv):
     hkv, ntok = 4, 128                     # 128 tokens x 4 heads x 128 dims = 65536 values
-    say("exhaustive encode: 112 scales x 65536 bf16 patterns, K and V")
+    say("exhaustive encode: 212 scales x 65536 bf16 patterns, K and V")
     vals = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(ntok, hkv, 128)
     vvals = vals[::-1].copy()
     bt = torch.arange(8, dtype=torch.int32, device=DEV).view(1, 8)
@@ -47,6 +54,7 @@ def test_append_quant_every_bf16_value_many_scales(kv):
     kn = torch.from_numpy(vals.view(np.int16)).to(DEV)
     vn = torch.from_numpy(vvals.view(np.int16)).to(DEV)
     scales = _encode_scales()
+    assert len(scales) % hkv == 0
     for i in range(0, len(scales), hkv):
         ks = scales[i:i + hkv]
         vs = scales[::-1][i:i + hkv]

@@ -194,3 +194,46 @@ def test_planted_tie_rule_mistake_is_caught():
     tie_away = np.where(a >= 448, 0x7E, tie_away).astype(np.uint8)
     good = e4m3.encode(np.abs(y)) & 0x7F
     assert np.any(tie_away[~np.isnan(y)] != good[~np.isnan(y)])
+
+
+def _amax_scales(n=40, seed=5):
+    """fp32(amax / 448) for bf16 amax values: the scale shape the cache uses."""
+    rng = np.random.default_rng(seed)
+    v = all_bf16_values()
+    cand = np.unique(np.abs(v[np.isfinite(v) & (np.abs(v) > 1e-3) & (np.abs(v) < 1e3)]))
+    return (rng.choice(cand, size=n, replace=False).astype(np.float32) / np.float32(448))
+
+
+def test_quantize_is_exact_on_every_near_tie_of_amax_scales():
+    """With s = amax/448 the exact quotient often sits a hair off an E4M3
+    midpoint. Every such near-tie (float64 quotient within 2^-30 relative of
+    a midpoint) is checked against exact rational rounding."""
+    x_bits = ALL_BF16[np.isfinite(all_bf16_values())]
+    x = e4m3.bf16_bits_to_f64(x_bits)
+    mags = e4m3.DECODE[:0x7F]
+    mids = (mags[:-1] + mags[1:]) / 2
+    checked = 0
+    for s in _amax_scales():
+        q = np.abs(x / np.float64(s))
+        i = np.clip(np.searchsorted(mids, q), 1, len(mids) - 1)
+        near = np.minimum(np.abs(q - mids[i - 1]), np.abs(q - mids[i])) <= q * 2.0 ** -30
+        got = e4m3.quantize(x_bits[near], s)
+        for xb, g in zip(x_bits[near], got):
+            xv = e4m3.bf16_bits_to_f64(np.array([xb]))[0]
+            assert g == _rne_exact(Fraction(xv) / Fraction(float(s))), (hex(int(xb)), float(s))
+            checked += 1
+    assert checked > 100
+
+
+def test_plain_fp32_quotient_would_double_round():
+    """The trap the GPU encoder must avoid: rounding the correctly rounded
+    fp32 quotient gives wrong codes for amax/448 scales (so a GPU encoder
+    that passes the exhaustive test with these scales is not doing that)."""
+    x_bits = ALL_BF16[np.isfinite(all_bf16_values())]
+    x32 = e4m3.bf16_bits_to_f64(x_bits).astype(np.float32)
+    wrong = 0
+    with np.errstate(over="ignore"):
+        for s in _amax_scales(12):
+            plain = e4m3.encode((x32 / np.float32(s)).astype(np.float64))
+            wrong += int((plain != e4m3.quantize(x_bits, s)).sum())
+    assert wrong > 0
