@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--mode", default="step", choices=["step", "copy"],
+                    help="copy: time a plain device copy of --copy-mib MiB (counter calibration)")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
 
 
@@ -113,7 +116,7 @@ def cpu_baseline(args, wl, scales, step_index):
     sm = 1.0 / math.sqrt(wl.head_dim)
     done, t_total, per_req = 0, 0.0, []
     with threadpool_limits(limits=1):
-        while t_total < args.cpu_seconds and done < 64:
+        while t_total < args.cpu_seconds and done < 600:
             for (b, L, kp, vp, bt, tags, q, kn, vn) in prepared:
                 kp2, vp2 = kp.copy(), vp.copy()
                 t0 = time.perf_counter()
@@ -144,8 +147,34 @@ def cpu_baseline(args, wl, scales, step_index):
     }
 
 
+def copy_calibration(args):
+    """A plain device-to-device copy of known size: the reference that HBM
+    byte counters are scaled by."""
+    import torch
+    n = args.copy_mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "ms_per_copy": round(ms, 4), "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
+
+
 def main():
     args = parse()
+    if args.mode == "copy":
+        copy_calibration(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)

@@ -53,12 +53,14 @@ __device__ inline void load_pair(PairTiles<FP8>& r, const uint8_t* __restrict__ 
     const uint8_t* kb = k_pool + tile_b * T + 16 * lane;
     const uint8_t* va = v_pool + tile_a * T + 16 * lane;
     const uint8_t* vb = v_pool + tile_b * T + 16 * lane;
+    // The cache is streamed once per step: non-temporal loads keep it from
+    // displacing reusable lines in the caches.
 #pragma unroll
     for (int h = 0; h < PairTiles<FP8>::N; ++h) {
-        r.ka[h] = *reinterpret_cast<const u32x4*>(ka + 1024 * h);
-        r.kb[h] = *reinterpret_cast<const u32x4*>(kb + 1024 * h);
-        r.va[h] = *reinterpret_cast<const u32x4*>(va + 1024 * h);
-        r.vb[h] = *reinterpret_cast<const u32x4*>(vb + 1024 * h);
+        r.ka[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ka + 1024 * h));
+        r.kb[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + 1024 * h));
+        r.va[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(va + 1024 * h));
+        r.vb[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + 1024 * h));
     }
 }
 
@@ -111,6 +113,88 @@ __device__ inline void mask_v(u32x4 (&v)[PairTiles<FP8>::N], int valid) {
             v[h][1] &= hi;
             v[h][2] &= lo;
             v[h][3] &= hi;
+        }
+    }
+}
+
+// One page pair of the online softmax: scores of pages a and b (tokens
+// tok_a .. tok_a + 31), masking past t_end, running max / sum update and the
+// P.V accumulation. Wave-uniform control flow only (MFMA needs all lanes).
+template <bool FP8>
+__device__ inline void process_pair(PairTiles<FP8>& cur, int tok_a, int t_end, int jgrp,
+                                    float s_scale, const bf16x8 (&qop)[4], float& m_run,
+                                    float& l_run, f32x4 (&acc_o)[8]) {
+    const int tok_b = tok_a + kPage;
+    // Tokens past t_end (the tail of the last page, or a missing page b)
+    // must not contribute: mask their scores and zero their V bytes
+    // (the slots may hold stale codes, NaN included).
+    if (tok_b + kPage > t_end) {
+        mask_v<FP8>(cur.va, t_end - (tok_a + 4 * jgrp));
+        mask_v<FP8>(cur.vb, t_end - (tok_b + 4 * jgrp));
+    }
+    const f32x4 sa = qk_page<FP8>(cur.ka, qop);
+    const f32x4 sb = qk_page<FP8>(cur.kb, qop);
+    float s[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        s[r] = (tok_a + 4 * jgrp + r < t_end) ? sa[r] * s_scale : -INFINITY;
+        s[4 + r] = (tok_b + 4 * jgrp + r < t_end) ? sb[r] * s_scale : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float pv[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        pv[r] = exp2f(s[r] - m_use);
+        psum += pv[r];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc_o[c] *= alpha;
+
+    if constexpr (FP8) {
+        // B = P^T: slots 0..3 = page a tokens 4j..4j+3, 4..7 = page b.
+        f16x8 P;
+#pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+            const f16x2 h2 = __builtin_convertvector((f32x2{pv[r], pv[r + 1]}), f16x2);
+            P[r] = h2[0];
+            P[r + 1] = h2[1];
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            // A = V^T: row = dim 16c + col, slots = tokens 4j..4j+3 of
+            // page a then of page b (dword c%4 of load c/4).
+            f16x2 a0, a1, b0, b1;
+            decode4_f16(cur.va[c / 4][c % 4], a0, a1);
+            decode4_f16(cur.vb[c / 4][c % 4], b0, b1);
+            const f16x8 A = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+            acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, P, acc_o[c], 0, 0, 0);
+        }
+    } else {
+        // P = hi + lo, both bf16: hi = RNE(p), lo = RNE(p - hi).
+        bf16x8 Ph, Pl;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const __bf16 h = static_cast<__bf16>(pv[r]);
+            Ph[r] = h;
+            Pl[r] = static_cast<__bf16>(pv[r] - static_cast<float>(h));
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const u32x4 w = {cur.va[c / 2][2 * (c % 2)], cur.va[c / 2][2 * (c % 2) + 1],
+                             cur.vb[c / 2][2 * (c % 2)], cur.vb[c / 2][2 * (c % 2) + 1]};
+            const bf16x8 A = __builtin_bit_cast(bf16x8, w);
+            acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Ph, acc_o[c], 0, 0, 0);
+            acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pl, acc_o[c], 0, 0, 0);
         }
     }
 }
@@ -199,96 +283,52 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
             return static_cast<size_t>(id) * hkv + g;
         };
 
-        int pr = wave;
-        PairTiles<FP8> cur;
-        if (pr < npairs) {
-            const int ia = 2 * pr, ib = min(2 * pr + 1, npg - 1);
-            load_pair<FP8>(cur, k_pool, v_pool, tile_of(ia), tile_of(ib), lane);
-        }
-        for (; pr < npairs; pr += kWaves) {
-            // Prefetch the wave's next pair (or re-read the current one at the
-            // end, which hits in cache) before touching the current registers.
-            PairTiles<FP8> nxt;
-            {
-                const int pn = (pr + kWaves < npairs) ? pr + kWaves : pr;
-                const int ia = 2 * pn, ib = min(2 * pn + 1, npg - 1);
-                load_pair<FP8>(nxt, k_pool, v_pool, tile_of(ia), tile_of(ib), lane);
-            }
-            const int tok_a = (pg0 + 2 * pr) * kPage;       // first token of page a
-            const int tok_b = tok_a + kPage;
-            // Tokens past t_end (the tail of the last page, or a missing page b)
-            // must not contribute: mask their scores and zero their V bytes
-            // (the slots may hold stale codes, NaN included).
-            if (tok_b + kPage > t_end) {
-                mask_v<FP8>(cur.va, t_end - (tok_a + 4 * jgrp));
-                mask_v<FP8>(cur.vb, t_end - (tok_b + 4 * jgrp));
-            }
-            const f32x4 sa = qk_page<FP8>(cur.ka, qop);
-            const f32x4 sb = qk_page<FP8>(cur.kb, qop);
-            float s[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s[r] = (tok_a + 4 * jgrp + r < t_end) ? sa[r] * s_scale : -INFINITY;
-                s[4 + r] = (tok_b + 4 * jgrp + r < t_end) ? sb[r] * s_scale : -INFINITY;
-            }
-            float mx = s[0];
-#pragma unroll
-            for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run - m_use);
-            float pv[8];
-            float psum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                pv[r] = exp2f(s[r] - m_use);
-                psum += pv[r];
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc_o[c] *= alpha;
-
+        // This wave's pairs are wave, wave + 4, ...; n_w of them. Register
+        // buffers rotate: while one pair is processed the next ones are in
+        // flight (two for FP8, one for BF16). Loads are never skipped (past
+        // the end they re-read the wave's last pair, which is cached), so
+        // every wait is static.
+        const int n_w = npairs > wave ? (npairs - wave + kWaves - 1) / kWaves : 0;
+        const auto issue = [&](PairTiles<FP8>& t, int i) {
+            const int pr = wave + kWaves * min(i, n_w - 1);
+            load_pair<FP8>(t, k_pool, v_pool, tile_of(2 * pr), tile_of(min(2 * pr + 1, npg - 1)),
+                           lane);
+        };
+        const auto first_token = [&](int i) { return (pg0 + 2 * (wave + kWaves * i)) * kPage; };
+        if (n_w > 0) {
             if constexpr (FP8) {
-                // B = P^T: slots 0..3 = page a tokens 4j..4j+3, 4..7 = page b.
-                f16x8 P;
-#pragma unroll
-                for (int r = 0; r < 8; r += 2) {
-                    const f16x2 h2 = __builtin_convertvector((f32x2{pv[r], pv[r + 1]}), f16x2);
-                    P[r] = h2[0];
-                    P[r + 1] = h2[1];
-                }
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    // A = V^T: row = dim 16c + col, slots = tokens 4j..4j+3 of
-                    // page a then of page b (dword c%4 of load c/4).
-                    f16x2 a0, a1, b0, b1;
-                    decode4_f16(cur.va[c / 4][c % 4], a0, a1);
-                    decode4_f16(cur.vb[c / 4][c % 4], b0, b1);
-                    const f16x8 A = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
-                    acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, P, acc_o[c], 0, 0, 0);
+                PairTiles<FP8> t0, t1, t2;
+                issue(t0, 0);
+                issue(t1, 1);
+                issue(t2, 2);
+                for (int i = 0; i < n_w; i += 3) {
+                    process_pair<FP8>(t0, first_token(i), t_end, jgrp, s_scale, qop, m_run,
+                                      l_run, acc_o);
+                    issue(t0, i + 3);
+                    if (i + 1 < n_w)
+                        process_pair<FP8>(t1, first_token(i + 1), t_end, jgrp, s_scale, qop,
+                                          m_run, l_run, acc_o);
+                    issue(t1, i + 4);
+                    if (i + 2 < n_w)
+                        process_pair<FP8>(t2, first_token(i + 2), t_end, jgrp, s_scale, qop,
+                                          m_run, l_run, acc_o);
+                    issue(t2, i + 5);
                 }
             } else {
-                // P = hi + lo, both bf16: hi = RNE(p), lo = RNE(p - hi).
-                bf16x8 Ph, Pl;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const __bf16 h = static_cast<__bf16>(pv[r]);
-                    Ph[r] = h;
-                    Pl[r] = static_cast<__bf16>(pv[r] - static_cast<float>(h));
-                }
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const u32x4 w = {cur.va[c / 2][2 * (c % 2)], cur.va[c / 2][2 * (c % 2) + 1],
-                                     cur.vb[c / 2][2 * (c % 2)], cur.vb[c / 2][2 * (c % 2) + 1]};
-                    const bf16x8 A = __builtin_bit_cast(bf16x8, w);
-                    acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Ph, acc_o[c], 0, 0, 0);
-                    acc_o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Pl, acc_o[c], 0, 0, 0);
+                // BF16 tiles are twice as large: two buffers fit the registers.
+                PairTiles<FP8> t0, t1;
+                issue(t0, 0);
+                issue(t1, 1);
+                for (int i = 0; i < n_w; i += 2) {
+                    process_pair<FP8>(t0, first_token(i), t_end, jgrp, s_scale, qop, m_run,
+                                      l_run, acc_o);
+                    issue(t0, i + 2);
+                    if (i + 1 < n_w)
+                        process_pair<FP8>(t1, first_token(i + 1), t_end, jgrp, s_scale, qop,
+                                          m_run, l_run, acc_o);
+                    issue(t1, i + 3);
                 }
             }
-            cur = nxt;
         }
     }
 

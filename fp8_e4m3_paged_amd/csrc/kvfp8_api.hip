@@ -33,18 +33,19 @@ int check_append_common(const void* k_new, const void* v_new, const int32_t* tok
     return KV_OK;
 }
 
-// Automatic split-K size: enough (partition, request, KV head) workgroups to
-// keep every compute unit streaming (at least ~4 per CU of the 256), but no
-// partition shorter than 1024 tokens so that the partial traffic (520 B per
-// query head and partition) stays small next to the KV bytes, and none longer
-// than the maximum the kernel's LDS page list holds.
+// Automatic split-K size. Long partitions stream best (the per-workgroup
+// set-up and the partial traffic are amortised, and no reduction pass is
+// needed with one partition), so split only as far as needed to give every
+// compute unit at least two (request, KV head, partition) workgroups: 512 of
+// them for the 256 CUs. Partitions are equal shares of max_seq_len rounded up
+// to 256 tokens, at least 512 and at most the LDS page list's capacity.
 int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
     const int64_t items = static_cast<int64_t>(batch) * num_kv_heads;
-    const int64_t target = 1024;
+    const int64_t target = 512;
     int64_t parts = items >= target ? 1 : (target + items - 1) / items;
     int64_t tokens = (static_cast<int64_t>(max_seq_len) + parts - 1) / parts;
     tokens = ((tokens + 255) / 256) * 256;
-    if (tokens < 1024) tokens = 1024;
+    if (tokens < 512) tokens = 512;
     if (tokens > KV_MAX_PARTITION_TOKENS) tokens = KV_MAX_PARTITION_TOKENS;
     return static_cast<int32_t>(tokens);
 }
