@@ -36,6 +36,8 @@ constexpr int kAttnThreads = 256;
 constexpr int kWaves = kAttnThreads / 64;
 constexpr int kAccStride = kDim + 4;           // padded LDS row (floats)
 constexpr float kLog2e = 1.4426950408889634f;
+// Partitions up to this many tokens run one per wavefront (see the kernel).
+constexpr int kWaveModeMaxTokens = 2048;
 
 // Raw registers of one page pair: K and V tiles of pages a and b.
 template <bool FP8>
@@ -199,7 +201,61 @@ __device__ inline void process_pair(PairTiles<FP8>& cur, int tok_a, int t_end, i
     }
 }
 
-template <bool FP8>
+// Software pipeline over a wavefront's n page pairs: register buffers rotate
+// so that while one pair is processed the next ones are in flight (two for
+// FP8, one for BF16, whose tiles take twice the registers). Every load in the
+// steady-state loop is unconditional (the index is clamped to the last pair),
+// so each wait is a static partial vmcnt; the FP8 epilogue issues only the
+// loads that are still needed.
+template <bool FP8, typename Issue, typename Proc>
+__device__ inline void pipeline_pairs(int n, Issue&& issue, Proc&& proc) {
+    if (n <= 0) return;
+    if constexpr (FP8) {
+        PairTiles<FP8> t0, t1, t2;
+        issue(t0, 0);
+        issue(t1, 1);
+        issue(t2, 2);
+        int i = 0;
+        for (; i + 5 < n; i += 3) {
+            proc(t0, i);
+            issue(t0, i + 3);
+            proc(t1, i + 1);
+            issue(t1, i + 4);
+            proc(t2, i + 2);
+            issue(t2, i + 5);
+        }
+        // 1..5 pairs left: t0, t1, t2 hold pairs i, i+1, i+2 (when they exist)
+        proc(t0, i);
+        if (i + 3 < n) issue(t0, i + 3);
+        if (i + 1 < n) proc(t1, i + 1);
+        if (i + 4 < n) issue(t1, i + 4);
+        if (i + 2 < n) proc(t2, i + 2);
+        if (i + 3 < n) proc(t0, i + 3);
+        if (i + 4 < n) proc(t1, i + 4);
+    } else {
+        // BF16: no separate epilogue (its straight-line copies of the pair step
+        // exceed the register file); past the end the clamped loads re-read
+        // the wave's last pair.
+        PairTiles<FP8> t0, t1;
+        issue(t0, 0);
+        issue(t1, 1);
+        for (int i = 0; i < n; i += 2) {
+            proc(t0, i);
+            issue(t0, i + 2);
+            if (i + 1 < n) proc(t1, i + 1);
+            issue(t1, i + 3);
+        }
+    }
+}
+
+// Partition kernel. Grid: blockIdx.x = (slot * batch + b) * hkv + g.
+//   WAVE_PARTS = false: slot = partition p; the 4 wavefronts share it (pairs
+//     w, w + 4, ...) and merge in LDS; used for long partitions.
+//   WAVE_PARTS = true: slot covers partitions 4*slot .. 4*slot + 3 of (b, g),
+//     one per wavefront, each written straight from registers; used for
+//     short partitions, where sharing would leave each wave too few pairs to
+//     keep its pipeline full.
+template <bool FP8, bool WAVE_PARTS>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
@@ -210,17 +266,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
     int32_t part_tokens, int32_t n_parts) {
     extern __shared__ float smem[];
     const int group = hq / hkv;
-    // LDS: [wave][16] max, [wave][16] sum, [wave][group][kAccStride] output,
-    // and the partition's page ids (aliasing nothing used at the same time).
+    // LDS: [wave][16] max, [wave][16] sum, [wave][group][kAccStride] output
+    // (shared mode only), then the page ids of the partition(s).
     float* sm_m = smem;
     float* sm_l = sm_m + kWaves * 16;
     float* sm_acc = sm_l + kWaves * 16;
-    int32_t* sm_ids = reinterpret_cast<int32_t*>(sm_acc + kWaves * group * kAccStride);
+    int32_t* sm_ids =
+        reinterpret_cast<int32_t*>(sm_acc + (WAVE_PARTS ? 0 : kWaves * group * kAccStride));
 
     const int bid = blockIdx.x;
     const int g = bid % hkv;
     const int b = (bid / hkv) % batch;
-    const int p = bid / (hkv * batch);
+    const int slot = bid / (hkv * batch);
     const int tid = threadIdx.x;
     const int wave = tid / 64;
     const int lane = tid % 64;
@@ -231,29 +288,38 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
     const bool aborted = abort != nullptr && abort[b] != 0;
     const bool valid_req = !aborted && L >= 1 && L <= max_seq_len &&
                            (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
-    const int t_begin = p * part_tokens;
-    if (!valid_req || t_begin >= L) {
+    const int p_first = WAVE_PARTS ? slot * kWaves : slot;
+    if (!valid_req || static_cast<int64_t>(p_first) * part_tokens >= L) {
         // Only the single-partition case owns the final output here; with
         // several partitions the reduction writes zeros for such requests.
-        if (n_parts == 1) {
+        if (!WAVE_PARTS && n_parts == 1) {
             for (int i = tid; i < group * kDim; i += kAttnThreads)
                 out[(static_cast<size_t>(b) * hq + g * group) * kDim + i] = 0.f;
         }
         return;
     }
-    const int t_end = min(L, t_begin + part_tokens);
+    const int p = WAVE_PARTS ? p_first + wave : slot;
+    const int t_begin = p * part_tokens;
+    const bool active = t_begin < L;            // always true in shared mode
+    const int t_end = active ? min(L, t_begin + part_tokens) : t_begin;
     const int pg0 = t_begin / kPage;
-    const int npg = (t_end + kPage - 1) / kPage - pg0;
+    const int npg = active ? (t_end + kPage - 1) / kPage - pg0 : 0;
     const int npairs = (npg + 1) / 2;
 
-    // Page ids of the partition -> LDS; any id outside the pool poisons the
-    // request (its output becomes zero and no page of it is read).
+    // Page ids -> LDS; any id outside the pool poisons the request (its output
+    // becomes zero and no page of it is read). In wave mode every partition of
+    // the workgroup belongs to the same request, so one verdict serves all.
+    int32_t* ids = WAVE_PARTS ? sm_ids + wave * (part_tokens / kPage) : sm_ids;
     int bad = 0;
-    const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
-    for (int k = tid; k < npg; k += kAttnThreads) {
-        const int32_t id = bt_row[k];
-        bad |= (id < 0 || id >= num_pages);
-        sm_ids[k] = id;
+    {
+        const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
+        const int first = WAVE_PARTS ? lane : tid;
+        const int step = WAVE_PARTS ? 64 : kAttnThreads;
+        for (int k = first; k < npg; k += step) {
+            const int32_t id = bt_row[k];
+            bad |= (id < 0 || id >= num_pages);
+            ids[k] = id;
+        }
     }
     bad = __syncthreads_or(bad);
 
@@ -279,101 +345,81 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
         const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
 
         const auto tile_of = [&](int page_idx) -> size_t {
-            const int id = __builtin_amdgcn_readfirstlane(sm_ids[page_idx]);
+            const int id = __builtin_amdgcn_readfirstlane(ids[page_idx]);
             return static_cast<size_t>(id) * hkv + g;
         };
-
-        // This wave's pairs are wave, wave + 4, ...; n_w of them. Register
-        // buffers rotate: while one pair is processed the next ones are in
-        // flight (two for FP8, one for BF16). Loads are never skipped (past
-        // the end they re-read the wave's last pair, which is cached), so
-        // every wait is static.
-        const int n_w = npairs > wave ? (npairs - wave + kWaves - 1) / kWaves : 0;
+        // This wave's pairs: shared mode w, w + 4, ...; wave mode all of them.
+        const int first = WAVE_PARTS ? 0 : wave;
+        const int stride = WAVE_PARTS ? 1 : kWaves;
+        const int n_w = npairs > first ? (npairs - first + stride - 1) / stride : 0;
         const auto issue = [&](PairTiles<FP8>& t, int i) {
-            const int pr = wave + kWaves * min(i, n_w - 1);
+            const int pr = first + stride * min(i, n_w - 1);
             load_pair<FP8>(t, k_pool, v_pool, tile_of(2 * pr), tile_of(min(2 * pr + 1, npg - 1)),
                            lane);
         };
-        const auto first_token = [&](int i) { return (pg0 + 2 * (wave + kWaves * i)) * kPage; };
-        if (n_w > 0) {
-            if constexpr (FP8) {
-                PairTiles<FP8> t0, t1, t2;
-                issue(t0, 0);
-                issue(t1, 1);
-                issue(t2, 2);
-                for (int i = 0; i < n_w; i += 3) {
-                    process_pair<FP8>(t0, first_token(i), t_end, jgrp, s_scale, qop, m_run,
-                                      l_run, acc_o);
-                    issue(t0, i + 3);
-                    if (i + 1 < n_w)
-                        process_pair<FP8>(t1, first_token(i + 1), t_end, jgrp, s_scale, qop,
-                                          m_run, l_run, acc_o);
-                    issue(t1, i + 4);
-                    if (i + 2 < n_w)
-                        process_pair<FP8>(t2, first_token(i + 2), t_end, jgrp, s_scale, qop,
-                                          m_run, l_run, acc_o);
-                    issue(t2, i + 5);
-                }
-            } else {
-                // BF16 tiles are twice as large: two buffers fit the registers.
-                PairTiles<FP8> t0, t1;
-                issue(t0, 0);
-                issue(t1, 1);
-                for (int i = 0; i < n_w; i += 2) {
-                    process_pair<FP8>(t0, first_token(i), t_end, jgrp, s_scale, qop, m_run,
-                                      l_run, acc_o);
-                    issue(t0, i + 2);
-                    if (i + 1 < n_w)
-                        process_pair<FP8>(t1, first_token(i + 1), t_end, jgrp, s_scale, qop,
-                                          m_run, l_run, acc_o);
-                    issue(t1, i + 3);
-                }
-            }
-        }
+        const auto proc = [&](PairTiles<FP8>& t, int i) {
+            process_pair<FP8>(t, (pg0 + 2 * (first + stride * i)) * kPage, t_end, jgrp, s_scale,
+                              qop, m_run, l_run, acc_o);
+        };
+        pipeline_pairs<FP8>(n_w, issue, proc);
     }
 
-    // ---- merge the 4 wavefronts ------------------------------------------
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    __syncthreads();   // sm_ids is no longer read; LDS is reused below
-    if (jgrp == 0) {
-        sm_m[wave * 16 + col] = m_run;
-        sm_l[wave * 16 + col] = l_tot;
-    }
-    if (col < group) {
-        float* row = sm_acc + (wave * group + col) * kAccStride;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-            *reinterpret_cast<f32x4*>(row + 16 * c + 4 * jgrp) = acc_o[c];
-    }
-    __syncthreads();
 
-    const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
-    for (int it = tid; it < group * (kDim / 4); it += kAttnThreads) {
-        const int qh = it / (kDim / 4);
-        const int d = (it % (kDim / 4)) * 4;
-        float M = -INFINITY;
+    if constexpr (WAVE_PARTS) {
+        // ---- one partition per wavefront: write its partial directly -----
+        if (!active || col >= group) return;
+        const size_t pslot = (q_row + col) * n_parts + p;
+        float* dst = part_acc + pslot * kDim + 4 * jgrp;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        float lt = 0.f;
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = exp2f(sm_m[w * 16 + qh] - M_use);
-            lt += f * sm_l[w * 16 + qh];
-            o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
+        for (int c = 0; c < 8; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc_o[c];
+        if (jgrp == 0) {
+            part_ml[2 * pslot] = m_run;
+            part_ml[2 * pslot + 1] = bad ? -1.f : l_tot;
         }
-        if (n_parts == 1) {
-            f32x4 r = {0.f, 0.f, 0.f, 0.f};
-            if (!bad && lt > 0.f) r = o * (vs / lt);
-            *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
-        } else {
-            const size_t slot = (q_row + qh) * n_parts + p;
-            *reinterpret_cast<f32x4*>(part_acc + slot * kDim + d) = o;
-            if (d == 0) {
-                part_ml[2 * slot] = M;
-                part_ml[2 * slot + 1] = bad ? -1.f : lt;
+    } else {
+        // ---- merge the 4 wavefronts --------------------------------------
+        __syncthreads();   // the page ids are no longer read; LDS is reused below
+        if (jgrp == 0) {
+            sm_m[wave * 16 + col] = m_run;
+            sm_l[wave * 16 + col] = l_tot;
+        }
+        if (col < group) {
+            float* row = sm_acc + (wave * group + col) * kAccStride;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                *reinterpret_cast<f32x4*>(row + 16 * c + 4 * jgrp) = acc_o[c];
+        }
+        __syncthreads();
+
+        const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
+        for (int it = tid; it < group * (kDim / 4); it += kAttnThreads) {
+            const int qh = it / (kDim / 4);
+            const int d = (it % (kDim / 4)) * 4;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
+            const float M_use = (M == -INFINITY) ? 0.f : M;
+            float lt = 0.f;
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float f = exp2f(sm_m[w * 16 + qh] - M_use);
+                lt += f * sm_l[w * 16 + qh];
+                o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
+            }
+            if (n_parts == 1) {
+                f32x4 r = {0.f, 0.f, 0.f, 0.f};
+                if (!bad && lt > 0.f) r = o * (vs / lt);
+                *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
+            } else {
+                const size_t pslot = (q_row + qh) * n_parts + p;
+                *reinterpret_cast<f32x4*>(part_acc + pslot * kDim + d) = o;
+                if (d == 0) {
+                    part_ml[2 * pslot] = M;
+                    part_ml[2 * pslot + 1] = bad ? -1.f : lt;
+                }
             }
         }
     }
@@ -382,74 +428,131 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
 // Combine the partitions of each (request, query head):
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p acc_p / sum_p w_p l_p
 // Requests that are aborted, empty, too long, or that a partition marked as
-// mapped to an invalid page (l_p < 0) get zeros.
-__global__ __launch_bounds__(kDim) void reduce_partials_kernel(
+// mapped to an invalid page (l_p < 0) get zeros. One 512-thread workgroup
+// per (b, h): the weights go through LDS, then 16 groups of 32 threads (4
+// dims each) sum interleaved partitions with independent, unrolled loads and
+// the 16 group sums are added in LDS.
+constexpr int kReduceThreads = 512;
+
+__device__ inline float block_max(float v, float* red) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    const int w = threadIdx.x / 64;
+    __syncthreads();
+    if (threadIdx.x % 64 == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kReduceThreads / 64; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+
+__device__ inline float block_sum(float v, float* red) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x / 64;
+    __syncthreads();
+    if (threadIdx.x % 64 == 0) red[w] = v;
+    __syncthreads();
+    float r = 0.f;
+    for (int i = 0; i < kReduceThreads / 64; ++i) r += red[i];
+    return r;
+}
+
+__global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_acc,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, int32_t bt_stride,
     const uint8_t* __restrict__ abort, const float* __restrict__ v_scale,
     float* __restrict__ out, int32_t hq, int32_t hkv, int32_t part_tokens, int32_t n_parts) {
+    extern __shared__ float wts[];                  // [n_parts] weights
+    __shared__ float red[kReduceThreads / 64];
     const int bh = blockIdx.x;
     const int b = bh / hq;
     const int h = bh % hq;
-    const int d = threadIdx.x;
+    const int tid = threadIdx.x;
     const int L = seq_lens[b];
     const bool aborted = abort != nullptr && abort[b] != 0;
     const bool valid_req = !aborted && L >= 1 && L <= max_seq_len &&
                            (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
-    float* o = out + static_cast<size_t>(bh) * kDim + d;
-    if (!valid_req) {
-        *o = 0.f;
+    float* o = out + static_cast<size_t>(bh) * kDim;
+    if (!valid_req) {                               // block-uniform
+        if (tid < kDim) o[tid] = 0.f;
         return;
     }
     const int np = (L + part_tokens - 1) / part_tokens;
     const float* ml = part_ml + static_cast<size_t>(bh) * n_parts * 2;
-    const float* acc = part_acc + static_cast<size_t>(bh) * n_parts * kDim + d;
-    float M = -INFINITY;
-    bool bad = false;
-    for (int i = 0; i < np; ++i) {
-        M = fmaxf(M, ml[2 * i]);
+    float mx = -INFINITY;
+    int bad = 0;
+    for (int i = tid; i < np; i += kReduceThreads) {
+        const float m = ml[2 * i];
         bad |= ml[2 * i + 1] < 0.f;
+        wts[i] = m;
+        mx = fmaxf(mx, m);
     }
+    bad = __syncthreads_or(bad);
     if (bad) {
-        *o = 0.f;
+        if (tid < kDim) o[tid] = 0.f;
         return;
     }
-    float lt = 0.f, num = 0.f;
-    for (int i = 0; i < np; ++i) {
-        const float w = exp2f(ml[2 * i] - M);
-        lt += w * ml[2 * i + 1];
-        num += w * acc[static_cast<size_t>(i) * kDim];
+    const float M = block_max(mx, red);
+    float lsum = 0.f;
+    for (int i = tid; i < np; i += kReduceThreads) {
+        const float w = exp2f(wts[i] - M);
+        lsum += w * ml[2 * i + 1];
+        wts[i] = w;
     }
-    const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
-    *o = lt > 0.f ? num * (vs / lt) : 0.f;
+    const float lt = block_sum(lsum, red);          // ends with a barrier: wts is complete
+    const int grp = tid / (kDim / 4);               // 16 groups of 32 threads x 4 dims
+    const int d4 = tid % (kDim / 4);
+    const float* acc = part_acc + static_cast<size_t>(bh) * n_parts * kDim + 4 * d4;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kGroups = kReduceThreads / (kDim / 4);
+#pragma unroll 4
+    for (int i = grp; i < np; i += kGroups)
+        num += wts[i] * *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i) * kDim);
+    __shared__ f32x4 part[kGroups][kDim / 4];
+    part[grp][d4] = num;
+    __syncthreads();
+    if (tid < kDim / 4) {
+        f32x4 t = part[0][tid];
+        for (int k = 1; k < kGroups; ++k) t += part[k][tid];
+        const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
+        const f32x4 r = lt > 0.f ? t * (vs / lt) : f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(o + 4 * tid) = r;
+    }
+}
+
+bool use_wave_partitions(const AttnArgs& a) {
+    return a.num_partitions > 1 && a.partition_tokens <= kWaveModeMaxTokens;
 }
 
 hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
     const int group = a.num_q_heads / a.num_kv_heads;
-    const size_t lds = sizeof(float) * (2 * kWaves * 16 + kWaves * group * kAccStride) +
-                       sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage);
-    const dim3 grid(static_cast<uint32_t>(a.num_partitions) * a.batch * a.num_kv_heads);
+    const bool wave_mode = use_wave_partitions(a);
+    const size_t ids_bytes = sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage) *
+                             (wave_mode ? kWaves : 1);
+    const size_t lds = sizeof(float) * (2 * kWaves * 16 + (wave_mode ? 0 : kWaves * group * kAccStride)) +
+                       ids_bytes;
+    const uint32_t slots = wave_mode ? (a.num_partitions + kWaves - 1) / kWaves : a.num_partitions;
+    const dim3 grid(slots * a.batch * a.num_kv_heads);
     const float sm_log2 = a.sm_scale * kLog2e;
+#define KVFP8_LAUNCH(F8, WP)                                                                     \
+    hipLaunchKernelGGL((attn_partition_kernel<F8, WP>), grid, dim3(kAttnThreads), lds, stream,  \
+                       a.q, static_cast<const uint8_t*>(a.k_pool),                               \
+                       static_cast<const uint8_t*>(a.v_pool), F8 ? a.k_scale : nullptr,          \
+                       F8 ? a.v_scale : nullptr, a.block_table, a.bt_stride, a.seq_lens,         \
+                       a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2, a.batch,   \
+                       a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens,           \
+                       a.num_partitions)
     if (fp8) {
-        hipLaunchKernelGGL(attn_partition_kernel<true>, grid, dim3(kAttnThreads), lds, stream,
-                           a.q, static_cast<const uint8_t*>(a.k_pool),
-                           static_cast<const uint8_t*>(a.v_pool), a.k_scale, a.v_scale,
-                           a.block_table, a.bt_stride, a.seq_lens, a.max_seq_len, a.abort, a.out,
-                           a.part_ml, a.part_acc, sm_log2, a.batch, a.num_q_heads,
-                           a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions);
+        if (wave_mode) KVFP8_LAUNCH(true, true); else KVFP8_LAUNCH(true, false);
     } else {
-        hipLaunchKernelGGL(attn_partition_kernel<false>, grid, dim3(kAttnThreads), lds, stream,
-                           a.q, static_cast<const uint8_t*>(a.k_pool),
-                           static_cast<const uint8_t*>(a.v_pool), nullptr, nullptr,
-                           a.block_table, a.bt_stride, a.seq_lens, a.max_seq_len, a.abort, a.out,
-                           a.part_ml, a.part_acc, sm_log2, a.batch, a.num_q_heads,
-                           a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions);
+        if (wave_mode) KVFP8_LAUNCH(false, true); else KVFP8_LAUNCH(false, false);
     }
+#undef KVFP8_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_partitions == 1) return e;
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3(a.batch * a.num_q_heads), dim3(kDim), 0,
-                       stream, a.part_ml, a.part_acc, a.seq_lens, a.max_seq_len, a.bt_stride,
-                       a.abort, fp8 ? a.v_scale : nullptr, a.out, a.num_q_heads, a.num_kv_heads,
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(a.batch * a.num_q_heads), dim3(kReduceThreads),
+                       sizeof(float) * static_cast<size_t>(a.num_partitions), stream, a.part_ml,
+                       a.part_acc, a.seq_lens, a.max_seq_len, a.bt_stride, a.abort,
+                       fp8 ? a.v_scale : nullptr, a.out, a.num_q_heads, a.num_kv_heads,
                        a.partition_tokens, a.num_partitions);
     return hipGetLastError();
 }

@@ -172,7 +172,7 @@ int paged_decode_attn(const void* q, int32_t cache_dtype, const void* k_pool, co
         (k_scale && misaligned(k_scale, 4)) || (v_scale && misaligned(v_scale, 4)))
         return KV_ERR_ALIGN;
     const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
-    if (parts64 > (1 << 20)) return KV_ERR_SHAPE;
+    if (parts64 > KV_MAX_PARTITIONS) return KV_ERR_UNSUPPORTED;
     const int32_t parts = static_cast<int32_t>(parts64);
     const int64_t blocks = parts64 * batch * num_kv_heads;
     if (blocks > 0x7FFFFFFFLL) return KV_ERR_SHAPE;

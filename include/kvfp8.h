@@ -107,6 +107,7 @@ typedef enum { KV_CACHE_FP8_E4M3 = 0, KV_CACHE_BF16 = 1 } kv_cache_dtype;
 #define KV_HEAD_DIM 128
 #define KV_MAX_GROUP 16
 #define KV_MAX_PARTITION_TOKENS 16384
+#define KV_MAX_PARTITIONS 8192        /* ceil(max_seq_len / partition_tokens) */
 
 /*
  * Batched page-tag check (the separate batch operation the pages describe).
@@ -209,8 +210,9 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * [head_dim], fully written. k_scale/v_scale: fp32 [num_kv_heads] (may be
  * NULL for the BF16 cache). workspace: device memory of at least
  * paged_decode_attn_workspace_bytes(...) bytes (may be NULL when that is 0).
- * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE,
- * KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED (also when
+ * ceil(max_seq_len / partition_tokens) exceeds KV_MAX_PARTITIONS),
+ * KV_ERR_WORKSPACE, KV_ERR_ALIGN, KV_ERR_LAUNCH.
  */
 int paged_decode_attn(const void* q, int32_t cache_dtype,
                       const void* k_pool, const void* v_pool,

@@ -156,12 +156,18 @@ class Workload:
         return self.k_sigma if kind == "k" else self.v_sigma
 
     def kv_bits(self, layer: int, kind: str, b: int, t0: int, t1: int) -> np.ndarray:
-        """bf16 bits [t1 - t0][Hkv][D] of tokens t0..t1-1 of request b."""
+        """bf16 bits [t1 - t0][Hkv][D] of tokens t0..t1-1 of request b.
+
+        Counter of (t, g, d) = (t * Hkv + g) * D + d, evaluated head by head."""
+        return np.stack([self.kv_bits_head(layer, kind, b, g, t0, t1)
+                         for g in range(self.num_kv_heads)], axis=1)
+
+    def kv_bits_head(self, layer: int, kind: str, b: int, g: int, t0: int, t1: int) -> np.ndarray:
+        """bf16 bits [t1 - t0][D] of KV head g only (the same values as kv_bits)."""
         hkv, d = self.num_kv_heads, self.head_dim
-        t = np.arange(t0, t1, dtype=np.uint32)[:, None, None]
-        g = np.arange(hkv, dtype=np.uint32)[None, :, None]
-        j = np.arange(d, dtype=np.uint32)[None, None, :]
-        ctr = (t * np.uint32(hkv) + g) * np.uint32(d) + j
+        t = np.arange(t0, t1, dtype=np.uint32)[:, None]
+        j = np.arange(d, dtype=np.uint32)[None, :]
+        ctr = (t * np.uint32(hkv) + np.uint32(g)) * np.uint32(d) + j
         return normal_bf16(self._kv_key(layer, kind, b), ctr, self.kv_sigma(kind))
 
     def new_token_bits(self, layer: int, kind: str, step: int) -> np.ndarray:
