@@ -33,6 +33,28 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 
+# HBM bytes per attention launch of the headline workload from two rocprofv3
+# --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
+# reads for a plain 1 GiB device copy (fetch x2.000, write x1.000); valid only
+# for the kernel sources they were taken on (sha256 prefix of decode_attn.hip
+# + kv_device.h). See profiles/attn_partition_kernel_c4_hbm_counters.md.
+COUNTER_TRAFFIC = {
+    "source_sha": "ef9310e3a1752f40",
+    "workload": "c4_headline",
+    "read_bytes": 1.143e9,
+    "write_bytes": 2.097e6,
+    "algorithmic_bytes": 1144619443,
+}
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode_attn.hip", "kv_device.h"):
+        with open(os.path.join(ROOT, "fp8_e4m3_paged_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -45,6 +67,8 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="split-K partition size; -1 = the workload's own (0 = automatic)")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--verify-cost", default="on", choices=["on", "off"],
+                    help="also time as many steps with the no-op tracker (no tag check)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--quiet", action="store_true")
@@ -147,6 +171,11 @@ def cpu_baseline(args, wl, scales, step_index):
     }
 
 
+def max_len_partition(max_len: int) -> int:
+    """The single-partition size the headline workload runs with (auto)."""
+    return ((max_len + 255) // 256) * 256
+
+
 def copy_calibration(args):
     """A plain device-to-device copy of known size: the reference that HBM
     byte counters are scaled by."""
@@ -190,7 +219,8 @@ def main():
     kv.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
-    total_steps = args.warmup + args.steps
+    measure_noop = args.verify == "on" and args.verify_cost == "on"
+    total_steps = args.warmup + args.steps * (2 if measure_noop else 1)
     make = {"c3": synth.c3_uniform, "c4": synth.c4_headline, "c5": synth.c5_skewed}[args.config]
     wl = make(max_steps=total_steps)
     pt = wl.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
@@ -226,13 +256,13 @@ def main():
     cd = kv.KV_CACHE_FP8_E4M3 if fp8 else kv.KV_CACHE_BF16
     sm = 1.0 / math.sqrt(wl.head_dim)
     stream = torch.cuda.current_stream()
-    abort = st.abort if verify else None
 
     ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps * wl.num_layers)]
 
-    def run_step(s, timed_slot=None):
-        if verify:
+    def run_step(s, timed_slot=None, check=verify):
+        abort = st.abort if check else None
+        if check:
             kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens[s],
                               st.abort, stream=stream)
         for layer in range(wl.num_layers):
@@ -282,6 +312,28 @@ def main():
     log(args, f"{ms_per_step:.3f} ms/step, {gbs:.0f} GB/s, attention call {attn_avg_ms*1e3:.1f} us "
               f"= {attn_gbs:.0f} GB/s")
 
+    noop = None
+    if measure_noop:
+        # the same number of steps with the no-op tracker: no tag check, abort = NULL
+        a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a2.record(stream)
+        for i in range(args.steps):
+            run_step(args.warmup + args.steps + i, check=False)
+        b2.record(stream)
+        torch.cuda.synchronize()
+        off_ms = a2.elapsed_time(b2)
+        by_off = [step_bytes(wl, wl.seq_lens_at(args.warmup + args.steps + i), cache, False)
+                  for i in range(args.steps)]
+        kv_on = sum(b["kv_per_layer"] for b in by)
+        kv_off = sum(b["kv_per_layer"] for b in by_off)
+        # per KV byte, so the 20 tokens the contexts grew in between do not count
+        overhead = (elapsed_ms / kv_on) / (off_ms / kv_off) - 1.0
+        noop = {"ms_per_step": round(off_ms / args.steps, 4),
+                "tag_check_overhead_pct": round(100.0 * overhead, 2)}
+        log(args, f"no-op tracker: {off_ms / args.steps:.3f} ms/step; tag check costs "
+                  f"{100 * overhead:.2f}%")
+
     cpu = None
     if args.cpu_baseline == "on" and fp8:
         log(args, "timing the CPU oracle on a bounded sample")
@@ -289,6 +341,11 @@ def main():
         sec_per_seq_step = 1.0 / cpu["value"]
         mean_bytes_per_seq_step = total_bytes / args.steps / wl.batch
         cpu["effective_GBps"] = mean_bytes_per_seq_step / sec_per_seq_step / 1e9
+
+    traffic = None
+    if (fp8 and wl.name == COUNTER_TRAFFIC["workload"] and pt_eff == max_len_partition(max_len)
+            and kernel_source_sha() == COUNTER_TRAFFIC["source_sha"]):
+        traffic = int(COUNTER_TRAFFIC["read_bytes"] + COUNTER_TRAFFIC["write_bytes"])
 
     result = {
         "metric": "paged FP8-KV decode attn: achieved HBM GB/s + seq-steps/s at B=64, ctx=8k",
@@ -319,11 +376,12 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_launch_us": round(attn_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": int(attn_bytes),
         },
         "cpu_baseline": cpu,
+        "no_op_tracker": noop,
     }
     print(json.dumps(result), flush=True)
 
