@@ -220,7 +220,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
     measure_noop = args.verify == "on" and args.verify_cost == "on"
-    total_steps = args.warmup + args.steps * (2 if measure_noop else 1)
+    # timed passes of --steps steps each: the step itself (no per-kernel events,
+    # which would add gaps), the attention calls bracketed by events, and
+    # optionally the no-op tracker
+    total_steps = args.warmup + args.steps * (3 if measure_noop else 2)
     make = {"c3": synth.c3_uniform, "c4": synth.c4_headline, "c5": synth.c5_skewed}[args.config]
     wl = make(max_steps=total_steps)
     pt = wl.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
@@ -290,23 +293,33 @@ def main():
         assert int(st.abort.sum().item()) == 0, "no request of this workload may abort"
     log(args, f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
+    # pass 1: the timed steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        run_step(args.warmup + i, timed_slot=i * wl.num_layers)
+        run_step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(end)
     ms_per_step = elapsed_ms / args.steps
+
+    # pass 2: the next steps again, each attention call bracketed by events on
+    # its launch stream (the event pair also spans the call's dispatch latency)
+    base2 = args.warmup + args.steps
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        run_step(base2 + i, timed_slot=i * wl.num_layers)
+    torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in ev_attn]
     attn_avg_ms = float(np.mean(attn_ms))
 
     by = [step_bytes(wl, wl.seq_lens_at(args.warmup + i), cache, verify)
           for i in range(args.steps)]
+    by2 = [step_bytes(wl, wl.seq_lens_at(base2 + i), cache, verify) for i in range(args.steps)]
     total_bytes = sum(b["total"] for b in by)
     gbs = total_bytes / (elapsed_ms * 1e-3) / 1e9
-    attn_bytes = float(np.mean([b["attn_per_layer"] for b in by]))
+    attn_bytes = float(np.mean([b["attn_per_layer"] for b in by2]))
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     seq_steps = wl.batch * args.steps / (elapsed_ms * 1e-3)
     log(args, f"{ms_per_step:.3f} ms/step, {gbs:.0f} GB/s, attention call {attn_avg_ms*1e3:.1f} us "
@@ -318,16 +331,17 @@ def main():
         a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a2.record(stream)
+        base3 = args.warmup + 2 * args.steps
         for i in range(args.steps):
-            run_step(args.warmup + args.steps + i, check=False)
+            run_step(base3 + i, check=False)
         b2.record(stream)
         torch.cuda.synchronize()
         off_ms = a2.elapsed_time(b2)
-        by_off = [step_bytes(wl, wl.seq_lens_at(args.warmup + args.steps + i), cache, False)
+        by_off = [step_bytes(wl, wl.seq_lens_at(base3 + i), cache, False)
                   for i in range(args.steps)]
         kv_on = sum(b["kv_per_layer"] for b in by)
         kv_off = sum(b["kv_per_layer"] for b in by_off)
-        # per KV byte, so the 20 tokens the contexts grew in between do not count
+        # per KV byte, so the tokens the contexts grew in between do not count
         overhead = (elapsed_ms / kv_on) / (off_ms / kv_off) - 1.0
         noop = {"ms_per_step": round(off_ms / args.steps, 4),
                 "tag_check_overhead_pct": round(100.0 * overhead, 2)}

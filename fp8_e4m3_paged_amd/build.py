@@ -31,7 +31,7 @@ def command(out: str = LIB, extra=()) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function",
+        "-Wall", "-Wno-unused-function", "-I", os.path.join(os.path.dirname(HERE), "include"),
         *extra,
         "-o", out,
         *[os.path.join(CSRC, s) for s in SOURCES],

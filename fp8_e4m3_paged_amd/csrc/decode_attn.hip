@@ -66,27 +66,33 @@ __device__ inline void load_pair(PairTiles<FP8>& r, const uint8_t* __restrict__ 
     }
 }
 
-// S^T (16 tokens x 16 query columns) of one page: 4 MFMAs over head_dim.
+// A operand of QK^T MFMA c for one page: slot i <- dim 32j + 8c + i, which is
+// bytes 8(c%2)..+7 of the lane's load c/2 (FP8, decoded to bf16) or load c
+// itself (BF16).
 template <bool FP8>
-__device__ inline f32x4 qk_page(const u32x4 (&k)[PairTiles<FP8>::N], const bf16x8 (&qop)[4]) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+__device__ inline bf16x8 k_operand(const u32x4 (&k)[PairTiles<FP8>::N], int c) {
+    if constexpr (FP8) {
+        bf16x2 p0, p1, p2, p3;
+        decode4_bf16(k[c / 2][2 * (c % 2)], p0, p1);
+        decode4_bf16(k[c / 2][2 * (c % 2) + 1], p2, p3);
+        return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    } else {
+        return __builtin_bit_cast(bf16x8, k[c]);
+    }
+}
+
+// S^T (16 tokens x 16 query columns) of pages a and b: two chains of 4 MFMAs
+// over head_dim, interleaved so neither waits on its own previous result.
+template <bool FP8>
+__device__ inline void qk_pair(const PairTiles<FP8>& t, const bf16x8 (&qop)[4], f32x4& sa,
+                               f32x4& sb) {
+    sa = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        bf16x8 a;
-        if constexpr (FP8) {
-            // slot i of MFMA c <- dim 32j + 8c + i = bytes 8(c%2)..+7 of load c/2
-            const uint32_t w0 = k[c / 2][2 * (c % 2)];
-            const uint32_t w1 = k[c / 2][2 * (c % 2) + 1];
-            bf16x2 p0, p1, p2, p3;
-            decode4_bf16(w0, p0, p1);
-            decode4_bf16(w1, p2, p3);
-            a = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        } else {
-            a = __builtin_bit_cast(bf16x8, k[c]);
-        }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[c], acc, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(t.ka, c), qop[c], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(t.kb, c), qop[c], sb, 0, 0, 0);
     }
-    return acc;
 }
 
 // Zero the bytes of tokens >= valid in a lane's 4-token groups (FP8: 1 byte
@@ -119,48 +125,71 @@ __device__ inline void mask_v(u32x4 (&v)[PairTiles<FP8>::N], int valid) {
     }
 }
 
-// One page pair of the online softmax: scores of pages a and b (tokens
-// tok_a .. tok_a + 31), masking past t_end, running max / sum update and the
-// P.V accumulation. Wave-uniform control flow only (MFMA needs all lanes).
+// Running-max slack (log2 units): the reference max m_run only moves when a
+// new score exceeds it by more than this, so most pairs skip the rescale of
+// the output accumulators. Probabilities then stay <= 2^8, which f16 holds
+// with full precision; the normaliser is built against the same reference.
+constexpr float kMaxSlack = 8.0f;
+
+// One page pair of the online softmax: raw scores of pages a and b (tokens
+// tok_a .. tok_a + 31), the running max / sum update and the P.V accumulation.
+// s_scale = sm_scale * k_scale * log2(e) >= 0 multiplies the raw q.k sums, so
+// the max is taken on raw sums and the scale is folded into exp2's argument.
+// Only the pair that crosses t_end needs masking. Control flow is
+// wave-uniform (MFMA needs all lanes).
 template <bool FP8>
 __device__ inline void process_pair(PairTiles<FP8>& cur, int tok_a, int t_end, int jgrp,
                                     float s_scale, const bf16x8 (&qop)[4], float& m_run,
                                     float& l_run, f32x4 (&acc_o)[8]) {
     const int tok_b = tok_a + kPage;
-    // Tokens past t_end (the tail of the last page, or a missing page b)
-    // must not contribute: mask their scores and zero their V bytes
-    // (the slots may hold stale codes, NaN included).
-    if (tok_b + kPage > t_end) {
+    const bool tail = tok_b + kPage > t_end;
+    if (tail) {
+        // Tokens past t_end (the tail of the last page, or a missing page b)
+        // must not contribute: their V bytes are zeroed (the slots may hold
+        // stale codes, NaN included) and their scores masked below.
         mask_v<FP8>(cur.va, t_end - (tok_a + 4 * jgrp));
         mask_v<FP8>(cur.vb, t_end - (tok_b + 4 * jgrp));
     }
-    const f32x4 sa = qk_page<FP8>(cur.ka, qop);
-    const f32x4 sb = qk_page<FP8>(cur.kb, qop);
-    float s[8];
+    f32x4 sa, sb;
+    qk_pair<FP8>(cur, qop, sa, sb);
+    float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+    if (tail) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        s[r] = (tok_a + 4 * jgrp + r < t_end) ? sa[r] * s_scale : -INFINITY;
-        s[4 + r] = (tok_b + 4 * jgrp + r < t_end) ? sb[r] * s_scale : -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+            if (tok_a + 4 * jgrp + r >= t_end) s[r] = -INFINITY;
+            if (tok_b + 4 * jgrp + r >= t_end) s[4 + r] = -INFINITY;
+        }
     }
-    float mx = s[0];
+    // This lane's 8 scores; only if one of them exceeds the reference by the
+    // slack (always on the first pair, where m_run is -inf) does the wave take
+    // the column max over the 4 lanes of each column and rescale.
+    const float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                           fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))) * s_scale;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kMaxSlack) != 0) {
+        float mcol = fmaxf(mx, __shfl_xor(mx, 16));
+        mcol = fmaxf(mcol, __shfl_xor(mcol, 32));
+        const float m_new = fmaxf(m_run, mcol);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);    // 0 when m_run = -inf
+        l_run *= alpha;
 #pragma unroll
-    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+        for (int c = 0; c < 8; ++c) acc_o[c] *= alpha;
+        m_run = m_new;
+    }
     float pv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(s[r], s_scale, -m_run));
+    if (tail) {
+        // explicit zeros: with s_scale == 0 the masked -inf would give NaN
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (tok_a + 4 * jgrp + r >= t_end) pv[r] = 0.f;
+            if (tok_b + 4 * jgrp + r >= t_end) pv[4 + r] = 0.f;
+        }
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        pv[r] = exp2f(s[r] - m_use);
-        psum += pv[r];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc_o[c] *= alpha;
+    for (int r = 0; r < 8; ++r) psum += pv[r];
+    l_run += psum;
 
     if constexpr (FP8) {
         // B = P^T: slots 0..3 = page a tokens 4j..4j+3, 4..7 = page b.
@@ -279,7 +308,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
     const int b = (bid / hkv) % batch;
     const int slot = bid / (hkv * batch);
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wavefront
     const int lane = tid % 64;
     const int col = lane % 16;       // query column of the MFMA tiles
     const int jgrp = lane / 16;      // k-group of the operands / row group of the result

@@ -1,7 +1,7 @@
 // C-ABI entry points: argument validation, partition sizing and dispatch to
 // the kernel launchers. Validation happens before any HIP call, so invalid
 // arguments return a negative status and enqueue nothing.
-#include "../../include/kvfp8.h"
+#include "kvfp8.h"
 
 #include <hip/hip_runtime.h>
 
@@ -160,6 +160,7 @@ int paged_decode_attn(const void* q, int32_t cache_dtype, const void* k_pool, co
     if (num_q_heads / num_kv_heads > KV_MAX_GROUP) return KV_ERR_UNSUPPORTED;
     if (cache_dtype != KV_CACHE_FP8_E4M3 && cache_dtype != KV_CACHE_BF16)
         return KV_ERR_UNSUPPORTED;
+    if (!(sm_scale >= 0.0f) || !(sm_scale < INFINITY)) return KV_ERR_UNSUPPORTED;
     const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
                                                           partition_tokens);
     if (pt <= 0) return KV_ERR_UNSUPPORTED;

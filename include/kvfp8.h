@@ -206,12 +206,15 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * softmax and the partials are merged by a second kernel when there is more
  * than one partition.
  *
+ * sm_scale must be finite and >= 0 (usually 1/sqrt(head_dim)); the scales
+ * must be positive and finite.
  * q: bf16 [batch][num_q_heads][head_dim]. out: fp32 [batch][num_q_heads]
  * [head_dim], fully written. k_scale/v_scale: fp32 [num_kv_heads] (may be
  * NULL for the BF16 cache). workspace: device memory of at least
  * paged_decode_attn_workspace_bytes(...) bytes (may be NULL when that is 0).
  * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED (also when
- * ceil(max_seq_len / partition_tokens) exceeds KV_MAX_PARTITIONS),
+ * ceil(max_seq_len / partition_tokens) exceeds KV_MAX_PARTITIONS, or for a
+ * negative or non-finite sm_scale),
  * KV_ERR_WORKSPACE, KV_ERR_ALIGN, KV_ERR_LAUNCH.
  */
 int paged_decode_attn(const void* q, int32_t cache_dtype,

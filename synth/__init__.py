@@ -253,14 +253,17 @@ def scales_from_amax(amax) -> np.ndarray:
 
 def _build(name, cfg_index, *, batch, layers, hq, hkv, d, page, seq_lens0, max_steps,
            pool_pages, k_sigma, v_sigma, q_sigma, garbage_tail, rng,
-           partition_tokens=0):
-    """Allocate pages from a shuffled pool and record matching tags."""
+           partition_tokens=0, shuffle=True):
+    """Allocate pages from a shuffled (or, if shuffle=False, in-order) pool and
+    record matching tags."""
     seq_lens0 = np.asarray(seq_lens0, dtype=np.int32)
     need = [-(-(int(L) + max_steps) // page) for L in seq_lens0]
     total = sum(need)
     num_pages = pool_pages(total)
     assert num_pages >= total
     perm = rng.permutation(num_pages).astype(np.int32)
+    if not shuffle:
+        perm = np.arange(num_pages, dtype=np.int32)
     max_pages = max(need)
     if garbage_tail:
         bt = rng.integers(-(2 ** 31), 2 ** 31 - 1, size=(batch, max_pages), dtype=np.int64)

@@ -127,6 +127,9 @@ def test_attention_rejects_bad_arguments(lib):
     assert attn(lib, out=A + 4) == ALIGN
     assert attn(lib, workspace=None, partition_tokens=512) == WORKSPACE
     assert attn(lib, workspace_bytes=16, partition_tokens=512) == WORKSPACE
+    assert attn(lib, sm_scale=-0.5) == UNSUP
+    assert attn(lib, sm_scale=float("nan")) == UNSUP
+    assert attn(lib, sm_scale=float("inf")) == UNSUP
     assert attn(lib, batch=0, q=None) == OK
 
 
