@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="split-K partition size; -1 = the workload's own (0 = automatic)")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--fused", default="on", choices=["on", "off"],
+                    help="append + attention in one launch per layer (paged_decode_attn_append)")
     ap.add_argument("--verify-cost", default="on", choices=["on", "off"],
                     help="also time as many steps with the no-op tracker (no tag check)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -228,6 +230,7 @@ def main():
     wl = make(max_steps=total_steps)
     pt = wl.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
     verify = args.verify == "on"
+    fused = args.fused == "on"
     cache = args.cache
     fp8 = cache == "fp8"
     log(args, f"workload {wl.name}: B={wl.batch} layers={wl.num_layers} pages={wl.num_pages} "
@@ -270,6 +273,17 @@ def main():
                               st.abort, stream=stream)
         for layer in range(wl.num_layers):
             q, kn, vn = inputs[s][layer]
+            if fused:
+                if timed_slot is not None:
+                    ev_attn[timed_slot + layer][0].record(stream)
+                kv.paged_decode_attn_append(q, kn, vn, st.k_pool[layer], st.v_pool[layer],
+                                            st.k_scale[layer], st.v_scale[layer], st.block_table,
+                                            seq_lens[s], max_len, outs[layer], sm, workspace=ws,
+                                            abort=abort, partition_tokens=pt, cache_dtype=cd,
+                                            stream=stream)
+                if timed_slot is not None:
+                    ev_attn[timed_slot + layer][1].record(stream)
+                continue
             if fp8:
                 kv.kv_append_quant(kn, vn, st.tok_seq, tok_pos[s], st.block_table,
                                    st.k_scale[layer], st.v_scale[layer], st.k_pool[layer],
@@ -319,7 +333,8 @@ def main():
     by2 = [step_bytes(wl, wl.seq_lens_at(base2 + i), cache, verify) for i in range(args.steps)]
     total_bytes = sum(b["total"] for b in by)
     gbs = total_bytes / (elapsed_ms * 1e-3) / 1e9
-    attn_bytes = float(np.mean([b["attn_per_layer"] for b in by2]))
+    attn_bytes = float(np.mean([b["attn_per_layer"] + (b["append_per_layer"] if fused else 0)
+                                for b in by2]))
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     seq_steps = wl.batch * args.steps / (elapsed_ms * 1e-3)
     log(args, f"{ms_per_step:.3f} ms/step, {gbs:.0f} GB/s, attention call {attn_avg_ms*1e3:.1f} us "
@@ -382,10 +397,12 @@ def main():
             "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
             "page_size": wl.page_size, "mean_ctx": round(float(wl.seq_lens0.mean()) + 1, 1),
             "cache": cache, "verify": verify, "partition_tokens": pt_eff,
+            "append": "fused into the attention launch" if fused else "separate launch",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_attn (partition kernel + cross-partition reduce)",
+            "kernel": ("paged_decode_attn_append (append + attention partition kernel)" if fused
+                       else "paged_decode_attn (partition kernel + cross-partition reduce)"),
             "achieved": round(attn_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -9,8 +9,8 @@ works but the first call raises ``KvLibraryMissing``.
 
 Entry points (same names as the C ABI):
     kv_verify_tags, kv_append_quant, kv_append_bf16, paged_decode_attn,
-    paged_decode_attn_workspace_bytes, paged_decode_attn_partition_tokens,
-    kv_status_str
+    paged_decode_attn_append, paged_decode_attn_workspace_bytes,
+    paged_decode_attn_partition_tokens, kv_status_str
 plus ``decode_step``, which enqueues one decode step (tag check, then per
 layer append and attention) in the order the operations require.
 """
@@ -23,7 +23,7 @@ import os
 __all__ = [
     "KV_CACHE_FP8_E4M3", "KV_CACHE_BF16", "KvError", "KvLibraryMissing", "lib_path",
     "load", "kv_status_str", "kv_verify_tags", "kv_append_quant", "kv_append_bf16",
-    "paged_decode_attn", "paged_decode_attn_workspace_bytes",
+    "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_workspace_bytes",
     "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
 ]
 
@@ -66,6 +66,9 @@ _SIGS = {
     "paged_decode_attn": (ctypes.c_int, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P,
                                          ctypes.c_float, _I, _I, _I, _I, _I, _I, _I, _P,
                                          ctypes.c_size_t, _P]),
+    "paged_decode_attn_append": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _I,
+                                                _P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _I,
+                                                _I, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -241,11 +244,43 @@ def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens
     _check("paged_decode_attn", st)
 
 
+def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table,
+                             seq_lens, max_seq_len, out, sm_scale, workspace=None, abort=None,
+                             partition_tokens=0, cache_dtype=KV_CACHE_FP8_E4M3,
+                             page_size=PAGE_SIZE, stream=None):
+    """Append each request's new token (position seq_lens[b] - 1) and attend, in one launch."""
+    d = _dt()
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
+    batch, hq, hd = q.shape
+    hkv = k_pool.shape[1]
+    if k_new.shape != (batch, hkv, hd) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [batch][num_kv_heads][head_dim]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
+    st = load().paged_decode_attn_append(
+        _ptr(q, "q", d["bf16"]), _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
+        int(cache_dtype), _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
+        _ptr(v_pool, "v_pool", d["u8"] if fp8 else d["pool"]),
+        _ptr(k_scale, "k_scale", d["f32"], allow_none=not fp8),
+        _ptr(v_scale, "v_scale", d["f32"], allow_none=not fp8),
+        _ptr(block_table, "block_table", d["i32"]), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", d["i32"]), int(max_seq_len),
+        _ptr(abort, "abort", d["u8"], allow_none=True), _ptr(out, "out", d["f32"]),
+        float(sm_scale), batch, hq, hkv, hd, page_size, k_pool.shape[0], int(partition_tokens),
+        ws_ptr, ws_bytes, _stream(stream))
+    _check("paged_decode_attn_append", st)
+
+
 def decode_step(layers, block_table, seq_lens, tok_pos, tok_seq, max_seq_len, sm_scale,
                 pool_tags=None, expected_tags=None, abort=None, cache_dtype=KV_CACHE_FP8_E4M3,
-                workspace=None, partition_tokens=0, stream=None):
+                workspace=None, partition_tokens=0, fused=True, stream=None):
     """Enqueue one decode step: tag check (if pool_tags is given), then for
-    each layer the append of the new token and attention over the pages.
+    each layer the append of the new token and attention over the pages
+    (one fused launch per layer, or the two separate calls with fused=False).
 
     ``layers`` is a sequence of dicts with keys q, k_new, v_new, k_pool, v_pool,
     k_scale, v_scale, out. With pool_tags=None no check runs and abort=None is
@@ -256,6 +291,14 @@ def decode_step(layers, block_table, seq_lens, tok_pos, tok_seq, max_seq_len, sm
     else:
         abort = None
     for ly in layers:
+        if fused:
+            paged_decode_attn_append(ly["q"], ly["k_new"], ly["v_new"], ly["k_pool"],
+                                     ly["v_pool"], ly.get("k_scale"), ly.get("v_scale"),
+                                     block_table, seq_lens, max_seq_len, ly["out"], sm_scale,
+                                     workspace=workspace, abort=abort,
+                                     partition_tokens=partition_tokens, cache_dtype=cache_dtype,
+                                     stream=stream)
+            continue
         if cache_dtype == KV_CACHE_FP8_E4M3:
             kv_append_quant(ly["k_new"], ly["v_new"], tok_seq, tok_pos, block_table,
                             ly["k_scale"], ly["v_scale"], ly["k_pool"], ly["v_pool"],

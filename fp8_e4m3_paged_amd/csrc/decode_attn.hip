@@ -47,7 +47,7 @@ struct PairTiles {
 };
 
 template <bool FP8>
-__device__ inline void load_pair(PairTiles<FP8>& r, const uint8_t* __restrict__ k_pool,
+__device__ __forceinline__ void load_pair(PairTiles<FP8>& r, const uint8_t* __restrict__ k_pool,
                                  const uint8_t* __restrict__ v_pool, size_t tile_a,
                                  size_t tile_b, int lane) {
     constexpr int T = FP8 ? kTileFp8 : kTileBf16;
@@ -70,7 +70,7 @@ __device__ inline void load_pair(PairTiles<FP8>& r, const uint8_t* __restrict__ 
 // bytes 8(c%2)..+7 of the lane's load c/2 (FP8, decoded to bf16) or load c
 // itself (BF16).
 template <bool FP8>
-__device__ inline bf16x8 k_operand(const u32x4 (&k)[PairTiles<FP8>::N], int c) {
+__device__ __forceinline__ bf16x8 k_operand(const u32x4 (&k)[PairTiles<FP8>::N], int c) {
     if constexpr (FP8) {
         bf16x2 p0, p1, p2, p3;
         decode4_bf16(k[c / 2][2 * (c % 2)], p0, p1);
@@ -84,7 +84,7 @@ __device__ inline bf16x8 k_operand(const u32x4 (&k)[PairTiles<FP8>::N], int c) {
 // S^T (16 tokens x 16 query columns) of pages a and b: two chains of 4 MFMAs
 // over head_dim, interleaved so neither waits on its own previous result.
 template <bool FP8>
-__device__ inline void qk_pair(const PairTiles<FP8>& t, const bf16x8 (&qop)[4], f32x4& sa,
+__device__ __forceinline__ void qk_pair(const PairTiles<FP8>& t, const bf16x8 (&qop)[4], f32x4& sa,
                                f32x4& sb) {
     sa = f32x4{0.f, 0.f, 0.f, 0.f};
     sb = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -97,31 +97,28 @@ __device__ inline void qk_pair(const PairTiles<FP8>& t, const bf16x8 (&qop)[4], 
 
 // Zero the bytes of tokens >= valid in a lane's 4-token groups (FP8: 1 byte
 // per token per dword; BF16: 2 bytes per token, two dwords per group).
-__device__ inline uint32_t token_mask_fp8(int valid) {
+__device__ __forceinline__ uint32_t token_mask_fp8(int valid) {
     return valid >= 4 ? 0xFFFFFFFFu : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
 }
-__device__ inline uint64_t token_mask_bf16(int valid) {
+__device__ __forceinline__ uint64_t token_mask_bf16(int valid) {
     return valid >= 4 ? ~0ull : (valid <= 0 ? 0ull : ((1ull << (16 * valid)) - 1ull));
 }
 
+// (Whole-vector updates only: element stores into these register arrays can
+// push them out to scratch memory.)
 template <bool FP8>
-__device__ inline void mask_v(u32x4 (&v)[PairTiles<FP8>::N], int valid) {
+__device__ __forceinline__ void mask_v(u32x4 (&v)[PairTiles<FP8>::N], int valid) {
     if constexpr (FP8) {
         const uint32_t m = token_mask_fp8(valid);
+        const u32x4 mm = {m, m, m, m};
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[h][e] &= m;
+        for (int h = 0; h < 2; ++h) v[h] = v[h] & mm;
     } else {
         const uint64_t m = token_mask_bf16(valid);
         const uint32_t lo = static_cast<uint32_t>(m), hi = static_cast<uint32_t>(m >> 32);
+        const u32x4 mm = {lo, hi, lo, hi};
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            v[h][0] &= lo;
-            v[h][1] &= hi;
-            v[h][2] &= lo;
-            v[h][3] &= hi;
-        }
+        for (int h = 0; h < 4; ++h) v[h] = v[h] & mm;
     }
 }
 
@@ -138,7 +135,7 @@ constexpr float kMaxSlack = 8.0f;
 // Only the pair that crosses t_end needs masking. Control flow is
 // wave-uniform (MFMA needs all lanes).
 template <bool FP8>
-__device__ inline void process_pair(PairTiles<FP8>& cur, int tok_a, int t_end, int jgrp,
+__device__ __forceinline__ void process_pair(PairTiles<FP8>& cur, int tok_a, int t_end, int jgrp,
                                     float s_scale, const bf16x8 (&qop)[4], float& m_run,
                                     float& l_run, f32x4 (&acc_o)[8]) {
     const int tok_b = tok_a + kPage;
@@ -230,20 +227,163 @@ __device__ inline void process_pair(PairTiles<FP8>& cur, int tok_a, int t_end, i
     }
 }
 
+// The new token's codes, computed by the lanes that hold its bytes once
+// loaded. Lane (t, j) holds K dims 32j..32j+31 of token t; lane (m, j) holds
+// V dim 16c + m of tokens 4j..4j+3 for every chunk c. K: the lane's 16-byte
+// chunks of that slot (2 for FP8, 4 for BF16). V: the 8 values of dims
+// 16c + m (FP8: 8 codes in 2 dwords; BF16: 8 halves in 4 dwords).
+template <bool FP8>
+struct NewToken {
+    u32x4 k[PairTiles<FP8>::N];
+    uint32_t v[FP8 ? 2 : 4];
+};
+
+// The bf16 inputs a lane needs for its part of the new token: K dims
+// 32j..32j+31 (64 bytes) and V dims 16c + m, c = 0..7.
+struct NewTokenRaw {
+    u32x4 k[4];
+    uint16_t v[8];
+};
+
+__device__ __forceinline__ void load_new_token(NewTokenRaw& r, int lane, const uint16_t* __restrict__ krow,
+                                      const uint16_t* __restrict__ vrow) {
+    const int m = lane % 16;
+    const int j = lane / 16;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) r.k[h] = *reinterpret_cast<const u32x4*>(krow + 32 * j + 8 * h);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) r.v[c] = vrow[16 * c + m];
+}
+
+// Encode (same arithmetic as kv_append_quant) in registers only.
+template <bool FP8>
+__device__ __forceinline__ void encode_new_token(NewToken<FP8>& nt, const NewTokenRaw& r, float ks,
+                                        float vs) {
+    if constexpr (FP8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t c4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const u32x4 w = r.k[2 * h + e / 2];            // dims 32j + 16h + 4e ..
+                const uint32_t lo = w[2 * (e % 2)], hi = w[2 * (e % 2) + 1];
+                c4[e] = encode4_e4m3(div_round_odd(bf16_bits_to_float(lo & 0xFFFF), ks),
+                                     div_round_odd(bf16_bits_to_float(lo >> 16), ks),
+                                     div_round_odd(bf16_bits_to_float(hi & 0xFFFF), ks),
+                                     div_round_odd(bf16_bits_to_float(hi >> 16), ks));
+            }
+            nt.k[h] = u32x4{c4[0], c4[1], c4[2], c4[3]};
+        }
+        float y[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] = div_round_odd(bf16_bits_to_float(r.v[c]), vs);
+        nt.v[0] = encode4_e4m3(y[0], y[1], y[2], y[3]);
+        nt.v[1] = encode4_e4m3(y[4], y[5], y[6], y[7]);
+    } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) nt.k[h] = r.k[h];
+#pragma unroll
+        for (int c = 0; c < 8; c += 2)
+            nt.v[c / 2] = static_cast<uint32_t>(r.v[c]) | (static_cast<uint32_t>(r.v[c + 1]) << 16);
+    }
+}
+
+// Store the new token's codes into its pool tiles for later steps (K: whole
+// 16-byte chunks, which hold only this slot; V: single bytes / halves, so the
+// other slots of the same dwords keep their bytes). Runs after the wave's
+// last load so its stores cannot disturb the pipeline's wait counts.
+template <bool FP8>
+__device__ __forceinline__ void store_new_token(const NewToken<FP8>& nt, int slot, int lane,
+                                       uint8_t* __restrict__ ktile, uint8_t* __restrict__ vtile) {
+    const int m = lane % 16;
+    const int j = lane / 16;
+    if (m == slot) {
+#pragma unroll
+        for (int h = 0; h < PairTiles<FP8>::N; ++h)
+            *reinterpret_cast<u32x4*>(ktile + 1024 * h + 16 * lane) = nt.k[h];
+    }
+    if (j == slot / 4) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if constexpr (FP8) {
+                vtile[off_v_fp8(slot, 16 * c + m)] = static_cast<uint8_t>(nt.v[c / 4] >> (8 * (c % 4)));
+            } else {
+                *reinterpret_cast<uint16_t*>(vtile + off_v_bf16(slot, 16 * c + m)) =
+                    static_cast<uint16_t>(nt.v[c / 2] >> (16 * (c % 2)));
+            }
+        }
+    }
+}
+
+// Overwrite the new token's slot in one page's K / V registers with its codes
+// when `on` (the token is in this page). Value selects only, called for both
+// pages of the pair: choosing between the two pages' arrays at run time would
+// force them out of registers.
+template <bool FP8>
+__device__ __forceinline__ void apply_new_token(u32x4 (&K)[PairTiles<FP8>::N],
+                                                u32x4 (&V)[PairTiles<FP8>::N],
+                                                const NewToken<FP8>& nt, int slot, int lane,
+                                                bool on) {
+    const int m = lane % 16;
+    const int j = lane / 16;
+    const bool pk = on && m == slot;
+#pragma unroll
+    for (int h = 0; h < PairTiles<FP8>::N; ++h) K[h] = pk ? nt.k[h] : K[h];
+    const bool pv = on && j == slot / 4;
+    const int sel = slot % 4;
+    if constexpr (FP8) {
+        // load h holds chunks c = 4h..4h+3, one dword each, token byte sel
+        const uint32_t keep = ~(0xFFu << (8 * sel));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 w = V[h];
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = (w[e] & keep) | (((nt.v[h] >> (8 * e)) & 0xFFu) << (8 * sel));
+            V[h] = pv ? u32x4{o[0], o[1], o[2], o[3]} : w;
+        }
+    } else {
+        // load h holds chunks c = 2h, 2h+1: dwords 2(c%2) (tokens 0, 1) and
+        // 2(c%2) + 1 (tokens 2, 3) of the 4-token group; half sel % 2
+        const uint32_t keep = ~(0xFFFFu << (16 * (sel % 2)));
+        const bool upper = sel >= 2;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const u32x4 w = V[h];
+            uint32_t o[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const uint32_t val = (nt.v[h] >> (16 * cc)) & 0xFFFFu;   // chunk 2h + cc
+                const uint32_t lo2 = (o[2 * cc] & keep) | (val << (16 * (sel % 2)));
+                const uint32_t hi2 = (o[2 * cc + 1] & keep) | (val << (16 * (sel % 2)));
+                o[2 * cc] = upper ? o[2 * cc] : lo2;
+                o[2 * cc + 1] = upper ? hi2 : o[2 * cc + 1];
+            }
+            V[h] = pv ? u32x4{o[0], o[1], o[2], o[3]} : w;
+        }
+    }
+}
+
 // Software pipeline over a wavefront's n page pairs: register buffers rotate
 // so that while one pair is processed the next ones are in flight (two for
 // FP8, one for BF16, whose tiles take twice the registers). Every load in the
 // steady-state loop is unconditional (the index is clamped to the last pair),
 // so each wait is a static partial vmcnt; the FP8 epilogue issues only the
 // loads that are still needed.
-template <bool FP8, typename Issue, typename Proc>
-__device__ inline void pipeline_pairs(int n, Issue&& issue, Proc&& proc) {
+// `proc_end` processes the pairs of the FP8 epilogue, which always include
+// the wave's last pair (the only one the fused append ever patches), so the
+// steady-state loop carries no patch logic.
+template <bool FP8, typename Issue, typename Proc, typename ProcEnd, typename Hook>
+__device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc, ProcEnd&& proc_end,
+                                               Hook&& after_issue) {
     if (n <= 0) return;
     if constexpr (FP8) {
         PairTiles<FP8> t0, t1, t2;
         issue(t0, 0);
         issue(t1, 1);
         issue(t2, 2);
+        after_issue();     // runs while the first tiles are in flight
         int i = 0;
         for (; i + 5 < n; i += 3) {
             proc(t0, i);
@@ -254,13 +394,13 @@ __device__ inline void pipeline_pairs(int n, Issue&& issue, Proc&& proc) {
             issue(t2, i + 5);
         }
         // 1..5 pairs left: t0, t1, t2 hold pairs i, i+1, i+2 (when they exist)
-        proc(t0, i);
+        proc_end(t0, i);
         if (i + 3 < n) issue(t0, i + 3);
-        if (i + 1 < n) proc(t1, i + 1);
+        if (i + 1 < n) proc_end(t1, i + 1);
         if (i + 4 < n) issue(t1, i + 4);
-        if (i + 2 < n) proc(t2, i + 2);
-        if (i + 3 < n) proc(t0, i + 3);
-        if (i + 4 < n) proc(t1, i + 4);
+        if (i + 2 < n) proc_end(t2, i + 2);
+        if (i + 3 < n) proc_end(t0, i + 3);
+        if (i + 4 < n) proc_end(t1, i + 4);
     } else {
         // BF16: no separate epilogue (its straight-line copies of the pair step
         // exceed the register file); past the end the clamped loads re-read
@@ -268,10 +408,11 @@ __device__ inline void pipeline_pairs(int n, Issue&& issue, Proc&& proc) {
         PairTiles<FP8> t0, t1;
         issue(t0, 0);
         issue(t1, 1);
+        after_issue();
         for (int i = 0; i < n; i += 2) {
-            proc(t0, i);
+            proc_end(t0, i);
             issue(t0, i + 2);
-            if (i + 1 < n) proc(t1, i + 1);
+            if (i + 1 < n) proc_end(t1, i + 1);
             issue(t1, i + 3);
         }
     }
@@ -284,10 +425,23 @@ __device__ inline void pipeline_pairs(int n, Issue&& issue, Proc&& proc) {
 //     one per wavefront, each written straight from registers; used for
 //     short partitions, where sharing would leave each wave too few pairs to
 //     keep its pipeline full.
-template <bool FP8, bool WAVE_PARTS>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
-    const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
+//   APPEND = true (paged_decode_attn_append): the wavefront that will process
+//     the page pair holding the new token t = L - 1 quantizes k_new[b][g] /
+//     v_new[b][g] itself (same encoder as kv_append_quant) while its first
+//     loads are in flight, overwrites that slot's bytes in the pair's
+//     registers when it gets there, and stores the codes to the pool for
+//     later steps after its last load. Nothing in the launch reads the codes
+//     back from memory, so no fence or barrier is involved.
+// Occupancy is pinned at 2 waves per SIMD: the register pipeline needs ~200
+// VGPRs, and without the cap the scheduler may trade the in-flight loads for a
+// third wave (sinking the prefetches next to their uses), which halves the
+// streaming rate.
+template <bool FP8, bool WAVE_PARTS, bool APPEND>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_partition_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const uint8_t* __restrict__ abort,
     float* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_acc,
@@ -373,7 +527,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
         }
         const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
 
-        const auto tile_of = [&](int page_idx) -> size_t {
+        const auto tile_of = [&](int page_idx) __attribute__((always_inline)) -> size_t {
             const int id = __builtin_amdgcn_readfirstlane(ids[page_idx]);
             return static_cast<size_t>(id) * hkv + g;
         };
@@ -381,16 +535,56 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
         const int first = WAVE_PARTS ? 0 : wave;
         const int stride = WAVE_PARTS ? 1 : kWaves;
         const int n_w = npairs > first ? (npairs - first + stride - 1) / stride : 0;
-        const auto issue = [&](PairTiles<FP8>& t, int i) {
+        const auto issue = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
             const int pr = first + stride * min(i, n_w - 1);
             load_pair<FP8>(t, k_pool, v_pool, tile_of(2 * pr), tile_of(min(2 * pr + 1, npg - 1)),
                            lane);
         };
-        const auto proc = [&](PairTiles<FP8>& t, int i) {
+        // Fused append: the wave that will process the new token's pair loads
+        // its bf16 inputs before its first tile loads (so every wait count in
+        // the pipeline stays static), encodes them in registers while those
+        // tiles are in flight, patches the pair's registers when it gets there,
+        // and stores the codes to the pool after its last load.
+        const int t_new = L - 1;
+        const int pr_new = (t_new / kPage - pg0) / 2;
+        const bool owns_new = APPEND && t_new >= t_begin && t_new < t_end &&
+                              pr_new >= first && (pr_new - first) % stride == 0;
+        const bool new_in_b = ((t_new / kPage - pg0) % 2) == 1;
+        const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
+        NewTokenRaw raw;
+        NewToken<FP8> nt;
+        if constexpr (APPEND) {
+            if (owns_new) load_new_token(raw, lane, k_new + new_row, v_new + new_row);
+        }
+        const auto prepare = [&]() __attribute__((always_inline)) {
+            if constexpr (APPEND) {
+                if (owns_new)
+                    encode_new_token<FP8>(nt, raw, FP8 ? k_scale[g] : 1.0f, FP8 ? v_scale[g] : 1.0f);
+            }
+        };
+        const auto proc = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
             process_pair<FP8>(t, (pg0 + 2 * (first + stride * i)) * kPage, t_end, jgrp, s_scale,
                               qop, m_run, l_run, acc_o);
         };
-        pipeline_pairs<FP8>(n_w, issue, proc);
+        const auto proc_end = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
+            const int pr = first + stride * i;
+            if constexpr (APPEND) {
+                if (owns_new && pr == pr_new) {                  // wave-uniform
+                    apply_new_token<FP8>(t.ka, t.va, nt, t_new % kPage, lane, !new_in_b);
+                    apply_new_token<FP8>(t.kb, t.vb, nt, t_new % kPage, lane, new_in_b);
+                }
+            }
+            process_pair<FP8>(t, (pg0 + 2 * pr) * kPage, t_end, jgrp, s_scale, qop, m_run, l_run,
+                              acc_o);
+        };
+        pipeline_pairs<FP8>(n_w, issue, proc, proc_end, prepare);
+        if constexpr (APPEND) {
+            if (owns_new) {
+                const size_t tile = tile_of(t_new / kPage - pg0);
+                constexpr int T = FP8 ? kTileFp8 : kTileBf16;
+                store_new_token<FP8>(nt, t_new % kPage, lane, k_pool + tile * T, v_pool + tile * T);
+            }
+        }
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -463,7 +657,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partition_kernel(
 // the 16 group sums are added in LDS.
 constexpr int kReduceThreads = 512;
 
-__device__ inline float block_max(float v, float* red) {
+__device__ __forceinline__ float block_max(float v, float* red) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     const int w = threadIdx.x / 64;
     __syncthreads();
@@ -474,7 +668,7 @@ __device__ inline float block_max(float v, float* red) {
     return r;
 }
 
-__device__ inline float block_sum(float v, float* red) {
+__device__ __forceinline__ float block_sum(float v, float* red) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     const int w = threadIdx.x / 64;
     __syncthreads();
@@ -562,20 +756,27 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
     const uint32_t slots = wave_mode ? (a.num_partitions + kWaves - 1) / kWaves : a.num_partitions;
     const dim3 grid(slots * a.batch * a.num_kv_heads);
     const float sm_log2 = a.sm_scale * kLog2e;
-#define KVFP8_LAUNCH(F8, WP)                                                                     \
-    hipLaunchKernelGGL((attn_partition_kernel<F8, WP>), grid, dim3(kAttnThreads), lds, stream,  \
-                       a.q, static_cast<const uint8_t*>(a.k_pool),                               \
-                       static_cast<const uint8_t*>(a.v_pool), F8 ? a.k_scale : nullptr,          \
+#define KVFP8_LAUNCH3(F8, WP, AP)                                                                \
+    hipLaunchKernelGGL((attn_partition_kernel<F8, WP, AP>), grid, dim3(kAttnThreads), lds,      \
+                       stream, a.q, a.k_new, a.v_new, static_cast<uint8_t*>(a.k_pool),          \
+                       static_cast<uint8_t*>(a.v_pool), F8 ? a.k_scale : nullptr,                \
                        F8 ? a.v_scale : nullptr, a.block_table, a.bt_stride, a.seq_lens,         \
                        a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2, a.batch,   \
                        a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens,           \
                        a.num_partitions)
+#define KVFP8_LAUNCH(F8, WP)                          \
+    do {                                              \
+        if (append) KVFP8_LAUNCH3(F8, WP, true);      \
+        else KVFP8_LAUNCH3(F8, WP, false);            \
+    } while (0)
+    const bool append = a.k_new != nullptr;
     if (fp8) {
         if (wave_mode) KVFP8_LAUNCH(true, true); else KVFP8_LAUNCH(true, false);
     } else {
         if (wave_mode) KVFP8_LAUNCH(false, true); else KVFP8_LAUNCH(false, false);
     }
 #undef KVFP8_LAUNCH
+#undef KVFP8_LAUNCH3
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_partitions == 1) return e;
     hipLaunchKernelGGL(reduce_partials_kernel, dim3(a.batch * a.num_q_heads), dim3(kReduceThreads),

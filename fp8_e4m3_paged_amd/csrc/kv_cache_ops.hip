@@ -119,35 +119,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const u32x2 raw = *reinterpret_cast<const u32x2*>(src);
     const size_t tile = static_cast<size_t>(page) * num_kv_heads + g;
 
-    if constexpr (FP8) {
-        const float s = (is_v ? v_scale : k_scale)[g];
-        const float y0 = div_round_odd(bf16_bits_to_float(raw.x & 0xFFFF), s);
-        const float y1 = div_round_odd(bf16_bits_to_float(raw.x >> 16), s);
-        const float y2 = div_round_odd(bf16_bits_to_float(raw.y & 0xFFFF), s);
-        const float y3 = div_round_odd(bf16_bits_to_float(raw.y >> 16), s);
-        const uint32_t codes = encode4_e4m3(y0, y1, y2, y3);
-        uint8_t* base = (is_v ? v_pool : k_pool) + tile * kTileFp8;
-        if (!is_v) {
-            // 4 consecutive dims are 4 consecutive bytes in the K tile.
-            *reinterpret_cast<uint32_t*>(base + off_k_fp8(slot, d)) = codes;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) base[off_v_fp8(slot, d + i)] = (codes >> (8 * i)) & 0xFF;
-        }
-    } else {
-        uint8_t* base = (is_v ? v_pool : k_pool) + tile * kTileBf16;
-        if (!is_v) {
-            *reinterpret_cast<u32x2*>(base + off_k_bf16(slot, d)) = raw;
-        } else {
-            const uint16_t h[4] = {static_cast<uint16_t>(raw.x & 0xFFFF),
-                                   static_cast<uint16_t>(raw.x >> 16),
-                                   static_cast<uint16_t>(raw.y & 0xFFFF),
-                                   static_cast<uint16_t>(raw.y >> 16)};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint16_t*>(base + off_v_bf16(slot, d + i)) = h[i];
-        }
-    }
+    const float s = FP8 ? (is_v ? v_scale : k_scale)[g] : 1.0f;
+    uint8_t* base = (is_v ? v_pool : k_pool) + tile * (FP8 ? kTileFp8 : kTileBf16);
+    store_token_quad<FP8>(is_v, raw, s, base, slot, d);
 }
 
 hipError_t launch_append(bool fp8, const uint16_t* k_new, const uint16_t* v_new,

@@ -26,16 +26,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // These are the layouts documented in kvfp8.h; the append kernels write
 // through them and the attention kernel's loads are their inverse.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline int off_k_fp8(int t, int d) {
+__host__ __device__ __forceinline__ int off_k_fp8(int t, int d) {
     return 1024 * ((d % 32) / 16) + 256 * (d / 32) + 16 * t + (d % 16);
 }
-__host__ __device__ inline int off_v_fp8(int t, int d) {
+__host__ __device__ __forceinline__ int off_v_fp8(int t, int d) {
     return 1024 * (d / 64) + 256 * (t / 4) + 16 * (d % 16) + 4 * ((d / 16) % 4) + (t % 4);
 }
-__host__ __device__ inline int off_k_bf16(int t, int d) {
+__host__ __device__ __forceinline__ int off_k_bf16(int t, int d) {
     return 1024 * ((d % 32) / 8) + 256 * (d / 32) + 16 * t + 2 * (d % 8);
 }
-__host__ __device__ inline int off_v_bf16(int t, int d) {
+__host__ __device__ __forceinline__ int off_v_bf16(int t, int d) {
     return 1024 * (d / 32) + 256 * (t / 4) + 16 * (d % 16) + 8 * ((d / 16) % 2) + 2 * (t % 4);
 }
 
@@ -46,12 +46,12 @@ __host__ __device__ inline int off_v_bf16(int t, int d) {
 // Encode two floats already divided by the scale. Finite values and
 // infinities are clamped to +-448 first, so the hardware's round-to-nearest-
 // even conversion never sees an overflow; NaN gets the NaN code with its sign.
-__device__ inline uint32_t sat_e4m3_byte_fixup(float y, uint32_t code) {
+__device__ __forceinline__ uint32_t sat_e4m3_byte_fixup(float y, uint32_t code) {
     if (y != y) return (__float_as_uint(y) >> 24 & 0x80u) | 0x7Fu;
     return code;
 }
 
-__device__ inline float clamp448(float y) {
+__device__ __forceinline__ float clamp448(float y) {
     // fminf/fmaxf would turn NaN into +-448; NaN is fixed up after the convert.
     return (y != y) ? 0.0f : fminf(fmaxf(y, -448.0f), 448.0f);
 }
@@ -64,7 +64,7 @@ __device__ inline float clamp448(float y) {
 // the exact quotient lies; truncating toward zero and forcing the last bit to
 // 1 when inexact gives round-to-odd, and a round-to-odd value with >= 4 + 2
 // significand bits rounds to E4M3 exactly as the exact quotient would.
-__device__ inline float div_round_odd(float x, float s) {
+__device__ __forceinline__ float div_round_odd(float x, float s) {
     const float y = x / s;                       // correctly rounded (IEEE) division
     if (!(fabsf(y) < INFINITY) || y == 0.0f) return y;
     const float r = fmaf(-y, s, x);
@@ -76,7 +76,7 @@ __device__ inline float div_round_odd(float x, float s) {
 }
 
 // Four floats (already x / s, round-to-odd) -> four e4m3 codes, little-endian.
-__device__ inline uint32_t encode4_e4m3(float y0, float y1, float y2, float y3) {
+__device__ __forceinline__ uint32_t encode4_e4m3(float y0, float y1, float y2, float y3) {
     uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y0), clamp448(y1), 0u, false);
     pk = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y2), clamp448(y3), pk, true);
     uint32_t b0 = sat_e4m3_byte_fixup(y0, pk & 0xFFu);
@@ -88,20 +88,54 @@ __device__ inline uint32_t encode4_e4m3(float y0, float y1, float y2, float y3) 
 
 // Decode the 4 e4m3 codes of one dword into 4 bf16 (exact: 4 significant
 // bits fit bf16's 8). Scale operand 1.0 keeps the conversion a pure decode.
-__device__ inline void decode4_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
+__device__ __forceinline__ void decode4_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
     lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
     hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
 }
 
 // Decode the 4 e4m3 codes of one dword into 4 f16 (exact: every e4m3 value,
 // subnormals included, is an f16 normal).
-__device__ inline void decode4_f16(uint32_t w, f16x2& lo, f16x2& hi) {
+__device__ __forceinline__ void decode4_f16(uint32_t w, f16x2& lo, f16x2& hi) {
     lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
     hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
 }
 
-__device__ inline float bf16_bits_to_float(uint16_t b) {
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Store 4 consecutive dims d..d+3 (bf16 bits in raw) of one token into slot
+// `slot` of a (page, head) tile: FP8 quantizes with the scale s first. K keeps
+// the 4 dims contiguous (one dword / one 8-byte store); V is token-minor, so
+// its 4 dims land 16 bytes apart. Both append paths use this one routine.
+template <bool FP8>
+__device__ __forceinline__ void store_token_quad(bool is_v, u32x2 raw, float s, uint8_t* tile_base,
+                                        int slot, int d) {
+    if constexpr (FP8) {
+        const float y0 = div_round_odd(bf16_bits_to_float(raw.x & 0xFFFF), s);
+        const float y1 = div_round_odd(bf16_bits_to_float(raw.x >> 16), s);
+        const float y2 = div_round_odd(bf16_bits_to_float(raw.y & 0xFFFF), s);
+        const float y3 = div_round_odd(bf16_bits_to_float(raw.y >> 16), s);
+        const uint32_t codes = encode4_e4m3(y0, y1, y2, y3);
+        if (!is_v) {
+            *reinterpret_cast<uint32_t*>(tile_base + off_k_fp8(slot, d)) = codes;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tile_base[off_v_fp8(slot, d + i)] = (codes >> (8 * i)) & 0xFF;
+        }
+    } else {
+        if (!is_v) {
+            *reinterpret_cast<u32x2*>(tile_base + off_k_bf16(slot, d)) = raw;
+        } else {
+            const uint16_t h[4] = {static_cast<uint16_t>(raw.x & 0xFFFF),
+                                   static_cast<uint16_t>(raw.x >> 16),
+                                   static_cast<uint16_t>(raw.y & 0xFFFF),
+                                   static_cast<uint16_t>(raw.y >> 16)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint16_t*>(tile_base + off_v_bf16(slot, d + i)) = h[i];
+        }
+    }
 }
 
 }  // namespace kvfp8

@@ -22,8 +22,10 @@ hipError_t launch_append(bool fp8, const uint16_t* k_new, const uint16_t* v_new,
 
 struct AttnArgs {
     const uint16_t* q;
-    const void* k_pool;
-    const void* v_pool;
+    const uint16_t* k_new;      // non-null: append the token L-1 first (fused path)
+    const uint16_t* v_new;
+    void* k_pool;
+    void* v_pool;
     const float* k_scale;
     const float* v_scale;
     const int32_t* block_table;

@@ -52,6 +52,79 @@ int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len)
 
 }  // namespace
 
+// Shared body of paged_decode_attn (k_new = v_new = NULL: read only) and
+// paged_decode_attn_append (the new token is written by the kernel first).
+static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_t cache_dtype,
+                     void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                     int32_t max_seq_len, const uint8_t* abort, float* out, float sm_scale,
+                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, int32_t num_pages, int32_t partition_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || bt_stride < 0 || num_pages < 0 ||
+        max_seq_len < 0)
+        return KV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return KV_ERR_SHAPE;
+    if (head_dim != KV_HEAD_DIM || page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > KV_MAX_GROUP) return KV_ERR_UNSUPPORTED;
+    if (cache_dtype != KV_CACHE_FP8_E4M3 && cache_dtype != KV_CACHE_BF16)
+        return KV_ERR_UNSUPPORTED;
+    if (!(sm_scale >= 0.0f) || !(sm_scale < INFINITY)) return KV_ERR_UNSUPPORTED;
+    const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
+                                                          partition_tokens);
+    if (pt <= 0) return KV_ERR_UNSUPPORTED;
+    if (batch == 0) return KV_OK;
+    const bool fp8 = cache_dtype == KV_CACHE_FP8_E4M3;
+    if (!q || !out || !seq_lens || !block_table || !k_pool || !v_pool) return KV_ERR_NULL;
+    if ((k_new == nullptr) != (v_new == nullptr)) return KV_ERR_NULL;
+    if (k_new && (misaligned(k_new, 16) || misaligned(v_new, 16))) return KV_ERR_ALIGN;
+    if (fp8 && (!k_scale || !v_scale)) return KV_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(out, 16) || misaligned(k_pool, 16) ||
+        misaligned(v_pool, 16) || misaligned(seq_lens, 4) || misaligned(block_table, 4) ||
+        (k_scale && misaligned(k_scale, 4)) || (v_scale && misaligned(v_scale, 4)))
+        return KV_ERR_ALIGN;
+    const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
+    if (parts64 > KV_MAX_PARTITIONS) return KV_ERR_UNSUPPORTED;
+    const int32_t parts = static_cast<int32_t>(parts64);
+    const int64_t blocks = parts64 * batch * num_kv_heads;
+    if (blocks > 0x7FFFFFFFLL) return KV_ERR_SHAPE;
+    const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
+                                                          head_dim, max_seq_len, pt);
+    if (parts > 1) {
+        if (!workspace || workspace_bytes < need) return KV_ERR_WORKSPACE;
+        if (misaligned(workspace, 16)) return KV_ERR_ALIGN;
+    }
+    kvfp8::AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.seq_lens = seq_lens;
+    a.max_seq_len = max_seq_len;
+    a.abort = abort;
+    a.out = out;
+    a.sm_scale = sm_scale;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.num_pages = num_pages;
+    a.partition_tokens = pt;
+    a.num_partitions = parts;
+    if (parts > 1) {
+        const size_t slots = static_cast<size_t>(batch) * num_q_heads * parts;
+        const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
+        a.part_ml = static_cast<float*>(workspace);
+        a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+    }
+    return launch_status(kvfp8::launch_decode_attn(fp8, a, static_cast<hipStream_t>(stream)));
+}
+
+
 extern "C" {
 
 const char* kv_status_str(int status) {
@@ -152,63 +225,28 @@ int paged_decode_attn(const void* q, int32_t cache_dtype, const void* k_pool, co
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t page_size, int32_t num_pages, int32_t partition_tokens,
                       void* workspace, size_t workspace_bytes, void* stream) {
-    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || bt_stride < 0 || num_pages < 0 ||
-        max_seq_len < 0)
-        return KV_ERR_SHAPE;
-    if (num_q_heads % num_kv_heads != 0) return KV_ERR_SHAPE;
-    if (head_dim != KV_HEAD_DIM || page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
-    if (num_q_heads / num_kv_heads > KV_MAX_GROUP) return KV_ERR_UNSUPPORTED;
-    if (cache_dtype != KV_CACHE_FP8_E4M3 && cache_dtype != KV_CACHE_BF16)
-        return KV_ERR_UNSUPPORTED;
-    if (!(sm_scale >= 0.0f) || !(sm_scale < INFINITY)) return KV_ERR_UNSUPPORTED;
-    const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
-                                                          partition_tokens);
-    if (pt <= 0) return KV_ERR_UNSUPPORTED;
-    if (batch == 0) return KV_OK;
-    const bool fp8 = cache_dtype == KV_CACHE_FP8_E4M3;
-    if (!q || !out || !seq_lens || !block_table || !k_pool || !v_pool) return KV_ERR_NULL;
-    if (fp8 && (!k_scale || !v_scale)) return KV_ERR_NULL;
-    if (misaligned(q, 16) || misaligned(out, 16) || misaligned(k_pool, 16) ||
-        misaligned(v_pool, 16) || misaligned(seq_lens, 4) || misaligned(block_table, 4) ||
-        (k_scale && misaligned(k_scale, 4)) || (v_scale && misaligned(v_scale, 4)))
-        return KV_ERR_ALIGN;
-    const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
-    if (parts64 > KV_MAX_PARTITIONS) return KV_ERR_UNSUPPORTED;
-    const int32_t parts = static_cast<int32_t>(parts64);
-    const int64_t blocks = parts64 * batch * num_kv_heads;
-    if (blocks > 0x7FFFFFFFLL) return KV_ERR_SHAPE;
-    const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
-                                                          head_dim, max_seq_len, pt);
-    if (parts > 1) {
-        if (!workspace || workspace_bytes < need) return KV_ERR_WORKSPACE;
-        if (misaligned(workspace, 16)) return KV_ERR_ALIGN;
-    }
-    kvfp8::AttnArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.block_table = block_table;
-    a.bt_stride = bt_stride;
-    a.seq_lens = seq_lens;
-    a.max_seq_len = max_seq_len;
-    a.abort = abort;
-    a.out = out;
-    a.sm_scale = sm_scale;
-    a.batch = batch;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.num_pages = num_pages;
-    a.partition_tokens = pt;
-    a.num_partitions = parts;
-    if (parts > 1) {
-        const size_t slots = static_cast<size_t>(batch) * num_q_heads * parts;
-        const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
-        a.part_ml = static_cast<float*>(workspace);
-        a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
-    }
-    return launch_status(kvfp8::launch_decode_attn(fp8, a, static_cast<hipStream_t>(stream)));
+    // the pools are only read on this path
+    return attn_impl(q, nullptr, nullptr, cache_dtype, const_cast<void*>(k_pool),
+                     const_cast<void*>(v_pool), k_scale, v_scale, block_table, bt_stride,
+                     seq_lens, max_seq_len, abort, out, sm_scale, batch, num_q_heads,
+                     num_kv_heads, head_dim, page_size, num_pages, partition_tokens, workspace,
+                     workspace_bytes, stream);
+}
+
+int paged_decode_attn_append(const void* q, const void* k_new, const void* v_new,
+                             int32_t cache_dtype, void* k_pool, void* v_pool,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t bt_stride,
+                             const int32_t* seq_lens, int32_t max_seq_len, const uint8_t* abort,
+                             float* out, float sm_scale, int32_t batch, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                             int32_t num_pages, int32_t partition_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (batch > 0 && (!k_new || !v_new)) return KV_ERR_NULL;
+    return attn_impl(q, k_new, v_new, cache_dtype, k_pool, v_pool, k_scale, v_scale,
+                     block_table, bt_stride, seq_lens, max_seq_len, abort, out, sm_scale, batch,
+                     num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                     partition_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -228,6 +228,38 @@ int paged_decode_attn(const void* q, int32_t cache_dtype,
                       int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * One decode step's append and attention for one layer in a single launch:
+ * the same result as kv_append_quant (FP8) / kv_append_bf16 (BF16) with
+ * tok_seq = 0..batch-1, tok_pos = seq_lens - 1, followed by paged_decode_attn,
+ * for every request the attention accepts (abort[b] == 0, 1 <= L <= max_seq_len,
+ * ceil(L/16) <= bt_stride). The new token is written exactly when its request
+ * is accepted and every page of the split-K partition holding it is a valid
+ * pool page (with the tag check run first, any request mapping an invalid
+ * page is aborted, so it is neither written nor read). The wavefront that
+ * processes the new token's page quantizes it, uses the codes from its
+ * registers and stores them for later steps, so nothing in the launch reads
+ * them back from memory. One launch per layer instead of two; the separate
+ * calls remain for bulk ingest and for callers that need them apart. The
+ * pages define the two operations (quantize on write, convert on read:
+ * remio.ai/it, sections "Cosa ha cambiato Cloudflare per Kimi e GLM" and
+ * "Perché le cache più piccole di Cloudflare battono la velocità pura");
+ * fusing them is this library's choice, and the tag check stays separate.
+ *
+ * k_new, v_new: bf16 [batch][num_kv_heads][head_dim], read. k_pool, v_pool are
+ * written (the new token's slot) and read. Other arguments and errors as for
+ * paged_decode_attn (KV_ERR_NULL also for a NULL k_new / v_new).
+ */
+int paged_decode_attn_append(const void* q, const void* k_new, const void* v_new,
+                             int32_t cache_dtype, void* k_pool, void* v_pool,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t bt_stride,
+                             const int32_t* seq_lens, int32_t max_seq_len, const uint8_t* abort,
+                             float* out, float sm_scale, int32_t batch, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                             int32_t num_pages, int32_t partition_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a kv_status value (static string, never NULL). */
 const char* kv_status_str(int status);
 

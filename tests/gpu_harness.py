@@ -33,8 +33,10 @@ def workspace(wl, partition_tokens: int, max_seq_len=None):
 
 
 def gpu_step(st: DeviceState, step: int, verify: bool = True, partition_tokens: int = 0,
-             sm_scale=None, layers=None, max_seq_len=None):
-    """One decode step on the GPU. Returns (abort or None, {layer: out}, {layer: (q, kn, vn)})."""
+             sm_scale=None, layers=None, max_seq_len=None, fused: bool = False):
+    """One decode step on the GPU (separate append + attention calls, or the
+    fused paged_decode_attn_append). Returns (abort or None, {layer: out},
+    {layer: (q, kn, vn)})."""
     wl = st.wl
     layers = st.layers if layers is None else layers
     sm = sm_scale_for(wl) if sm_scale is None else sm_scale
@@ -49,6 +51,18 @@ def gpu_step(st: DeviceState, step: int, verify: bool = True, partition_tokens: 
     outs, inputs = {}, {}
     for layer in layers:
         q, kn, vn = st.step_layer_inputs(layer, step)
+        cd = kv.KV_CACHE_FP8_E4M3 if st.cache == "fp8" else kv.KV_CACHE_BF16
+        if fused:
+            out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"),
+                             dtype=torch.float32, device=DEV)
+            kv.paged_decode_attn_append(q, kn, vn, st.k_pool[layer], st.v_pool[layer],
+                                        st.k_scale[layer], st.v_scale[layer], st.block_table,
+                                        seq_lens, msl, out, sm, workspace=ws, abort=abort,
+                                        partition_tokens=partition_tokens, cache_dtype=cd)
+            outs[layer] = out
+            inputs[layer] = (q.view(torch.int16).cpu().numpy().view(np.uint16),
+                             kn.cpu().numpy().view(np.uint16), vn.cpu().numpy().view(np.uint16))
+            continue
         if st.cache == "fp8":
             kv.kv_append_quant(kn, vn, st.tok_seq, tok_pos, st.block_table, st.k_scale[layer],
                                st.v_scale[layer], st.k_pool[layer], st.v_pool[layer],

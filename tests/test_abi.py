@@ -40,7 +40,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["kv_verify_tags", "kv_append_quant", "kv_append_bf16", "paged_decode_attn",
               "paged_decode_attn_workspace_bytes", "paged_decode_attn_partition_tokens",
-              "kv_status_str"]:
+              "paged_decode_attn_append", "kv_status_str"]:
         assert n in names
 
 
@@ -131,6 +131,29 @@ def test_attention_rejects_bad_arguments(lib):
     assert attn(lib, sm_scale=float("nan")) == UNSUP
     assert attn(lib, sm_scale=float("inf")) == UNSUP
     assert attn(lib, batch=0, q=None) == OK
+
+
+def attn_append(lib, k_new=A, v_new=A, **kw):
+    args = dict(q=A, k_new=k_new, v_new=v_new, cache_dtype=0, k_pool=A, v_pool=A, k_scale=A,
+                v_scale=A, block_table=A, bt_stride=600, seq_lens=A, max_seq_len=9000,
+                abort=None, out=A, sm_scale=0.088, batch=64, num_q_heads=64, num_kv_heads=8,
+                head_dim=128, page_size=16, num_pages=40000, partition_tokens=0, workspace=A,
+                workspace_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return lib.paged_decode_attn_append(*args.values())
+
+
+def test_fused_append_attention_rejects_bad_arguments(lib):
+    assert attn_append(lib, k_new=None) == NULL
+    assert attn_append(lib, v_new=None) == NULL
+    assert attn_append(lib, k_new=A + 2) == ALIGN
+    assert attn_append(lib, v_new=A + 8) == ALIGN
+    assert attn_append(lib, head_dim=64) == UNSUP
+    assert attn_append(lib, k_scale=None) == NULL
+    assert attn_append(lib, cache_dtype=1, k_scale=None, v_scale=None, out=A + 4) == ALIGN
+    assert attn_append(lib, sm_scale=-1.0) == UNSUP
+    assert attn_append(lib, workspace=None, partition_tokens=512) == WORKSPACE
+    assert attn_append(lib, batch=0, k_new=None, v_new=None, q=None) == OK
 
 
 def test_workspace_and_partition_sizing(lib):

@@ -71,7 +71,8 @@ def test_c4_headline_full_size(kv):
     wl = synth.c4_headline(max_steps=2)
     say("c4: building 8-layer FP8 pools (batch 64, ctx 8192+U[0,1000])")
     st = DeviceState(wl, kv, cache="fp8", device=DEV)
-    ab, outs, inputs = gpu_step(st, 0)           # verify on, automatic partition: as benchmarked
+    # verify on, automatic partition, fused append + attention: as benchmarked
+    ab, outs, inputs = gpu_step(st, 0, fused=True)
     assert not ab.any()
     L = wl.seq_lens_at(0)
     samples = [(int(np.argmax(L)), 7, 5), (int(np.argmin(L)), 0, 0), (17, 3, 2), (40, 5, 7)]
@@ -126,7 +127,7 @@ def test_c5_skewed_split_k_and_churn(kv):
     wl.notes["churn_step"] = 1
     wl.apply_churn(np.random.default_rng(wl.notes["churn_rng_seed"]), 0.10, stale)
     st.upload_tags()
-    ab1, outs1, inputs1 = gpu_step(st, 1, partition_tokens=pt)
+    ab1, outs1, inputs1 = gpu_step(st, 1, partition_tokens=pt, fused=True)
     want = paged.verify_tags(wl.pool_tags, wl.block_table, wl.expected_tags, wl.seq_lens_at(1), 16)
     assert np.array_equal(ab1, want)
     assert sorted(np.flatnonzero(ab1).tolist()) == sorted(stale)

@@ -95,7 +95,7 @@ def test_append_bf16_is_a_copy(kv):
 # ---------------------------------------------------------------------------
 # whole decode steps on the small configurations, everything compared
 # ---------------------------------------------------------------------------
-def _full_step_check(kv, wl, cache="fp8", partition_tokens=0, label=""):
+def _full_step_check(kv, wl, cache="fp8", partition_tokens=0, label="", fused=False):
     say(f"{label}: build device state ({wl.name}, {cache})")
     st = DeviceState(wl, kv, cache=cache, device=DEV)
     orc = OracleRun(st)
@@ -104,7 +104,7 @@ def _full_step_check(kv, wl, cache="fp8", partition_tokens=0, label=""):
         assert np.array_equal(kd, orc.kp[layer]), f"{label}: K pool after fill, layer {layer}"
         assert np.array_equal(vd, orc.vp[layer]), f"{label}: V pool after fill, layer {layer}"
     say(f"{label}: step 0")
-    ab, outs, inputs = gpu_step(st, 0, partition_tokens=partition_tokens)
+    ab, outs, inputs = gpu_step(st, 0, partition_tokens=partition_tokens, fused=fused)
     ab_o, outs_o = orc.step(0, inputs)
     assert np.array_equal(ab, ab_o), f"{label}: abort {ab} vs oracle {ab_o}"
     for layer in st.layers:
@@ -134,6 +134,33 @@ def test_c2_bf16_step(kv):
     wl = synth.c2_mixed()
     _, _, ab = _full_step_check(kv, wl, "bf16", 1024, label="c2/bf16")
     assert np.flatnonzero(ab).tolist() == list(wl.stale)
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_c1_fused_append_attention_step(kv, cache):
+    st, _, ab = _full_step_check(kv, synth.c1_tiny(), cache, label=f"c1 fused/{cache}",
+                                 fused=True)
+    assert not ab.any()
+
+
+@pytest.mark.parametrize("partition_tokens", [0, 512, 4096])
+def test_c2_fused_step_with_stale_tag(kv, partition_tokens):
+    wl = synth.c2_mixed()
+    _, _, ab = _full_step_check(kv, wl, "fp8", partition_tokens,
+                                label=f"c2 fused/p{partition_tokens}", fused=True)
+    assert np.flatnonzero(ab).tolist() == list(wl.stale)
+
+
+def test_fused_equals_separate_calls_bit_for_bit(kv):
+    wl = synth.c2_mixed(max_steps=3)
+    a = DeviceState(wl, kv, device=DEV)
+    b = DeviceState(wl, kv, device=DEV)
+    for step in range(3):
+        ab1, o1, _ = gpu_step(a, step, partition_tokens=1024, fused=False)
+        ab2, o2, _ = gpu_step(b, step, partition_tokens=1024, fused=True)
+        assert np.array_equal(ab1, ab2)
+        assert np.array_equal(o1[0], o2[0], equal_nan=True)
+        assert torch.equal(a.k_pool[0], b.k_pool[0]) and torch.equal(a.v_pool[0], b.v_pool[0])
 
 
 # ---------------------------------------------------------------------------
