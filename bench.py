@@ -39,11 +39,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # for the kernel sources they were taken on (sha256 prefix of decode_attn.hip
 # + kv_device.h). See profiles/attn_partition_kernel_c4_hbm_counters.md.
 COUNTER_TRAFFIC = {
-    "source_sha": "ef9310e3a1752f40",
+    "source_sha": "7c2981e0a1421dc3",
     "workload": "c4_headline",
-    "read_bytes": 1.143e9,
-    "write_bytes": 2.097e6,
-    "algorithmic_bytes": 1144619443,
+    "read_bytes": 1.144e9,
+    "write_bytes": 2.490e6,
+    "algorithmic_bytes": 1143833636,
 }
 
 

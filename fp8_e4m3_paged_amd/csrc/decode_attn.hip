@@ -24,7 +24,7 @@
 //    (e4m3 -> f16 is exact), B = P^T taken straight from the score registers
 //    and rounded to f16 (nearest-even). BF16 caches use the bf16 instruction
 //    with P split into a bf16 high and low part (two products) instead;
-//  * the 4 wavefronts merge their (max, sum, output) in LDS; with one
+//  * the 4 (or 8) wavefronts merge their (max, sum, output) in LDS; with one
 //    partition the workgroup writes the final output, otherwise a partial
 //    that reduce_partials_kernel combines across partitions.
 #include "kv_device.h"
@@ -32,8 +32,8 @@
 
 namespace kvfp8 {
 
-constexpr int kAttnThreads = 256;
-constexpr int kWaves = kAttnThreads / 64;
+constexpr int kWaves = 4;                      // wavefronts per workgroup (wave mode, shared)
+constexpr int kWavesWide = 8;                  // shared mode when the grid fills one per CU
 constexpr int kAccStride = kDim + 4;           // padded LDS row (floats)
 constexpr float kLog2e = 1.4426950408889634f;
 // Partitions up to this many tokens run one per wavefront (see the kernel).
@@ -432,12 +432,15 @@ __device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc
 //     registers when it gets there, and stores the codes to the pool for
 //     later steps after its last load. Nothing in the launch reads the codes
 //     back from memory, so no fence or barrier is involved.
+//   NW = wavefronts per workgroup: 4, or 8 in shared mode when the grid has at
+//     most one workgroup per CU (e.g. 32 requests x 8 KV heads), so each CU
+//     still streams with 8 wavefronts and no split-K reduction is needed.
 // Occupancy is pinned at 2 waves per SIMD: the register pipeline needs ~200
 // VGPRs, and without the cap the scheduler may trade the in-flight loads for a
 // third wave (sinking the prefetches next to their uses), which halves the
 // streaming rate.
-template <bool FP8, bool WAVE_PARTS, bool APPEND>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool FP8, bool WAVE_PARTS, int NW, bool APPEND>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_partition_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint8_t* __restrict__ k_pool,
@@ -452,10 +455,12 @@ void attn_partition_kernel(
     // LDS: [wave][16] max, [wave][16] sum, [wave][group][kAccStride] output
     // (shared mode only), then the page ids of the partition(s).
     float* sm_m = smem;
-    float* sm_l = sm_m + kWaves * 16;
-    float* sm_acc = sm_l + kWaves * 16;
+    static_assert(!WAVE_PARTS || NW == kWaves, "wave mode runs 4 partitions per workgroup");
+    constexpr int kThreads = NW * 64;
+    float* sm_l = sm_m + NW * 16;
+    float* sm_acc = sm_l + NW * 16;
     int32_t* sm_ids =
-        reinterpret_cast<int32_t*>(sm_acc + (WAVE_PARTS ? 0 : kWaves * group * kAccStride));
+        reinterpret_cast<int32_t*>(sm_acc + (WAVE_PARTS ? 0 : NW * group * kAccStride));
 
     const int bid = blockIdx.x;
     const int g = bid % hkv;
@@ -476,7 +481,7 @@ void attn_partition_kernel(
         // Only the single-partition case owns the final output here; with
         // several partitions the reduction writes zeros for such requests.
         if (!WAVE_PARTS && n_parts == 1) {
-            for (int i = tid; i < group * kDim; i += kAttnThreads)
+            for (int i = tid; i < group * kDim; i += kThreads)
                 out[(static_cast<size_t>(b) * hq + g * group) * kDim + i] = 0.f;
         }
         return;
@@ -497,7 +502,7 @@ void attn_partition_kernel(
     {
         const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
         const int first = WAVE_PARTS ? lane : tid;
-        const int step = WAVE_PARTS ? 64 : kAttnThreads;
+        const int step = WAVE_PARTS ? 64 : kThreads;
         for (int k = first; k < npg; k += step) {
             const int32_t id = bt_row[k];
             bad |= (id < 0 || id >= num_pages);
@@ -533,7 +538,7 @@ void attn_partition_kernel(
         };
         // This wave's pairs: shared mode w, w + 4, ...; wave mode all of them.
         const int first = WAVE_PARTS ? 0 : wave;
-        const int stride = WAVE_PARTS ? 1 : kWaves;
+        const int stride = WAVE_PARTS ? 1 : NW;
         const int n_w = npairs > first ? (npairs - first + stride - 1) / stride : 0;
         const auto issue = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
             const int pr = first + stride * min(i, n_w - 1);
@@ -602,7 +607,7 @@ void attn_partition_kernel(
             part_ml[2 * pslot + 1] = bad ? -1.f : l_tot;
         }
     } else {
-        // ---- merge the 4 wavefronts --------------------------------------
+        // ---- merge the NW wavefronts -------------------------------------
         __syncthreads();   // the page ids are no longer read; LDS is reused below
         if (jgrp == 0) {
             sm_m[wave * 16 + col] = m_run;
@@ -617,17 +622,17 @@ void attn_partition_kernel(
         __syncthreads();
 
         const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
-        for (int it = tid; it < group * (kDim / 4); it += kAttnThreads) {
+        for (int it = tid; it < group * (kDim / 4); it += kThreads) {
             const int qh = it / (kDim / 4);
             const int d = (it % (kDim / 4)) * 4;
             float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
             const float M_use = (M == -INFINITY) ? 0.f : M;
             float lt = 0.f;
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 const float f = exp2f(sm_m[w * 16 + qh] - M_use);
                 lt += f * sm_l[w * 16 + qh];
                 o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
@@ -742,38 +747,60 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
     }
 }
 
+// gfx950 (MI355X) has 256 CUs; a grid of at most this many workgroups runs
+// one per CU.
+constexpr int64_t kNumCUs = 256;
+
+// Wave mode (one short partition per wavefront) only pays when it still
+// yields at least one 4-wave workgroup per CU.
 bool use_wave_partitions(const AttnArgs& a) {
-    return a.num_partitions > 1 && a.partition_tokens <= kWaveModeMaxTokens;
+    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads;
+    return a.num_partitions > 1 && a.partition_tokens <= kWaveModeMaxTokens &&
+           items * a.num_partitions >= kWaves * kNumCUs;
+}
+
+// Shared mode with 8 wavefronts when the grid has at most one workgroup per
+// CU. Limited to GQA groups of up to 8 query heads, which keeps the merge's
+// LDS (8 waves x group x 132 floats) within the default 64 KiB per workgroup.
+bool use_wide_workgroups(const AttnArgs& a) {
+    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads;
+    return !use_wave_partitions(a) && items * a.num_partitions <= kNumCUs &&
+           a.num_q_heads / a.num_kv_heads <= 8;
 }
 
 hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
     const int group = a.num_q_heads / a.num_kv_heads;
     const bool wave_mode = use_wave_partitions(a);
+    const int nw = use_wide_workgroups(a) ? kWavesWide : kWaves;
     const size_t ids_bytes = sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage) *
                              (wave_mode ? kWaves : 1);
-    const size_t lds = sizeof(float) * (2 * kWaves * 16 + (wave_mode ? 0 : kWaves * group * kAccStride)) +
+    const size_t lds = sizeof(float) * (2 * nw * 16 + (wave_mode ? 0 : nw * group * kAccStride)) +
                        ids_bytes;
     const uint32_t slots = wave_mode ? (a.num_partitions + kWaves - 1) / kWaves : a.num_partitions;
     const dim3 grid(slots * a.batch * a.num_kv_heads);
     const float sm_log2 = a.sm_scale * kLog2e;
-#define KVFP8_LAUNCH3(F8, WP, AP)                                                                \
-    hipLaunchKernelGGL((attn_partition_kernel<F8, WP, AP>), grid, dim3(kAttnThreads), lds,      \
+#define KVFP8_LAUNCH3(F8, WP, NW, AP)                                                            \
+    hipLaunchKernelGGL((attn_partition_kernel<F8, WP, NW, AP>), grid, dim3(NW * 64), lds,       \
                        stream, a.q, a.k_new, a.v_new, static_cast<uint8_t*>(a.k_pool),          \
                        static_cast<uint8_t*>(a.v_pool), F8 ? a.k_scale : nullptr,                \
                        F8 ? a.v_scale : nullptr, a.block_table, a.bt_stride, a.seq_lens,         \
                        a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2, a.batch,   \
                        a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens,           \
                        a.num_partitions)
-#define KVFP8_LAUNCH(F8, WP)                          \
-    do {                                              \
-        if (append) KVFP8_LAUNCH3(F8, WP, true);      \
-        else KVFP8_LAUNCH3(F8, WP, false);            \
+#define KVFP8_LAUNCH(F8, WP, NW)                          \
+    do {                                                  \
+        if (append) KVFP8_LAUNCH3(F8, WP, NW, true);      \
+        else KVFP8_LAUNCH3(F8, WP, NW, false);            \
     } while (0)
     const bool append = a.k_new != nullptr;
     if (fp8) {
-        if (wave_mode) KVFP8_LAUNCH(true, true); else KVFP8_LAUNCH(true, false);
+        if (wave_mode) KVFP8_LAUNCH(true, true, kWaves);
+        else if (nw == kWavesWide) KVFP8_LAUNCH(true, false, kWavesWide);
+        else KVFP8_LAUNCH(true, false, kWaves);
     } else {
-        if (wave_mode) KVFP8_LAUNCH(false, true); else KVFP8_LAUNCH(false, false);
+        if (wave_mode) KVFP8_LAUNCH(false, true, kWaves);
+        else if (nw == kWavesWide) KVFP8_LAUNCH(false, false, kWavesWide);
+        else KVFP8_LAUNCH(false, false, kWaves);
     }
 #undef KVFP8_LAUNCH
 #undef KVFP8_LAUNCH3

@@ -16,13 +16,15 @@
 namespace kvfp8 {
 
 // ---------------------------------------------------------------------------
-// kv_verify_tags: one 256-thread workgroup per request. Each thread checks up
-// to 4 logical pages per sweep; loads of a sweep are independent so their
-// latencies overlap. The workgroup ORs the per-thread verdicts and one thread
-// writes the request's flag.
+// kv_verify_tags: one 1024-thread workgroup per request. Each thread checks up
+// to 8 logical pages per sweep; loads of a sweep are independent so their
+// latencies overlap, and one sweep covers 8192 pages (131,072 tokens), so
+// even a very long request costs two dependent round trips (table entries,
+// then the gathered pool tags). The workgroup ORs the per-thread verdicts and
+// one thread writes the request's flag.
 // ---------------------------------------------------------------------------
-constexpr int kVerifyThreads = 256;
-constexpr int kVerifyUnroll = 4;
+constexpr int kVerifyThreads = 1024;
+constexpr int kVerifyUnroll = 8;
 
 __global__ __launch_bounds__(kVerifyThreads) void verify_tags_kernel(
     const uint32_t* __restrict__ pool_tags, int32_t num_pages,

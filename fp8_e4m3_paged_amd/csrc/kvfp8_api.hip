@@ -35,14 +35,19 @@ int check_append_common(const void* k_new, const void* v_new, const int32_t* tok
 
 // Automatic split-K size. Long partitions stream best (the per-workgroup
 // set-up and the partial traffic are amortised, and no reduction pass is
-// needed with one partition), so split only as far as needed to give every
-// compute unit at least two (request, KV head, partition) workgroups: 512 of
-// them for the 256 CUs. Partitions are equal shares of max_seq_len rounded up
-// to 256 tokens, at least 512 and at most the LDS page list's capacity.
+// needed with one partition), so split only as far as needed to keep 8
+// wavefronts streaming on every compute unit. Partitions are equal shares of
+// max_seq_len rounded up to 256 tokens, at least 512 and at most the LDS page
+// list's capacity.
 int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+    // 512 four-wave workgroups for the 256 CUs, or, when the (request, KV
+    // head) items divide 256, 256 eight-wave ones (half the partitions to
+    // reduce). One partition when the items alone fill the chip.
     const int64_t items = static_cast<int64_t>(batch) * num_kv_heads;
-    const int64_t target = 512;
-    int64_t parts = items >= target ? 1 : (target + items - 1) / items;
+    int64_t parts;
+    if (items >= 512) parts = 1;
+    else if (items <= 256 && 256 % items == 0) parts = 256 / items;
+    else parts = (512 + items - 1) / items;
     int64_t tokens = (static_cast<int64_t>(max_seq_len) + parts - 1) / parts;
     tokens = ((tokens + 255) / 256) * 256;
     if (tokens < 512) tokens = 512;
