@@ -27,6 +27,8 @@
 //  * the 4 (or 8) wavefronts merge their (max, sum, output) in LDS; with one
 //    partition the workgroup writes the final output, otherwise a partial
 //    that reduce_partials_kernel combines across partitions.
+#include <algorithm>
+
 #include "kv_device.h"
 #include "kv_launch.h"
 
@@ -418,28 +420,104 @@ __device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc
     }
 }
 
-// Partition kernel. Grid: blockIdx.x = (slot * batch + b) * hkv + g.
-//   WAVE_PARTS = false: slot = partition p; the 4 wavefronts share it (pairs
-//     w, w + 4, ...) and merge in LDS; used for long partitions.
-//   WAVE_PARTS = true: slot covers partitions 4*slot .. 4*slot + 3 of (b, g),
-//     one per wavefront, each written straight from registers; used for
-//     short partitions, where sharing would leave each wave too few pairs to
-//     keep its pipeline full.
-//   APPEND = true (paged_decode_attn_append): the wavefront that will process
-//     the page pair holding the new token t = L - 1 quantizes k_new[b][g] /
-//     v_new[b][g] itself (same encoder as kv_append_quant) while its first
-//     loads are in flight, overwrites that slot's bytes in the pair's
-//     registers when it gets there, and stores the codes to the pool for
-//     later steps after its last load. Nothing in the launch reads the codes
-//     back from memory, so no fence or barrier is involved.
-//   NW = wavefronts per workgroup: 4, or 8 in shared mode when the grid has at
-//     most one workgroup per CU (e.g. 32 requests x 8 KV heads), so each CU
-//     still streams with 8 wavefronts and no split-K reduction is needed.
+// B operand of QK^T for query heads q_row .. q_row + group - 1: column col =
+// query head q_row + col, slots = dims 32*jgrp + 8c + i. Columns past the
+// group stay zero.
+__device__ __forceinline__ void load_q_operand(bf16x8 (&qop)[4], const uint16_t* __restrict__ q,
+                                               size_t q_row, int group, int col, int jgrp) {
+    if (col < group) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(q + (q_row + col) * kDim + 32 * jgrp);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, qp[c]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+}
+
+// One wavefront's share of the partition [t_begin, t_end) of (b, g): page
+// pairs first, first + stride, ... of the partition's npg pages, where page k
+// of the partition is pool tile tile_of(k). Accumulates the online softmax
+// into (m_run, l_run, acc_o).
+// APPEND: the wavefront whose share holds the new token t = L - 1 loads its
+// bf16 K/V row (k_row, v_row) before its first tile loads (so every wait
+// count in the pipeline stays static), encodes it (same encoder as
+// kv_append_quant) while those tiles are in flight, overwrites the token's
+// slot in the pair's registers when it gets there, and stores the codes to
+// the pool after its last load. Nothing in the launch reads those codes back
+// from memory, so no fence or barrier is involved.
+template <bool FP8, bool APPEND, typename TileOf>
+__device__ __forceinline__ void stream_share(
+    TileOf&& tile_of, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int npg,
+    int pg0, int first, int stride, int t_begin, int t_end, int L, int lane, int jgrp,
+    float s_scale, const bf16x8 (&qop)[4], const uint16_t* __restrict__ k_row,
+    const uint16_t* __restrict__ v_row, const float* __restrict__ ks_ptr,
+    const float* __restrict__ vs_ptr, float& m_run, float& l_run, f32x4 (&acc_o)[8]) {
+    const int npairs = (npg + 1) / 2;
+    const int n_w = npairs > first ? (npairs - first + stride - 1) / stride : 0;
+    const auto issue = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
+        const int pr = first + stride * min(i, n_w - 1);
+        load_pair<FP8>(t, k_pool, v_pool, tile_of(2 * pr), tile_of(min(2 * pr + 1, npg - 1)),
+                       lane);
+    };
+    const int t_new = L - 1;
+    const int pr_new = (t_new / kPage - pg0) / 2;
+    const bool owns_new = APPEND && t_new >= t_begin && t_new < t_end && pr_new >= first &&
+                          (pr_new - first) % stride == 0;
+    const bool new_in_b = ((t_new / kPage - pg0) % 2) == 1;
+    NewTokenRaw raw;
+    NewToken<FP8> nt;
+    if constexpr (APPEND) {
+        if (owns_new) load_new_token(raw, lane, k_row, v_row);
+    }
+    const auto prepare = [&]() __attribute__((always_inline)) {
+        if constexpr (APPEND) {
+            if (owns_new) encode_new_token<FP8>(nt, raw, FP8 ? *ks_ptr : 1.0f, FP8 ? *vs_ptr : 1.0f);
+        }
+    };
+    const auto proc = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
+        process_pair<FP8>(t, (pg0 + 2 * (first + stride * i)) * kPage, t_end, jgrp, s_scale, qop,
+                          m_run, l_run, acc_o);
+    };
+    const auto proc_end = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
+        const int pr = first + stride * i;
+        if constexpr (APPEND) {
+            if (owns_new && pr == pr_new) {                  // wave-uniform
+                apply_new_token<FP8>(t.ka, t.va, nt, t_new % kPage, lane, !new_in_b);
+                apply_new_token<FP8>(t.kb, t.vb, nt, t_new % kPage, lane, new_in_b);
+            }
+        }
+        process_pair<FP8>(t, (pg0 + 2 * pr) * kPage, t_end, jgrp, s_scale, qop, m_run, l_run,
+                          acc_o);
+    };
+    pipeline_pairs<FP8>(n_w, issue, proc, proc_end, prepare);
+    if constexpr (APPEND) {
+        if (owns_new) {
+            const size_t tile = tile_of(t_new / kPage - pg0);
+            constexpr int T = FP8 ? kTileFp8 : kTileBf16;
+            store_new_token<FP8>(nt, t_new % kPage, lane, k_pool + tile * T, v_pool + tile * T);
+        }
+    }
+}
+
+__device__ __forceinline__ bool request_ok(const int32_t* __restrict__ seq_lens,
+                                           const uint8_t* __restrict__ abort, int b, int L,
+                                           int32_t max_seq_len, int32_t bt_stride) {
+    const bool aborted = abort != nullptr && abort[b] != 0;
+    return !aborted && L >= 1 && L <= max_seq_len &&
+           (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
+}
+
+// Shared-mode partition kernel. Grid: blockIdx.x = (p * batch + b) * hkv + g;
+// the NW wavefronts of the workgroup share partition p of (b, g) (pairs w,
+// w + NW, ...) and merge in LDS. NW = 4, or 8 when the grid has at most one
+// workgroup per CU (e.g. 32 requests x 8 KV heads), so each CU still streams
+// with 8 wavefronts and no split-K reduction is needed.
 // Occupancy is pinned at 2 waves per SIMD: the register pipeline needs ~200
 // VGPRs, and without the cap the scheduler may trade the in-flight loads for a
 // third wave (sinking the prefetches next to their uses), which halves the
 // streaming rate.
-template <bool FP8, bool WAVE_PARTS, int NW, bool APPEND>
+template <bool FP8, int NW, bool APPEND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_partition_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
@@ -451,21 +529,19 @@ void attn_partition_kernel(
     float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv, int32_t num_pages,
     int32_t part_tokens, int32_t n_parts) {
     extern __shared__ float smem[];
-    const int group = hq / hkv;
-    // LDS: [wave][16] max, [wave][16] sum, [wave][group][kAccStride] output
-    // (shared mode only), then the page ids of the partition(s).
-    float* sm_m = smem;
-    static_assert(!WAVE_PARTS || NW == kWaves, "wave mode runs 4 partitions per workgroup");
     constexpr int kThreads = NW * 64;
+    const int group = hq / hkv;
+    // LDS: [wave][16] max, [wave][16] sum, [wave][group][kAccStride] output,
+    // then the page ids of the partition.
+    float* sm_m = smem;
     float* sm_l = sm_m + NW * 16;
     float* sm_acc = sm_l + NW * 16;
-    int32_t* sm_ids =
-        reinterpret_cast<int32_t*>(sm_acc + (WAVE_PARTS ? 0 : NW * group * kAccStride));
+    int32_t* sm_ids = reinterpret_cast<int32_t*>(sm_acc + NW * group * kAccStride);
 
     const int bid = blockIdx.x;
     const int g = bid % hkv;
     const int b = (bid / hkv) % batch;
-    const int slot = bid / (hkv * batch);
+    const int p = bid / (hkv * batch);
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wavefront
     const int lane = tid % 64;
@@ -473,40 +549,30 @@ void attn_partition_kernel(
     const int jgrp = lane / 16;      // k-group of the operands / row group of the result
 
     const int L = seq_lens[b];
-    const bool aborted = abort != nullptr && abort[b] != 0;
-    const bool valid_req = !aborted && L >= 1 && L <= max_seq_len &&
-                           (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
-    const int p_first = WAVE_PARTS ? slot * kWaves : slot;
-    if (!valid_req || static_cast<int64_t>(p_first) * part_tokens >= L) {
+    if (!request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride) ||
+        static_cast<int64_t>(p) * part_tokens >= L) {
         // Only the single-partition case owns the final output here; with
         // several partitions the reduction writes zeros for such requests.
-        if (!WAVE_PARTS && n_parts == 1) {
+        if (n_parts == 1) {
             for (int i = tid; i < group * kDim; i += kThreads)
                 out[(static_cast<size_t>(b) * hq + g * group) * kDim + i] = 0.f;
         }
         return;
     }
-    const int p = WAVE_PARTS ? p_first + wave : slot;
     const int t_begin = p * part_tokens;
-    const bool active = t_begin < L;            // always true in shared mode
-    const int t_end = active ? min(L, t_begin + part_tokens) : t_begin;
+    const int t_end = min(L, t_begin + part_tokens);
     const int pg0 = t_begin / kPage;
-    const int npg = active ? (t_end + kPage - 1) / kPage - pg0 : 0;
-    const int npairs = (npg + 1) / 2;
+    const int npg = (t_end + kPage - 1) / kPage - pg0;
 
-    // Page ids -> LDS; any id outside the pool poisons the request (its output
-    // becomes zero and no page of it is read). In wave mode every partition of
-    // the workgroup belongs to the same request, so one verdict serves all.
-    int32_t* ids = WAVE_PARTS ? sm_ids + wave * (part_tokens / kPage) : sm_ids;
+    // Page ids -> LDS; any id outside the pool poisons the partition (its
+    // output, and the request's, becomes zero and none of its pages is read).
     int bad = 0;
     {
         const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
-        const int first = WAVE_PARTS ? lane : tid;
-        const int step = WAVE_PARTS ? 64 : kThreads;
-        for (int k = first; k < npg; k += step) {
+        for (int k = tid; k < npg; k += kThreads) {
             const int32_t id = bt_row[k];
             bad |= (id < 0 || id >= num_pages);
-            ids[k] = id;
+            sm_ids[k] = id;
         }
     }
     bad = __syncthreads_or(bad);
@@ -519,135 +585,199 @@ void attn_partition_kernel(
     for (int c = 0; c < 8; ++c) acc_o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (!bad) {
-        // B operand of QK^T: column = query head g*G + col, slots = dims
-        // 32*jgrp + 8c + i. Columns past the group stay zero.
         bf16x8 qop[4];
-        if (col < group) {
-            const u32x4* qp = reinterpret_cast<const u32x4*>(q + (q_row + col) * kDim + 32 * jgrp);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, qp[c]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) qop[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        }
+        load_q_operand(qop, q, q_row, group, col, jgrp);
         const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
-
         const auto tile_of = [&](int page_idx) __attribute__((always_inline)) -> size_t {
-            const int id = __builtin_amdgcn_readfirstlane(ids[page_idx]);
+            const int id = __builtin_amdgcn_readfirstlane(sm_ids[page_idx]);
             return static_cast<size_t>(id) * hkv + g;
         };
-        // This wave's pairs: shared mode w, w + 4, ...; wave mode all of them.
-        const int first = WAVE_PARTS ? 0 : wave;
-        const int stride = WAVE_PARTS ? 1 : NW;
-        const int n_w = npairs > first ? (npairs - first + stride - 1) / stride : 0;
-        const auto issue = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
-            const int pr = first + stride * min(i, n_w - 1);
-            load_pair<FP8>(t, k_pool, v_pool, tile_of(2 * pr), tile_of(min(2 * pr + 1, npg - 1)),
-                           lane);
-        };
-        // Fused append: the wave that will process the new token's pair loads
-        // its bf16 inputs before its first tile loads (so every wait count in
-        // the pipeline stays static), encodes them in registers while those
-        // tiles are in flight, patches the pair's registers when it gets there,
-        // and stores the codes to the pool after its last load.
-        const int t_new = L - 1;
-        const int pr_new = (t_new / kPage - pg0) / 2;
-        const bool owns_new = APPEND && t_new >= t_begin && t_new < t_end &&
-                              pr_new >= first && (pr_new - first) % stride == 0;
-        const bool new_in_b = ((t_new / kPage - pg0) % 2) == 1;
         const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
-        NewTokenRaw raw;
-        NewToken<FP8> nt;
-        if constexpr (APPEND) {
-            if (owns_new) load_new_token(raw, lane, k_new + new_row, v_new + new_row);
-        }
-        const auto prepare = [&]() __attribute__((always_inline)) {
-            if constexpr (APPEND) {
-                if (owns_new)
-                    encode_new_token<FP8>(nt, raw, FP8 ? k_scale[g] : 1.0f, FP8 ? v_scale[g] : 1.0f);
-            }
-        };
-        const auto proc = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
-            process_pair<FP8>(t, (pg0 + 2 * (first + stride * i)) * kPage, t_end, jgrp, s_scale,
-                              qop, m_run, l_run, acc_o);
-        };
-        const auto proc_end = [&](PairTiles<FP8>& t, int i) __attribute__((always_inline)) {
-            const int pr = first + stride * i;
-            if constexpr (APPEND) {
-                if (owns_new && pr == pr_new) {                  // wave-uniform
-                    apply_new_token<FP8>(t.ka, t.va, nt, t_new % kPage, lane, !new_in_b);
-                    apply_new_token<FP8>(t.kb, t.vb, nt, t_new % kPage, lane, new_in_b);
-                }
-            }
-            process_pair<FP8>(t, (pg0 + 2 * pr) * kPage, t_end, jgrp, s_scale, qop, m_run, l_run,
-                              acc_o);
-        };
-        pipeline_pairs<FP8>(n_w, issue, proc, proc_end, prepare);
-        if constexpr (APPEND) {
-            if (owns_new) {
-                const size_t tile = tile_of(t_new / kPage - pg0);
-                constexpr int T = FP8 ? kTileFp8 : kTileBf16;
-                store_new_token<FP8>(nt, t_new % kPage, lane, k_pool + tile * T, v_pool + tile * T);
-            }
-        }
+        stream_share<FP8, APPEND>(tile_of, k_pool, v_pool, npg, pg0, wave, NW, t_begin, t_end, L,
+                                  lane, jgrp, s_scale, qop, k_new + new_row, v_new + new_row,
+                                  k_scale + g, v_scale + g, m_run, l_run, acc_o);
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
 
-    if constexpr (WAVE_PARTS) {
-        // ---- one partition per wavefront: write its partial directly -----
-        if (!active || col >= group) return;
-        const size_t pslot = (q_row + col) * n_parts + p;
-        float* dst = part_acc + pslot * kDim + 4 * jgrp;
+    // ---- merge the NW wavefronts -----------------------------------------
+    if (jgrp == 0) {
+        sm_m[wave * 16 + col] = m_run;
+        sm_l[wave * 16 + col] = l_tot;
+    }
+    if (col < group) {
+        float* row = sm_acc + (wave * group + col) * kAccStride;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc_o[c];
-        if (jgrp == 0) {
-            part_ml[2 * pslot] = m_run;
-            part_ml[2 * pslot + 1] = bad ? -1.f : l_tot;
-        }
-    } else {
-        // ---- merge the NW wavefronts -------------------------------------
-        __syncthreads();   // the page ids are no longer read; LDS is reused below
-        if (jgrp == 0) {
-            sm_m[wave * 16 + col] = m_run;
-            sm_l[wave * 16 + col] = l_tot;
-        }
-        if (col < group) {
-            float* row = sm_acc + (wave * group + col) * kAccStride;
+        for (int c = 0; c < 8; ++c)
+            *reinterpret_cast<f32x4*>(row + 16 * c + 4 * jgrp) = acc_o[c];
+    }
+    __syncthreads();
+
+    const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
+    for (int it = tid; it < group * (kDim / 4); it += kThreads) {
+        const int qh = it / (kDim / 4);
+        const int d = (it % (kDim / 4)) * 4;
+        float M = -INFINITY;
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<f32x4*>(row + 16 * c + 4 * jgrp) = acc_o[c];
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float lt = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = exp2f(sm_m[w * 16 + qh] - M_use);
+            lt += f * sm_l[w * 16 + qh];
+            o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
+        }
+        if (n_parts == 1) {
+            f32x4 r = {0.f, 0.f, 0.f, 0.f};
+            if (!bad && lt > 0.f) r = o * (vs / lt);
+            *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
+        } else {
+            const size_t pslot = (q_row + qh) * n_parts + p;
+            *reinterpret_cast<f32x4*>(part_acc + pslot * kDim + d) = o;
+            if (d == 0) {
+                part_ml[2 * pslot] = M;
+                part_ml[2 * pslot + 1] = bad ? -1.f : lt;
+            }
+        }
+    }
+}
+
+// Wave-mode kernel for short partitions (<= 2048 tokens): every wavefront
+// works alone on whole partitions, so no wavefront's pipeline is starved by
+// sharing a short partition, and the grid is persistent. The (request,
+// partition, KV head) items that have work are numbered request by request,
+// KV head fastest (the 4 wavefronts of a workgroup then read neighbouring
+// tiles of the same pages); each workgroup first builds the per-request
+// prefix of partition counts in LDS, then wavefront w of the grid takes items
+// w, w + W, w + 2W, ... (W = all wavefronts of the grid), finding each item's
+// request by binary search. Aborted, empty or unmappable requests have no
+// items (the reduction writes their zeros), and no workgroup is launched
+// only to find it has nothing to do. Each item writes its partial straight
+// from registers; its page ids sit in two registers per lane (page k in lane
+// k % 64 of register k / 64) and are broadcast with readlane.
+constexpr int kWaveModeMaxBatch = 4096;     // LDS: 2 * batch + 1 ints
+
+template <bool FP8, bool APPEND>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_wave_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int32_t bt_stride,
+    const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const uint8_t* __restrict__ abort,
+    float* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_acc,
+    float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv, int32_t num_pages,
+    int32_t part_tokens, int32_t n_parts) {
+    constexpr int kThreads = kWaves * 64;
+    extern __shared__ int32_t wsm[];
+    int32_t* sm_pre = wsm;                  // [batch + 1] partitions before request b
+    int32_t* sm_len = wsm + batch + 1;      // [batch] seq_lens
+    __shared__ int32_t sm_wsum[kWaves];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64;
+    const int col = lane % 16;
+    const int jgrp = lane / 16;
+    const int group = hq / hkv;
+
+    // ---- per-request partition counts and their exclusive prefix ---------
+    {
+        const int per = (batch + kThreads - 1) / kThreads;     // contiguous requests per thread
+        const int b0 = tid * per;
+        int local = 0;
+        for (int k = 0; k < per; ++k) {
+            const int b = b0 + k;
+            if (b >= batch) break;
+            const int L = seq_lens[b];
+            sm_len[b] = L;
+            if (request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride))
+                local += (L + part_tokens - 1) / part_tokens;
+        }
+        int incl = local;                                      // inclusive scan in the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            if (lane >= o) incl += v;
+        }
+        if (lane == 63) sm_wsum[wave] = incl;
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += sm_wsum[w];
+        int run = before + incl - local;                       // exclusive prefix of b0
+        for (int k = 0; k < per; ++k) {
+            const int b = b0 + k;
+            if (b >= batch) break;
+            sm_pre[b] = run;
+            const int L = sm_len[b];
+            if (request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride))
+                run += (L + part_tokens - 1) / part_tokens;
+        }
+        if (tid == kThreads - 1) {
+            int total = 0;
+            for (int w = 0; w < kWaves; ++w) total += sm_wsum[w];
+            sm_pre[batch] = total;
         }
         __syncthreads();
+    }
+    const int64_t n_items = static_cast<int64_t>(sm_pre[batch]) * hkv;
+    const int64_t w_stride = static_cast<int64_t>(gridDim.x) * kWaves;
 
-        const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
-        for (int it = tid; it < group * (kDim / 4); it += kThreads) {
-            const int qh = it / (kDim / 4);
-            const int d = (it % (kDim / 4)) * 4;
-            float M = -INFINITY;
+    for (int64_t item = static_cast<int64_t>(blockIdx.x) * kWaves + wave; item < n_items;
+         item += w_stride) {
+        const int g = static_cast<int>(item % hkv);
+        const int pidx = static_cast<int>(item / hkv);
+        int lo = 0, hi = batch - 1;                            // last b with pre[b] <= pidx
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (sm_pre[mid] <= pidx) lo = mid;
+            else hi = mid - 1;
+        }
+        const int b = __builtin_amdgcn_readfirstlane(lo);
+        const int p = __builtin_amdgcn_readfirstlane(pidx - sm_pre[b]);
+        const int L = __builtin_amdgcn_readfirstlane(sm_len[b]);
+        const int t_begin = p * part_tokens;
+        const int t_end = min(L, t_begin + part_tokens);
+        const int pg0 = t_begin / kPage;
+        const int npg = (t_end + kPage - 1) / kPage - pg0;     // 1 .. 128
+
+        const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
+        const int32_t id0 = lane < npg ? bt_row[lane] : 0;
+        const int32_t id1 = lane + 64 < npg ? bt_row[lane + 64] : 0;
+        const bool bad = __builtin_amdgcn_ballot_w64((id0 < 0 || id0 >= num_pages) ||
+                                                     (id1 < 0 || id1 >= num_pages)) != 0;
+
+        const size_t q_row = static_cast<size_t>(b) * hq + g * group;
+        float m_run = -INFINITY;
+        float l_run = 0.f;
+        f32x4 acc_o[8];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
-            const float M_use = (M == -INFINITY) ? 0.f : M;
-            float lt = 0.f;
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 8; ++c) acc_o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!bad) {
+            bf16x8 qop[4];
+            load_q_operand(qop, q, q_row, group, col, jgrp);
+            const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
+            const auto tile_of = [&](int page_idx) __attribute__((always_inline)) -> size_t {
+                const int id = __builtin_amdgcn_readlane(page_idx < 64 ? id0 : id1, page_idx % 64);
+                return static_cast<size_t>(id) * hkv + g;
+            };
+            const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
+            stream_share<FP8, APPEND>(tile_of, k_pool, v_pool, npg, pg0, 0, 1, t_begin, t_end, L,
+                                      lane, jgrp, s_scale, qop, k_new + new_row, v_new + new_row,
+                                      k_scale + g, v_scale + g, m_run, l_run, acc_o);
+        }
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (col < group) {
+            const size_t pslot = (q_row + col) * n_parts + p;
+            float* dst = part_acc + pslot * kDim + 4 * jgrp;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float f = exp2f(sm_m[w * 16 + qh] - M_use);
-                lt += f * sm_l[w * 16 + qh];
-                o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
-            }
-            if (n_parts == 1) {
-                f32x4 r = {0.f, 0.f, 0.f, 0.f};
-                if (!bad && lt > 0.f) r = o * (vs / lt);
-                *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
-            } else {
-                const size_t pslot = (q_row + qh) * n_parts + p;
-                *reinterpret_cast<f32x4*>(part_acc + pslot * kDim + d) = o;
-                if (d == 0) {
-                    part_ml[2 * pslot] = M;
-                    part_ml[2 * pslot + 1] = bad ? -1.f : lt;
-                }
+            for (int c = 0; c < 8; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc_o[c];
+            if (jgrp == 0) {
+                part_ml[2 * pslot] = m_run;
+                part_ml[2 * pslot + 1] = bad ? -1.f : l_tot;
             }
         }
     }
@@ -751,12 +881,13 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
 // one per CU.
 constexpr int64_t kNumCUs = 256;
 
-// Wave mode (one short partition per wavefront) only pays when it still
-// yields at least one 4-wave workgroup per CU.
+// Wave mode (one short partition per wavefront) only pays when there are
+// enough partitions for at least one 4-wave workgroup per CU; its LDS holds
+// two ints per request.
 bool use_wave_partitions(const AttnArgs& a) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads;
     return a.num_partitions > 1 && a.partition_tokens <= kWaveModeMaxTokens &&
-           items * a.num_partitions >= kWaves * kNumCUs;
+           a.batch <= kWaveModeMaxBatch && items * a.num_partitions >= kWaves * kNumCUs;
 }
 
 // Shared mode with 8 wavefronts when the grid has at most one workgroup per
@@ -770,40 +901,50 @@ bool use_wide_workgroups(const AttnArgs& a) {
 
 hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
     const int group = a.num_q_heads / a.num_kv_heads;
-    const bool wave_mode = use_wave_partitions(a);
-    const int nw = use_wide_workgroups(a) ? kWavesWide : kWaves;
-    const size_t ids_bytes = sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage) *
-                             (wave_mode ? kWaves : 1);
-    const size_t lds = sizeof(float) * (2 * nw * 16 + (wave_mode ? 0 : nw * group * kAccStride)) +
-                       ids_bytes;
-    const uint32_t slots = wave_mode ? (a.num_partitions + kWaves - 1) / kWaves : a.num_partitions;
-    const dim3 grid(slots * a.batch * a.num_kv_heads);
     const float sm_log2 = a.sm_scale * kLog2e;
-#define KVFP8_LAUNCH3(F8, WP, NW, AP)                                                            \
-    hipLaunchKernelGGL((attn_partition_kernel<F8, WP, NW, AP>), grid, dim3(NW * 64), lds,       \
-                       stream, a.q, a.k_new, a.v_new, static_cast<uint8_t*>(a.k_pool),          \
-                       static_cast<uint8_t*>(a.v_pool), F8 ? a.k_scale : nullptr,                \
-                       F8 ? a.v_scale : nullptr, a.block_table, a.bt_stride, a.seq_lens,         \
-                       a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2, a.batch,   \
-                       a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens,           \
-                       a.num_partitions)
-#define KVFP8_LAUNCH(F8, WP, NW)                          \
-    do {                                                  \
-        if (append) KVFP8_LAUNCH3(F8, WP, NW, true);      \
-        else KVFP8_LAUNCH3(F8, WP, NW, false);            \
-    } while (0)
     const bool append = a.k_new != nullptr;
-    if (fp8) {
-        if (wave_mode) KVFP8_LAUNCH(true, true, kWaves);
-        else if (nw == kWavesWide) KVFP8_LAUNCH(true, false, kWavesWide);
-        else KVFP8_LAUNCH(true, false, kWaves);
+    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads;
+#define KVFP8_ARGS                                                                               \
+    a.q, a.k_new, a.v_new, static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool),    \
+        fp8 ? a.k_scale : nullptr, fp8 ? a.v_scale : nullptr, a.block_table, a.bt_stride,        \
+        a.seq_lens, a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2, a.batch,      \
+        a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions
+    if (use_wave_partitions(a)) {
+        // persistent: at most 2 workgroups per CU, each wavefront loops over items
+        const int64_t wgs = std::min<int64_t>(2 * kNumCUs,
+                                              (items * a.num_partitions + kWaves - 1) / kWaves);
+        const size_t lds = sizeof(int32_t) * (2 * static_cast<size_t>(a.batch) + 1);
+#define KVFP8_WAVE(F8, AP)                                                                       \
+    hipLaunchKernelGGL((attn_wave_kernel<F8, AP>), dim3(static_cast<uint32_t>(wgs)),            \
+                       dim3(kWaves * 64), lds, stream, KVFP8_ARGS)
+        if (fp8) {
+            if (append) KVFP8_WAVE(true, true); else KVFP8_WAVE(true, false);
+        } else {
+            if (append) KVFP8_WAVE(false, true); else KVFP8_WAVE(false, false);
+        }
+#undef KVFP8_WAVE
     } else {
-        if (wave_mode) KVFP8_LAUNCH(false, true, kWaves);
-        else if (nw == kWavesWide) KVFP8_LAUNCH(false, false, kWavesWide);
-        else KVFP8_LAUNCH(false, false, kWaves);
+        const int nw = use_wide_workgroups(a) ? kWavesWide : kWaves;
+        const size_t lds = sizeof(float) * (2 * nw * 16 + nw * group * kAccStride) +
+                           sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage);
+        const dim3 grid(static_cast<uint32_t>(a.num_partitions * items));
+#define KVFP8_SHARED(F8, NW, AP)                                                                 \
+    hipLaunchKernelGGL((attn_partition_kernel<F8, NW, AP>), grid, dim3(NW * 64), lds, stream,   \
+                       KVFP8_ARGS)
+#define KVFP8_SHARED2(F8, NW)                                     \
+    do {                                                          \
+        if (append) KVFP8_SHARED(F8, NW, true);                   \
+        else KVFP8_SHARED(F8, NW, false);                         \
+    } while (0)
+        if (fp8) {
+            if (nw == kWavesWide) KVFP8_SHARED2(true, kWavesWide); else KVFP8_SHARED2(true, kWaves);
+        } else {
+            if (nw == kWavesWide) KVFP8_SHARED2(false, kWavesWide); else KVFP8_SHARED2(false, kWaves);
+        }
+#undef KVFP8_SHARED2
+#undef KVFP8_SHARED
     }
-#undef KVFP8_LAUNCH
-#undef KVFP8_LAUNCH3
+#undef KVFP8_ARGS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_partitions == 1) return e;
     hipLaunchKernelGGL(reduce_partials_kernel, dim3(a.batch * a.num_q_heads), dim3(kReduceThreads),

@@ -334,6 +334,43 @@ def test_edge_abort_bad_ids_and_overlong(kv, cache):
     assert np.all(got[3] == 0)
 
 
+def _runs_one_partition_per_wave(batch, hkv, max_len, pt):
+    """Whether the library picks its persistent wave-per-partition kernel
+    (short partitions and enough of them to give every CU a 4-wave group)."""
+    parts = -(-max_len // pt)
+    return parts > 1 and pt <= 2048 and batch <= 4096 and batch * hkv * parts >= 1024
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+@pytest.mark.parametrize("hq", [64, 128])
+def test_wave_mode_edges_aborts_and_bad_ids(kv, cache, hq):
+    """A batch large enough for the wave-per-partition kernel, with ragged
+    lengths (1 token, page and partition boundaries, empty requests) and
+    aborted and badly mapped requests between valid ones, so the kernel's
+    per-request numbering of its work items has to skip them."""
+    hkv = 8
+    base = [1, 2, 15, 16, 17, 31, 33, 100, 0, 47, 64, 65, 129, 200]
+    lens = base * 10
+    need = sum(max(1, -(-L // 16)) for L in lens)
+    e = _edge_state(kv, cache, hq, hkv, lens, pool_pages=need + 16)
+    bt = e["bt"].copy()
+    bt[5, 1] = 10 ** 6          # L = 31: its second page is outside the pool
+    bt[60, 1] = -2              # L = 17: likewise
+    bt[12, 8] = 10 ** 6         # L = 129: only the last (one-token) page is bad
+    abort = np.zeros(len(lens), np.uint8)
+    abort[4::9] = 1
+    zero = sorted({b for b, L in enumerate(lens) if L == 0} | {5, 60, 12} |
+                  set(np.flatnonzero(abort).tolist()))
+    want = _edge_oracle(e, cache, lens, abort=abort, bt=bt)
+    for pt in (16, 32, 64):
+        assert _runs_one_partition_per_wave(len(lens), hkv, max(lens), pt)
+        got = _edge_run(kv, e, cache, abort=abort, partition_tokens=pt, bt=bt)
+        helpers.check_attention(got, want, zero_rows=zero,
+                                label=f"wave mode {cache} G={hq // hkv} p{pt}")
+        b1 = lens.index(1)
+        assert np.allclose(got[b1], want[b1], rtol=2e-6, atol=1e-7)
+
+
 def test_verify_tags_cases(kv):
     rng = np.random.default_rng(17)
     num_pages, batch, width = 300, 9, 40
