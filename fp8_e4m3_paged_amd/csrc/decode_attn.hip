@@ -787,9 +787,10 @@ void attn_wave_kernel(
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p acc_p / sum_p w_p l_p
 // Requests that are aborted, empty, too long, or that a partition marked as
 // mapped to an invalid page (l_p < 0) get zeros. One 512-thread workgroup
-// per (b, h): the weights go through LDS, then 16 groups of 32 threads (4
-// dims each) sum interleaved partitions with independent, unrolled loads and
-// the 16 group sums are added in LDS.
+// per (b, h): 16 groups of 32 threads (4 dims each) sum interleaved
+// partitions. Each thread issues the loads of its first 16 partitions before
+// the weights are known, so they are in flight during the max / sum passes
+// (weights through LDS); the 16 group sums are added in LDS.
 constexpr int kReduceThreads = 512;
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -835,14 +836,30 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
         return;
     }
     const int np = (L + part_tokens - 1) / part_tokens;
+    const int grp = tid / (kDim / 4);               // 16 groups of 32 threads x 4 dims
+    const int d4 = tid % (kDim / 4);
+    constexpr int kGroups = kReduceThreads / (kDim / 4);
+    constexpr int kBatch = 16;                      // partitions per group in flight
+    const float* acc = part_acc + static_cast<size_t>(bh) * n_parts * kDim + 4 * d4;
+    const auto load_batch = [&](f32x4 (&v)[kBatch], int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int i = base + grp + kGroups * k;
+            v[k] = i < np ? *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i) * kDim)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    f32x4 v[kBatch];
+    load_batch(v, 0);
+
     const float* ml = part_ml + static_cast<size_t>(bh) * n_parts * 2;
     float mx = -INFINITY;
     int bad = 0;
     for (int i = tid; i < np; i += kReduceThreads) {
-        const float m = ml[2 * i];
-        bad |= ml[2 * i + 1] < 0.f;
-        wts[i] = m;
-        mx = fmaxf(mx, m);
+        const f32x2 e = *reinterpret_cast<const f32x2*>(ml + 2 * i);
+        bad |= e[1] < 0.f;
+        wts[i] = e[0];
+        mx = fmaxf(mx, e[0]);
     }
     bad = __syncthreads_or(bad);
     if (bad) {
@@ -857,14 +874,17 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
         wts[i] = w;
     }
     const float lt = block_sum(lsum, red);          // ends with a barrier: wts is complete
-    const int grp = tid / (kDim / 4);               // 16 groups of 32 threads x 4 dims
-    const int d4 = tid % (kDim / 4);
-    const float* acc = part_acc + static_cast<size_t>(bh) * n_parts * kDim + 4 * d4;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kGroups = kReduceThreads / (kDim / 4);
-#pragma unroll 4
-    for (int i = grp; i < np; i += kGroups)
-        num += wts[i] * *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i) * kDim);
+    for (int base = 0;;) {
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int i = base + grp + kGroups * k;
+            if (i < np) num += wts[i] * v[k];
+        }
+        base += kGroups * kBatch;
+        if (base >= np) break;
+        load_batch(v, base);
+    }
     __shared__ f32x4 part[kGroups][kDim / 4];
     part[grp][d4] = num;
     __syncthreads();

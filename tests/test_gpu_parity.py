@@ -163,6 +163,53 @@ def test_fused_equals_separate_calls_bit_for_bit(kv):
         assert torch.equal(a.k_pool[0], b.k_pool[0]) and torch.equal(a.v_pool[0], b.v_pool[0])
 
 
+@pytest.mark.parametrize("partition_tokens", [0, 512])
+def test_step_captured_in_a_graph_replays_like_eager(kv, partition_tokens):
+    """The tag check and the fused append + attention of one layer, captured
+    in a HIP graph (through torch's graph capture on its capture stream) and
+    replayed several times with eager work and synchronisations between
+    replays: every replay equals the eager run bit for bit. (Replaying the
+    same step rewrites the same codes into the same slot.)"""
+    wl = synth.c2_mixed(max_steps=1)
+    st = DeviceState(wl, kv, device=DEV, layers=[0])
+    seq = st.seq_lens(0)
+    q, kn, vn = st.step_layer_inputs(0, 0)
+    ws = workspace(wl, partition_tokens)
+    sm = sm_scale_for(wl)
+    shape = (wl.batch, wl.num_q_heads, wl.head_dim)
+
+    def step(out, abort):
+        kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq, abort)
+        kv.paged_decode_attn_append(q, kn, vn, st.k_pool[0], st.v_pool[0], st.k_scale[0],
+                                    st.v_scale[0], st.block_table, seq, wl.max_seq_len, out, sm,
+                                    workspace=ws, abort=abort, partition_tokens=partition_tokens)
+
+    out_e = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+    abort_e = torch.zeros(wl.batch, dtype=torch.uint8, device=DEV)
+    step(out_e, abort_e)
+    torch.cuda.synchronize()
+    kp_e, vp_e = st.k_pool[0].clone(), st.v_pool[0].clone()
+    assert int(abort_e.sum()) == 1
+
+    out_g = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+    abort_g = torch.zeros(wl.batch, dtype=torch.uint8, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(out_g, abort_g)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out_g.fill_(float("nan"))
+        abort_g.fill_(7)
+        out_e.add_(0.0)                      # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(abort_g, abort_e), f"replay {r}: abort mask"
+        assert torch.equal(out_g, out_e), f"replay {r}: attention output"
+        assert torch.equal(st.k_pool[0], kp_e) and torch.equal(st.v_pool[0], vp_e)
+    say(f"graph replay, partition {partition_tokens}: 4 replays equal the eager step")
+
+
 # ---------------------------------------------------------------------------
 # invariants on the GPU
 # ---------------------------------------------------------------------------
