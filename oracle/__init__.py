@@ -14,10 +14,12 @@ computes, in float64 numpy:
 * ``paged`` -- the three operations of the step as the pages state them:
   the batched page-tag check, quantize-on-append into pool pages, and decode
   attention over the pages with dequantize-on-read and a plain softmax.
+* ``ingest`` -- the prefill handoff into the decode cache: per-KV-head amax
+  and scale calibration, and the page-by-page write of whole prompts.
 
 The pages this follows are the five web reports of Cloudflare's FP8 KV-cache /
 page-tag post (remio.ai it/pt/ko, iitog.ru, manulx.blog). Each function names
 the page and section it follows.
 """
 
-from . import e4m3, paged  # noqa: F401
+from . import e4m3, ingest, paged  # noqa: F401
