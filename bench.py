@@ -74,8 +74,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--quiet", action="store_true")
-    ap.add_argument("--mode", default="step", choices=["step", "copy"],
-                    help="copy: time a plain device copy of --copy-mib MiB (counter calibration)")
+    ap.add_argument("--mode", default="step", choices=["step", "copy", "ingest"],
+                    help="copy: time a plain device copy of --copy-mib MiB (counter "
+                         "calibration); ingest: the prefill handoff of one layer's prompts")
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
 
@@ -201,10 +202,127 @@ def copy_calibration(args):
           flush=True)
 
 
+def _events_ms(fn, reps):
+    """Mean milliseconds of fn() over reps calls, HIP events on the current stream."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def ingest_bench(args):
+    """Prefill handoff of layer 0 of a workload's prompts: per-KV-head amax of
+    K and V, the scales, and the page-by-page write of every prompt
+    (kv_ingest_prefill), timed as one unit; beside it the same tokens through
+    the token-granular bulk kv_append_quant, for comparison."""
+    import numpy as np
+    import torch
+
+    import fp8_e4m3_paged_amd as kv
+    import synth
+    from synth import device as sd
+
+    kv.load()
+    dev = "cuda"
+    make = {"c3": synth.c3_uniform, "c4": synth.c4_headline, "c5": synth.c5_skewed}[args.config]
+    wl = make(max_steps=1)
+    fp8 = args.cache == "fp8"
+    hkv, D, P = wl.num_kv_heads, wl.head_dim, wl.page_size
+    ones = np.ones(hkv, np.float32)
+    st = sd.DeviceState(wl, kv, cache=args.cache, device=dev, layers=[0], fill=False,
+                        scales={0: (ones, ones)})
+    kr, start = sd.prompt_rows(wl, 0, "k", dev)
+    vr, _ = sd.prompt_rows(wl, 0, "v", dev)
+    lens0 = torch.from_numpy(wl.seq_lens0.astype(np.int32)).to(dev)
+    max_len = int(wl.seq_lens0.max())
+    ks = torch.empty(hkv, dtype=torch.float32, device=dev)
+    vs = torch.empty_like(ks)
+    amax = torch.zeros((2, hkv), dtype=torch.float32, device=dev)
+    cd = kv.KV_CACHE_FP8_E4M3 if fp8 else kv.KV_CACHE_BF16
+    kp, vp = st.k_pool[0], st.v_pool[0]
+
+    def handoff():
+        kv.ingest_layer(kr, vr, start, lens0, st.block_table, kp, vp, max_len, ks, vs,
+                        amax=amax, cache_dtype=cd)
+
+    def ingest_only():
+        kv.kv_ingest_prefill(kr, vr, start, lens0, st.block_table, kp, vp, max_len, ks, vs,
+                             cache_dtype=cd)
+
+    def amax_only():
+        kv.kv_amax_accumulate(kr, amax[0])
+
+    seq = torch.repeat_interleave(torch.arange(wl.batch, dtype=torch.int32, device=dev),
+                                  lens0.long()).to(torch.int32)
+    pos = torch.cat([torch.arange(int(L), dtype=torch.int32, device=dev)
+                     for L in wl.seq_lens0]).to(torch.int32)
+
+    def bulk_append():
+        if fp8:
+            kv.kv_append_quant(kr, vr, seq, pos, st.block_table, ks, vs, kp, vp)
+        else:
+            kv.kv_append_bf16(kr, vr, seq, pos, st.block_table, kp, vp)
+
+    for _ in range(max(1, args.warmup)):
+        handoff()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps)
+    t_handoff = _events_ms(handoff, reps)
+    t_ingest = _events_ms(ingest_only, reps)
+    t_amax = _events_ms(amax_only, reps)
+    t_append = _events_ms(bulk_append, max(1, reps // 4))
+
+    n_tok = int(wl.seq_lens0.sum())
+    pages = int((-(-wl.seq_lens0.astype(np.int64) // P)).sum())
+    esz = 1 if fp8 else 2
+    row_bytes = hkv * D * 2                            # one token's bf16 K (or V) row
+    tile = P * D * esz
+    ingest_bytes = 2 * n_tok * row_bytes + 2 * pages * hkv * tile + wl.batch * 12 + pages * 4
+    amax_bytes = 2 * n_tok * row_bytes if fp8 else 0
+    total = ingest_bytes + amax_bytes
+    append_bytes = 2 * n_tok * row_bytes + 2 * n_tok * hkv * D * esz + n_tok * 8
+    res = {
+        "metric": "prefill ingest: handoff of one layer's prompts into the paged cache, GB/s",
+        "mode": "ingest",
+        "value": round(total / t_handoff / 1e6, 1),
+        "unit": "GB/s",
+        "tokens_per_s": round(n_tok / t_handoff * 1e3, 1),
+        "ms_per_layer": round(t_handoff, 4),
+        "higher_is_better": True,
+        "dtype": "e4m3" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} prompts, layer 0", "batch": wl.batch,
+                   "tokens": n_tok, "pages": pages, "num_kv_heads": hkv, "head_dim": D,
+                   "cache": args.cache},
+        "roofline": {"bound": "hbm", "kernel": "ingest_kernel (kv_ingest_prefill)",
+                     "achieved": round(ingest_bytes / t_ingest / 1e6, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ingest_bytes / t_ingest / 1e6 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(t_ingest * 1e3, 2),
+                     "algorithmic_bytes_per_launch": ingest_bytes},
+        "amax_kernel": {"GBps": round(2 * n_tok * row_bytes / 2 / t_amax / 1e6, 1),
+                        "avg_launch_us": round(t_amax * 1e3, 2)} if fp8 else None,
+        "bulk_append_for_comparison": {"GBps": round(append_bytes / t_append / 1e6, 1),
+                                       "ms": round(t_append, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.mode == "copy":
         copy_calibration(args)
+        return
+    if args.mode == "ingest":
+        if args.gpus != 1:
+            print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
+                  file=sys.stderr)
+            sys.exit(2)
+        ingest_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

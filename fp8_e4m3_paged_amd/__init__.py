@@ -10,9 +10,11 @@ works but the first call raises ``KvLibraryMissing``.
 Entry points (same names as the C ABI):
     kv_verify_tags, kv_append_quant, kv_append_bf16, paged_decode_attn,
     paged_decode_attn_append, paged_decode_attn_workspace_bytes,
-    paged_decode_attn_partition_tokens, kv_status_str
+    paged_decode_attn_partition_tokens, kv_amax_accumulate,
+    kv_scales_from_amax, kv_ingest_prefill, kv_status_str
 plus ``decode_step``, which enqueues one decode step (tag check, then per
-layer append and attention) in the order the operations require.
+layer append and attention) in the order the operations require, and
+``ingest_layer``, which calibrates one layer's scales and writes its prompts.
 """
 
 from __future__ import annotations
@@ -25,6 +27,7 @@ __all__ = [
     "load", "kv_status_str", "kv_verify_tags", "kv_append_quant", "kv_append_bf16",
     "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_workspace_bytes",
     "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
+    "kv_amax_accumulate", "kv_scales_from_amax", "kv_ingest_prefill", "ingest_layer",
 ]
 
 KV_CACHE_FP8_E4M3 = 0
@@ -54,6 +57,7 @@ def lib_path() -> str:
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
+_L = ctypes.c_int64
 _SIGS = {
     "kv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "kv_verify_tags": (ctypes.c_int, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P]),
@@ -69,6 +73,10 @@ _SIGS = {
     "paged_decode_attn_append": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _I,
                                                 _P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _I,
                                                 _I, _P, ctypes.c_size_t, _P]),
+    "kv_amax_accumulate": (ctypes.c_int, [_P, _L, _I, _I, _P, _P]),
+    "kv_scales_from_amax": (ctypes.c_int, [_P, _I, _P, _P]),
+    "kv_ingest_prefill": (ctypes.c_int, [_P, _P, _L, _P, _P, _I, _I, _P, _I, _I, _P, _P, _P, _P,
+                                         _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -311,3 +319,71 @@ def decode_step(layers, block_table, seq_lens, tok_pos, tok_seq, max_seq_len, sm
                           sm_scale, workspace=workspace, abort=abort,
                           partition_tokens=partition_tokens, cache_dtype=cache_dtype,
                           stream=stream)
+
+
+def kv_amax_accumulate(x, amax_inout, stream=None):
+    """amax_inout[g] = max(amax_inout[g], max |x[:, g, :]|) over the finite bf16 values."""
+    d = _dt()
+    if x.dim() != 3 or amax_inout.numel() != x.shape[1]:
+        raise ValueError("x must be [rows][num_kv_heads][head_dim], amax_inout [num_kv_heads]")
+    st = load().kv_amax_accumulate(_ptr(x, "x", d["bf16"]), x.shape[0], x.shape[1], x.shape[2],
+                                   _ptr(amax_inout, "amax_inout", d["f32"]), _stream(stream))
+    _check("kv_amax_accumulate", st)
+
+
+def kv_scales_from_amax(amax, scale_out, stream=None):
+    """scale_out = max(fp32(amax / 448), FLT_MIN) for finite amax > 0, else 1.0."""
+    d = _dt()
+    if scale_out.numel() != amax.numel():
+        raise ValueError("amax / scale_out size mismatch")
+    st = load().kv_scales_from_amax(_ptr(amax, "amax", d["f32"]), amax.numel(),
+                                    _ptr(scale_out, "scale_out", d["f32"]), _stream(stream))
+    _check("kv_scales_from_amax", st)
+
+
+def kv_ingest_prefill(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, v_pool,
+                      max_seq_len, k_scale=None, v_scale=None, abort=None,
+                      cache_dtype=KV_CACHE_FP8_E4M3, page_size=PAGE_SIZE, stream=None):
+    """Write whole prompts (row_start[b] .. + seq_lens[b] of k_rows / v_rows) into their pages."""
+    d = _dt()
+    if k_rows.dim() != 3 or v_rows.shape != k_rows.shape:
+        raise ValueError("k_rows / v_rows must be [rows][num_kv_heads][head_dim]")
+    n_rows, hkv, hd = k_rows.shape
+    if k_pool.shape[:2] != v_pool.shape[:2] or k_pool.shape[1] != hkv:
+        raise ValueError("pools must be [num_pages][num_kv_heads][...]")
+    batch = seq_lens.numel()
+    if row_start.numel() != batch or block_table.shape[0] != batch:
+        raise ValueError("batch mismatch")
+    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
+    st = load().kv_ingest_prefill(
+        _ptr(k_rows, "k_rows", d["bf16"]), _ptr(v_rows, "v_rows", d["bf16"]), n_rows,
+        _ptr(row_start, "row_start", d["i32"]), _ptr(seq_lens, "seq_lens", d["i32"]), batch,
+        int(max_seq_len), _ptr(block_table, "block_table", d["i32"]), block_table.shape[1],
+        int(cache_dtype), _ptr(k_scale, "k_scale", d["f32"], allow_none=not fp8),
+        _ptr(v_scale, "v_scale", d["f32"], allow_none=not fp8),
+        _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
+        _ptr(v_pool, "v_pool", d["u8"] if fp8 else d["pool"]), k_pool.shape[0], hkv, hd,
+        page_size, _ptr(abort, "abort", d["u8"], allow_none=True), _stream(stream))
+    _check("kv_ingest_prefill", st)
+
+
+def ingest_layer(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, v_pool, max_seq_len,
+                 k_scale=None, v_scale=None, amax=None, abort=None,
+                 cache_dtype=KV_CACHE_FP8_E4M3, stream=None):
+    """Prefill handoff of one layer: for FP8, calibrate k_scale / v_scale
+    (fp32 [num_kv_heads], written) from the rows' amax, then write the prompts.
+    ``amax`` is an optional fp32 [2][num_kv_heads] scratch tensor (zeroed here)."""
+    if cache_dtype == KV_CACHE_FP8_E4M3:
+        import torch
+        hkv = k_rows.shape[1]
+        if amax is None:
+            amax = torch.zeros((2, hkv), dtype=torch.float32, device=k_rows.device)
+        else:
+            amax.zero_()
+        kv_amax_accumulate(k_rows, amax[0], stream=stream)
+        kv_amax_accumulate(v_rows, amax[1], stream=stream)
+        kv_scales_from_amax(amax[0], k_scale, stream=stream)
+        kv_scales_from_amax(amax[1], v_scale, stream=stream)
+    kv_ingest_prefill(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, v_pool,
+                      max_seq_len, k_scale, v_scale, abort=abort, cache_dtype=cache_dtype,
+                      stream=stream)

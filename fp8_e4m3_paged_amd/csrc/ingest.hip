@@ -1,0 +1,277 @@
+// Prefill ingest: the handoff of a prompt's BF16 keys and values into the
+// decode cache. The pages (remio.ai/it "Il serving di modelli più piccoli di
+// Cloudflare riduce la memoria, ma la sicurezza diventa la prova decisiva",
+// section "Cosa ha cambiato Cloudflare per Kimi e GLM") run prefill and
+// decode in separate pools: prefill builds a prompt's initial cache state in
+// BF16, decode reads the smaller FP8 cache. Three kernels serve that handoff:
+//
+//  * amax_kernel: per-KV-head max |x| over the finite bf16 values of a
+//    packed [rows][Hkv][128] tensor, accumulated into an fp32 array with one
+//    atomic max per 16-lane group (non-negative floats order like their bits);
+//  * scales_kernel: scale = fp32(amax / 448) (correctly rounded division),
+//    raised to the smallest normal fp32, 1.0 for amax = 0 or non-finite;
+//  * ingest_kernel<FP8>: whole (page, head) tiles of every prompt. Each lane
+//    builds exactly the 16-byte chunks that the tile layout places at
+//    16 * lane (+ 1 KiB per chunk), so every store is a full, coalesced
+//    16-byte write of the 2 KiB (FP8) or 4 KiB (BF16) tile; slots past the
+//    prompt's end are written as zeros.
+#include "kv_device.h"
+#include "kv_launch.h"
+
+namespace kvfp8 {
+
+// ---------------------------------------------------------------------------
+// amax
+// ---------------------------------------------------------------------------
+constexpr int kAmaxThreads = 256;
+
+__device__ __forceinline__ uint32_t finite_mag_max(uint32_t m, uint32_t w) {
+    const uint32_t lo = w & 0x7FFFu;
+    const uint32_t hi = (w >> 16) & 0x7FFFu;
+    m = lo < 0x7F80u ? max(m, lo) : m;     // exponent all ones: +-Inf or NaN, skipped
+    return hi < 0x7F80u ? max(m, hi) : m;
+}
+
+// Grid-stride over the 16-byte vectors of x; the stride is a multiple of
+// 16 * hkv, so vector v always belongs to head (v / 16) % hkv and each thread
+// keeps one running maximum (bf16 magnitude bits).
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const u32x4* __restrict__ x,
+                                                            int64_t n_vec, int32_t hkv,
+                                                            uint32_t* __restrict__ amax_bits) {
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kAmaxThreads + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kAmaxThreads;
+    const int g = static_cast<int>((first / 16) % hkv);
+    uint32_t m = 0;
+    int64_t v = first;
+    for (; v + 3 * stride < n_vec; v += 4 * stride) {
+        u32x4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = __builtin_nontemporal_load(x + v + u * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = finite_mag_max(m, w[u][e]);
+    }
+    for (; v < n_vec; v += stride) {
+        const u32x4 w = __builtin_nontemporal_load(x + v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = finite_mag_max(m, w[e]);
+    }
+    // the 16 lanes of a group cover one 256-byte head row segment: same head
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o)));
+    if ((threadIdx.x & 15) == 0 && m != 0) atomicMax(amax_bits + g, m << 16);
+}
+
+__global__ void scales_kernel(const float* __restrict__ amax, int32_t n, float* __restrict__ out) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+        const float a = amax[i];
+        float s = 1.0f;
+        if (a > 0.0f && a < INFINITY) s = fmaxf(a / 448.0f, 1.17549435082228750797e-38f);
+        out[i] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ingest
+// ---------------------------------------------------------------------------
+constexpr int kIngestWaves = 4;
+// One head's K rows, then its V rows, staged in LDS per wavefront (16 tokens
+// x 128 bf16), rows padded to 272 bytes so V's transposed reads (4 token
+// groups x 16 dims) hit disjoint banks and the 16-byte accesses stay aligned.
+// Global loads read whole rows, each byte once, and the next head's rows are
+// loaded into registers while the current head is encoded.
+constexpr int kVRowHalves = 136;
+
+// Orders one wavefront's LDS writes before its reads (and reads before the
+// next writes): LDS operations of a wave complete in order, so only the
+// compiler has to be kept from moving them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kIngestWaves * 64) void ingest_kernel(
+    const uint16_t* __restrict__ k_rows, const uint16_t* __restrict__ v_rows,
+    int64_t n_rows, const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_lens,
+    int32_t max_seq_len, int32_t max_pages, const int32_t* __restrict__ block_table,
+    int32_t bt_stride, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int32_t num_pages, int32_t hkv,
+    const uint8_t* __restrict__ abort) {
+    const int b = blockIdx.x / max_pages;
+    const int j = blockIdx.x % max_pages;
+    const int L = seq_lens[b];
+    if (abort != nullptr && abort[b] != 0) return;
+    if (L <= 0 || L > max_seq_len || (static_cast<int64_t>(L) + kPage - 1) / kPage > bt_stride)
+        return;
+    if (j * kPage >= L) return;
+    const int64_t r0 = row_start[b];
+    if (r0 < 0 || r0 + L > n_rows) return;                   // rows outside the inputs
+    const int page = block_table[static_cast<size_t>(b) * bt_stride + j];
+    if (page < 0 || page >= num_pages) return;
+    const int n = min(kPage, L - j * kPage);                  // live slots of this page
+    const size_t row0 = static_cast<size_t>(r0) + static_cast<size_t>(j) * kPage;
+    const size_t row_elems = static_cast<size_t>(hkv) * kDim;
+
+    const int wave = threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
+    const int m = lane % 16;          // K: token of the lane; V: dim within a 16-dim chunk
+    const int jg = lane / 16;         // K: 32-dim group; V: group of 4 tokens
+    constexpr int T = FP8 ? kTileFp8 : kTileBf16;
+    constexpr int NCH = T / 1024;     // 16-byte chunks per lane per tile
+    __shared__ uint16_t sx_all[kIngestWaves][kPage][kVRowHalves];
+    uint16_t (*sx)[kVRowHalves] = sx_all[wave];
+
+    const uint16_t* kbase = k_rows + row0 * row_elems;
+    const uint16_t* vbase = v_rows + row0 * row_elems;
+    // Rows of one head -> registers: each load instruction reads 4 whole
+    // 256-byte rows (each byte once); tokens past the prompt become zeros.
+    const auto load_head = [&](u32x4 (&kw)[4], u32x4 (&vw)[4], int g) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int piece = lane + 64 * k;
+            const int r = piece / 16, c = piece % 16;
+            const size_t off = static_cast<size_t>(r) * row_elems + static_cast<size_t>(g) * kDim + 8 * c;
+            kw[k] = r < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off))
+                          : u32x4{0u, 0u, 0u, 0u};
+            vw[k] = r < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off))
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    const auto stage = [&](const u32x4 (&w)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int piece = lane + 64 * k;
+            *reinterpret_cast<u32x4*>(&sx[piece / 16][8 * (piece % 16)]) = w[k];
+        }
+        wave_lds_sync();
+    };
+
+    u32x4 kw[4], vw[4];
+    load_head(kw, vw, wave);
+    for (int g = wave; g < hkv; g += kIngestWaves) {
+        const size_t tile = static_cast<size_t>(page) * hkv + g;
+        uint8_t* kt = k_pool + tile * T + 16 * lane;
+        uint8_t* vt = v_pool + tile * T + 16 * lane;
+        // the next head's rows are in flight while this one is encoded
+        u32x4 kn[4], vn[4];
+        const bool more = g + kIngestWaves < hkv;        // wave-uniform
+        if (more) load_head(kn, vn, g + kIngestWaves);
+        // ---- K: lane holds token m, dims 32 jg + (16 h | 8 h) ..
+        stage(kw);
+        if constexpr (FP8) {
+            const float ks = k_scale[g];
+#pragma unroll
+            for (int h = 0; h < NCH; ++h) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 16 * h]);
+                const u32x4 b2 = *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 16 * h + 8]);
+                const uint32_t w[8] = {a[0], a[1], a[2], a[3], b2[0], b2[1], b2[2], b2[3]};
+                uint32_t c[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = w[2 * e], hi = w[2 * e + 1];
+                    c[e] = encode4_e4m3(div_round_odd(bf16_bits_to_float(lo & 0xFFFF), ks),
+                                        div_round_odd(bf16_bits_to_float(lo >> 16), ks),
+                                        div_round_odd(bf16_bits_to_float(hi & 0xFFFF), ks),
+                                        div_round_odd(bf16_bits_to_float(hi >> 16), ks));
+                }
+                *reinterpret_cast<u32x4*>(kt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < NCH; ++h)
+                *reinterpret_cast<u32x4*>(kt + 1024 * h) =
+                    *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 8 * h]);
+        }
+        wave_lds_sync();                                 // K reads done before V overwrites
+        // ---- V: lane holds dim m of each 16-dim chunk, tokens 4 jg .. 4 jg + 3
+        stage(vw);
+        if constexpr (FP8) {
+            const float vs = v_scale[g];
+#pragma unroll
+            for (int h = 0; h < NCH; ++h) {
+                uint32_t c[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {               // dword e: dim 64 h + 16 e + m
+                    const int d = 64 * h + 16 * e + m;
+                    float y[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        y[r] = div_round_odd(bf16_bits_to_float(sx[4 * jg + r][d]), vs);
+                    c[e] = encode4_e4m3(y[0], y[1], y[2], y[3]);
+                }
+                *reinterpret_cast<u32x4*>(vt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < NCH; ++h) {
+                uint32_t c[4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {               // half e: dim 32 h + 16 e + m
+                    const int d = 32 * h + 16 * e + m;
+                    uint32_t hv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) hv[r] = sx[4 * jg + r][d];
+                    c[2 * e] = hv[0] | (hv[1] << 16);
+                    c[2 * e + 1] = hv[2] | (hv[3] << 16);
+                }
+                *reinterpret_cast<u32x4*>(vt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
+            }
+        }
+        wave_lds_sync();                                 // V reads done before the next head
+        if (more) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                kw[k] = kn[k];
+                vw[k] = vn[k];
+            }
+        }
+    }
+}
+
+hipError_t launch_amax(const uint16_t* x, int64_t n_rows, int32_t hkv, float* amax_inout,
+                       hipStream_t stream) {
+    const int64_t n_vec = n_rows * hkv * (kDim / 8);
+    if (n_vec == 0) return hipSuccess;
+    int64_t wgs = (n_vec + 4 * kAmaxThreads - 1) / (4 * kAmaxThreads);
+    wgs = wgs < 2048 ? wgs : 2048;
+    wgs = (wgs + hkv - 1) / hkv * hkv;            // stride a multiple of 16 * hkv
+    hipLaunchKernelGGL(amax_kernel, dim3(static_cast<uint32_t>(wgs)), dim3(kAmaxThreads), 0,
+                       stream, reinterpret_cast<const u32x4*>(x), n_vec, hkv,
+                       reinterpret_cast<uint32_t*>(amax_inout));
+    return hipGetLastError();
+}
+
+hipError_t launch_scales(const float* amax, int32_t n, float* out, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int wgs = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+    hipLaunchKernelGGL(scales_kernel, dim3(wgs), dim3(256), 0, stream, amax, n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_ingest(bool fp8, const uint16_t* k_rows, const uint16_t* v_rows,
+                         int64_t n_rows, const int32_t* row_start, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_seq_len, const int32_t* block_table, int32_t bt_stride,
+                         const float* k_scale, const float* v_scale, void* k_pool, void* v_pool,
+                         int32_t num_pages, int32_t num_kv_heads, const uint8_t* abort,
+                         hipStream_t stream) {
+    const int32_t max_pages = (max_seq_len + kPage - 1) / kPage;
+    if (batch == 0 || max_pages == 0) return hipSuccess;
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(batch) * max_pages));
+    if (fp8) {
+        hipLaunchKernelGGL(ingest_kernel<true>, grid, dim3(kIngestWaves * 64), 0, stream, k_rows,
+                           v_rows, n_rows, row_start, seq_lens, max_seq_len, max_pages, block_table,
+                           bt_stride, k_scale, v_scale, static_cast<uint8_t*>(k_pool),
+                           static_cast<uint8_t*>(v_pool), num_pages, num_kv_heads, abort);
+    } else {
+        hipLaunchKernelGGL(ingest_kernel<false>, grid, dim3(kIngestWaves * 64), 0, stream, k_rows,
+                           v_rows, n_rows, row_start, seq_lens, max_seq_len, max_pages, block_table,
+                           bt_stride, nullptr, nullptr, static_cast<uint8_t*>(k_pool),
+                           static_cast<uint8_t*>(v_pool), num_pages, num_kv_heads, abort);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvfp8

@@ -64,15 +64,18 @@ __device__ __forceinline__ float clamp448(float y) {
 // the exact quotient lies; truncating toward zero and forcing the last bit to
 // 1 when inexact gives round-to-odd, and a round-to-odd value with >= 4 + 2
 // significand bits rounds to E4M3 exactly as the exact quotient would.
+// Written with selects only (no early returns), so the encoder runs without
+// divergent branches; zero, infinite and NaN quotients and exact ones pass
+// through unchanged.
 __device__ __forceinline__ float div_round_odd(float x, float s) {
     const float y = x / s;                       // correctly rounded (IEEE) division
-    if (!(fabsf(y) < INFINITY) || y == 0.0f) return y;
-    const float r = fmaf(-y, s, x);
-    if (r == 0.0f) return y;                     // exact quotient
-    uint32_t u = __float_as_uint(y);
+    const float r = fmaf(-y, s, x);              // exact remainder (finite y)
+    const bool inexact = fabsf(y) < INFINITY && y != 0.0f && r != 0.0f;
     const bool toward_zero = ((r < 0.0f) != (s < 0.0f)) != (y < 0.0f);
-    if (toward_zero) u -= 1u;                    // |y| - 1 ulp: the truncated quotient
-    return __uint_as_float(u | 1u);
+    uint32_t u = __float_as_uint(y);
+    u -= (inexact && toward_zero) ? 1u : 0u;     // |y| - 1 ulp: the truncated quotient
+    u |= inexact ? 1u : 0u;
+    return __uint_as_float(u);
 }
 
 // Four floats (already x / s, round-to-odd) -> four e4m3 codes, little-endian.

@@ -47,4 +47,16 @@ struct AttnArgs {
 
 hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream);
 
+hipError_t launch_amax(const uint16_t* x, int64_t n_rows, int32_t hkv, float* amax_inout,
+                       hipStream_t stream);
+
+hipError_t launch_scales(const float* amax, int32_t n, float* out, hipStream_t stream);
+
+hipError_t launch_ingest(bool fp8, const uint16_t* k_rows, const uint16_t* v_rows,
+                         int64_t n_rows, const int32_t* row_start, const int32_t* seq_lens,
+                         int32_t batch, int32_t max_seq_len, const int32_t* block_table,
+                         int32_t bt_stride, const float* k_scale, const float* v_scale,
+                         void* k_pool, void* v_pool, int32_t num_pages, int32_t num_kv_heads,
+                         const uint8_t* abort, hipStream_t stream);
+
 }  // namespace kvfp8

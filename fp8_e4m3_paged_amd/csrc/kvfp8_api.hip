@@ -254,4 +254,51 @@ int paged_decode_attn_append(const void* q, const void* k_new, const void* v_new
                      partition_tokens, workspace, workspace_bytes, stream);
 }
 
+int kv_amax_accumulate(const void* x, int64_t n_rows, int32_t num_kv_heads, int32_t head_dim,
+                       float* amax_inout, void* stream) {
+    if (n_rows < 0 || num_kv_heads <= 0) return KV_ERR_SHAPE;
+    if (head_dim != KV_HEAD_DIM) return KV_ERR_UNSUPPORTED;
+    if (n_rows == 0) return KV_OK;
+    if (!x || !amax_inout) return KV_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(amax_inout, 4)) return KV_ERR_ALIGN;
+    return launch_status(kvfp8::launch_amax(static_cast<const uint16_t*>(x), n_rows, num_kv_heads,
+                                            amax_inout, static_cast<hipStream_t>(stream)));
+}
+
+int kv_scales_from_amax(const float* amax, int32_t n, float* scale_out, void* stream) {
+    if (n < 0) return KV_ERR_SHAPE;
+    if (n == 0) return KV_OK;
+    if (!amax || !scale_out) return KV_ERR_NULL;
+    if (misaligned(amax, 4) || misaligned(scale_out, 4)) return KV_ERR_ALIGN;
+    return launch_status(kvfp8::launch_scales(amax, n, scale_out, static_cast<hipStream_t>(stream)));
+}
+
+int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
+                      const int32_t* row_start, const int32_t* seq_lens, int32_t batch,
+                      int32_t max_seq_len, const int32_t* block_table, int32_t bt_stride,
+                      int32_t cache_dtype, const float* k_scale, const float* v_scale,
+                      void* k_pool, void* v_pool, int32_t num_pages, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, const uint8_t* abort, void* stream) {
+    if (n_rows < 0 || batch < 0 || max_seq_len < 0 || bt_stride < 0 || num_pages < 0 ||
+        num_kv_heads <= 0)
+        return KV_ERR_SHAPE;
+    if (head_dim != KV_HEAD_DIM || page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
+    if (cache_dtype != KV_CACHE_FP8_E4M3 && cache_dtype != KV_CACHE_BF16) return KV_ERR_UNSUPPORTED;
+    const int64_t max_pages = (static_cast<int64_t>(max_seq_len) + KV_PAGE_SIZE - 1) / KV_PAGE_SIZE;
+    if (max_pages * batch > 0x7FFFFFFFLL) return KV_ERR_SHAPE;
+    if (batch == 0 || max_seq_len == 0) return KV_OK;
+    const bool fp8 = cache_dtype == KV_CACHE_FP8_E4M3;
+    if (!row_start || !seq_lens || !block_table || !k_pool || !v_pool) return KV_ERR_NULL;
+    if (n_rows > 0 && (!k_rows || !v_rows)) return KV_ERR_NULL;
+    if (fp8 && (!k_scale || !v_scale)) return KV_ERR_NULL;
+    if (misaligned(k_rows, 16) || misaligned(v_rows, 16) || misaligned(k_pool, 16) ||
+        misaligned(v_pool, 16) || misaligned(row_start, 4) || misaligned(seq_lens, 4) ||
+        misaligned(block_table, 4) || (fp8 && (misaligned(k_scale, 4) || misaligned(v_scale, 4))))
+        return KV_ERR_ALIGN;
+    return launch_status(kvfp8::launch_ingest(
+        fp8, static_cast<const uint16_t*>(k_rows), static_cast<const uint16_t*>(v_rows), n_rows,
+        row_start, seq_lens, batch, max_seq_len, block_table, bt_stride, k_scale, v_scale, k_pool,
+        v_pool, num_pages, num_kv_heads, abort, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -260,6 +260,65 @@ int paged_decode_attn_append(const void* q, const void* k_new, const void* v_new
                              int32_t num_pages, int32_t partition_tokens, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * Prefill ingest: the handoff of a prompt's BF16 keys and values into the
+ * decode cache. The pages run prefill and decode in separate pools; prefill
+ * builds a prompt's initial cache state in BF16, decode reads the smaller
+ * FP8 cache (remio.ai/it, sections "Cosa ha cambiato Cloudflare per Kimi e
+ * GLM" and "Perché le cache più piccole di Cloudflare battono la velocità
+ * pura"). Calibration then ingest, per layer:
+ *     kv_amax_accumulate(k rows, ..., amax_k)   (amax_k starts at zeros;
+ *     kv_amax_accumulate(v rows, ..., amax_v)    call once per chunk of rows)
+ *     kv_scales_from_amax(amax_k, Hkv, k_scale); likewise for V
+ *     kv_ingest_prefill(...)
+ * The calibration rule (scale = amax / 448 per (layer, KV head)) is this
+ * library's reading; the pages state none.
+ */
+
+/*
+ * amax_inout[g] = max(amax_inout[g], max |x[r][g][d]|) over rows r < n_rows
+ * and d < head_dim, taking only finite values (NaN and +-Inf are skipped).
+ * x: bf16 [n_rows][num_kv_heads][head_dim], 16-byte aligned. amax_inout: fp32
+ * [num_kv_heads], finite and >= 0 on entry (zeros to start), updated with
+ * device atomics, so concurrent calls on one array are allowed. The result
+ * is exact (a maximum). Errors: KV_ERR_SHAPE, KV_ERR_UNSUPPORTED
+ * (head_dim != 128), KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ */
+int kv_amax_accumulate(const void* x, int64_t n_rows, int32_t num_kv_heads, int32_t head_dim,
+                       float* amax_inout, void* stream);
+
+/*
+ * scale_out[i] = max(fp32(amax[i] / 448), FLT_MIN) (correctly rounded
+ * division) for finite amax[i] > 0, else 1.0. Every scale is a positive
+ * normal fp32, as kv_append_quant / kv_ingest_prefill require.
+ * amax, scale_out: fp32 [n] (may alias). Errors: KV_ERR_SHAPE, KV_ERR_NULL,
+ * KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ */
+int kv_scales_from_amax(const float* amax, int32_t n, float* scale_out, void* stream);
+
+/*
+ * Write whole prompts into the pool, page by page. Token t of request b is
+ * row row_start[b] + t of k_rows / v_rows (bf16 [n_rows][num_kv_heads]
+ * [head_dim]). For every request b with abort[b] == 0 (or abort == NULL),
+ * 1 <= L = seq_lens[b] <= max_seq_len, ceil(L/16) <= bt_stride and
+ * 0 <= row_start[b], row_start[b] + L <= n_rows, and every page j < ceil(L/16)
+ * whose id p = block_table[b][j] is in [0, num_pages), and each KV head g:
+ *     tile (p, g) slot s = E4M3(x / scale[g]) of token 16 j + s  (FP8; BF16:
+ *                          the bits unchanged), for 16 j + s < L
+ *     tile (p, g) slot s = 0 (code or bits) for 16 j + s >= L
+ * i.e. the same codes kv_append_quant writes for those tokens, in whole tiles
+ * with full 16-byte stores. Other requests and pages are not touched.
+ * k_scale, v_scale: fp32 [num_kv_heads], positive normal (FP8; ignored and
+ * may be NULL for BF16). cache_dtype selects the pool format. Errors:
+ * KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ */
+int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
+                      const int32_t* row_start, const int32_t* seq_lens, int32_t batch,
+                      int32_t max_seq_len, const int32_t* block_table, int32_t bt_stride,
+                      int32_t cache_dtype, const float* k_scale, const float* v_scale,
+                      void* k_pool, void* v_pool, int32_t num_pages, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, const uint8_t* abort, void* stream);
+
 /* Human-readable name of a kv_status value (static string, never NULL). */
 const char* kv_status_str(int status);
 

@@ -24,9 +24,11 @@ taken here (each listed with its reason in the design notes) are:
 * ingest writes the pages j < ceil(L / P) of every request that is not
   aborted, whole: slot t < L of page j holds token 16 j + slot's codes and the
   slots past L in the last page are set to code 0 (BF16: bits 0); a page id
-  outside the pool is skipped; a request with L <= 0, or with more pages than
-  its table row holds, writes nothing. Token t of request b is row
-  row_start[b] + t of the packed bf16 inputs [rows][num_kv_heads][head_dim].
+  outside the pool is skipped; a request with L <= 0, with more pages than its
+  table row holds, longer than the call's max_seq_len, or whose rows are not
+  all inside the inputs writes nothing.
+  Token t of request b is row row_start[b] + t of the packed bf16 inputs
+  [rows][num_kv_heads][head_dim].
 """
 
 from __future__ import annotations
@@ -63,7 +65,7 @@ def scales_from_amax(amax) -> np.ndarray:
 
 
 def ingest(k_pool, v_pool, k_rows, v_rows, row_start, seq_lens, block_table, cache,
-           k_scale=None, v_scale=None, abort=None):
+           k_scale=None, v_scale=None, abort=None, max_seq_len=None):
     """Write whole prompts into the logical pools (in place); returns them.
 
     k_pool, v_pool: [num_pages][num_kv_heads][P][head_dim], uint8 codes (FP8)
@@ -75,6 +77,8 @@ def ingest(k_pool, v_pool, k_rows, v_rows, row_start, seq_lens, block_table, cac
                                  for P j + slot < L
         pool[page][g][slot][:] = 0 for the slots past L
     where the code is ENC(x / s_g) (FP8) or the bf16 bits unchanged (BF16).
+    A request longer than max_seq_len (when given), or whose rows are not all
+    inside the inputs, writes nothing.
     """
     block_table = np.asarray(block_table)
     num_pages, hkv, P, D = k_pool.shape
@@ -82,6 +86,10 @@ def ingest(k_pool, v_pool, k_rows, v_rows, row_start, seq_lens, block_table, cac
     for b in range(batch):
         L = int(seq_lens[b])
         if (abort is not None and abort[b]) or L <= 0 or -(-L // P) > stride:
+            continue
+        if max_seq_len is not None and L > max_seq_len:
+            continue
+        if int(row_start[b]) < 0 or int(row_start[b]) + L > k_rows.shape[0]:
             continue
         for j in range(-(-L // P)):
             page = int(block_table[b, j])

@@ -85,6 +85,19 @@ def _token_chunks(wl: Workload, chunk_tokens: int, device):
                torch.from_numpy(pos[i:i + chunk_tokens]).to(device))
 
 
+def prompt_rows(wl: Workload, layer: int, kind: str, device="cuda", chunk_tokens: int = 65536):
+    """Every request's initial tokens packed request by request: bf16 bits
+    (int16) [sum L0][Hkv][D] and the int32 row where each request starts."""
+    keys = _keys(wl, layer, kind, device)
+    parts = [kv_bits_tokens(wl, layer, kind, seq, pos, keys)
+             for seq, pos in _token_chunks(wl, chunk_tokens, device)]
+    rows = (torch.cat(parts) if parts else
+            torch.zeros((0, wl.num_kv_heads, wl.head_dim), dtype=torch.int16, device=device))
+    lens = wl.seq_lens0.astype(np.int64)
+    start = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    return rows, torch.from_numpy(start).to(device)
+
+
 def device_amax(wl: Workload, layer: int, chunk_tokens: int = 32768, device="cuda"):
     """Per-KV-head amax of |K| and |V| over the initial pool (exact: max of bf16)."""
     out = []

@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["kv_verify_tags", "kv_append_quant", "kv_append_bf16", "paged_decode_attn",
               "paged_decode_attn_workspace_bytes", "paged_decode_attn_partition_tokens",
-              "paged_decode_attn_append", "kv_status_str"]:
+              "paged_decode_attn_append", "kv_amax_accumulate", "kv_scales_from_amax",
+              "kv_ingest_prefill", "kv_status_str"]:
         assert n in names
 
 
@@ -154,6 +155,39 @@ def test_fused_append_attention_rejects_bad_arguments(lib):
     assert attn_append(lib, sm_scale=-1.0) == UNSUP
     assert attn_append(lib, workspace=None, partition_tokens=512) == WORKSPACE
     assert attn_append(lib, batch=0, k_new=None, v_new=None, q=None) == OK
+
+
+def ingest_call(lib, **kw):
+    args = dict(k_rows=A, v_rows=A, n_rows=1000, row_start=A, seq_lens=A, batch=4,
+                max_seq_len=300, block_table=A, bt_stride=32, cache_dtype=0, k_scale=A,
+                v_scale=A, k_pool=A, v_pool=A, num_pages=100, num_kv_heads=8, head_dim=128,
+                page_size=16, abort=None, stream=None)
+    args.update(kw)
+    return lib.kv_ingest_prefill(*args.values())
+
+
+def test_ingest_entry_points_reject_bad_arguments(lib):
+    assert lib.kv_amax_accumulate(A, 10, 8, 64, A, None) == UNSUP
+    assert lib.kv_amax_accumulate(A, -1, 8, 128, A, None) == SHAPE
+    assert lib.kv_amax_accumulate(A, 10, 0, 128, A, None) == SHAPE
+    assert lib.kv_amax_accumulate(None, 10, 8, 128, A, None) == NULL
+    assert lib.kv_amax_accumulate(A + 8, 10, 8, 128, A, None) == ALIGN
+    assert lib.kv_amax_accumulate(None, 0, 8, 128, None, None) == OK      # nothing to do
+    assert lib.kv_scales_from_amax(A, -1, A, None) == SHAPE
+    assert lib.kv_scales_from_amax(None, 4, A, None) == NULL
+    assert lib.kv_scales_from_amax(A, 4, A + 2, None) == ALIGN
+    assert lib.kv_scales_from_amax(None, 0, None, None) == OK
+    assert ingest_call(lib, head_dim=64) == UNSUP
+    assert ingest_call(lib, page_size=32) == UNSUP
+    assert ingest_call(lib, cache_dtype=3) == UNSUP
+    assert ingest_call(lib, n_rows=-1) == SHAPE
+    assert ingest_call(lib, batch=1 << 20, max_seq_len=1 << 30) == SHAPE   # grid too large
+    assert ingest_call(lib, k_scale=None) == NULL                          # FP8 needs scales
+    # BF16 takes no scales: NULL passes the pointer checks (stopped here by the alignment one)
+    assert ingest_call(lib, cache_dtype=1, k_scale=None, v_scale=None, v_pool=A + 4) == ALIGN
+    assert ingest_call(lib, row_start=None) == NULL
+    assert ingest_call(lib, k_pool=A + 4) == ALIGN
+    assert ingest_call(lib, batch=0, k_rows=None) == OK
 
 
 def test_workspace_and_partition_sizing(lib):

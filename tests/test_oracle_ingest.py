@@ -173,6 +173,19 @@ def test_ingest_skips_aborted_bad_pages_and_overlong():
     for j in (0, 2):
         assert not np.array_equal(got_k[bt[0, j]], kp[bt[0, j]])
     assert np.array_equal(got_k[bad_page], kp[bad_page])
+    # a length limit refuses the longer requests whole
+    lim_k, lim_v = kp.copy(), vp.copy()
+    ingest.ingest(lim_k, lim_v, kr, vr, starts, np.array([40, 20, 9]), bt, "fp8", ks, vs,
+                  max_seq_len=20)
+    assert np.array_equal(lim_k[bt[0, 0]], kp[bt[0, 0]])             # 40 > 20: untouched
+    assert not np.array_equal(lim_k[bt[1, 0]], kp[bt[1, 0]])         # 20 <= 20: written
+    # rows past the end of the inputs refuse the request whole
+    oob_k, oob_v = kp.copy(), vp.copy()
+    starts2 = starts.copy()
+    starts2[1] = kr.shape[0] - 19                              # needs 20 rows
+    ingest.ingest(oob_k, oob_v, kr, vr, starts2, np.array([40, 20, 9]), bt, "fp8", ks, vs)
+    assert np.array_equal(oob_k[bt[1, 0]], kp[bt[1, 0]])
+    assert not np.array_equal(oob_k[bt[2, 0]], kp[bt[2, 0]])
     # request 1 (aborted) and request 2 (needs 4 pages, its row holds 3) untouched
     for b in (1, 2):
         for j in range(bt.shape[1]):
