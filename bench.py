@@ -74,9 +74,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--quiet", action="store_true")
-    ap.add_argument("--mode", default="step", choices=["step", "copy", "ingest"],
+    ap.add_argument("--mode", default="step", choices=["step", "copy", "ingest", "sweep"],
                     help="copy: time a plain device copy of --copy-mib MiB (counter "
-                         "calibration); ingest: the prefill handoff of one layer's prompts")
+                         "calibration); ingest: the prefill handoff of one layer's prompts; "
+                         "sweep: BF16 vs FP8 decode at 1..64 requests under one pool budget")
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
 
@@ -312,17 +313,113 @@ def ingest_bench(args):
     print(json.dumps(res), flush=True)
 
 
+SWEEP_BATCHES = (1, 8, 16, 32, 64)
+
+
+def sweep_bench(args):
+    """BF16 vs FP8 cache at 1, 8, 16, 32 and 64 concurrent requests (the
+    headline's length draw, 8 layers), under one pool-memory budget: 1.01 x
+    the BF16 pools of 32 requests (room for the timed steps included), so
+    BF16 runs out above 32 while FP8 reaches 64. Each point that fits runs the
+    decode step (tag check, fused append + attention per layer) for --steps
+    steps after --warmup; a point that does not fit is reported as such."""
+    import numpy as np
+    import torch
+
+    import fp8_e4m3_paged_amd as kv
+    import synth
+    from synth import device as sd
+
+    kv.load()
+    dev = "cuda"
+    total_steps = args.warmup + args.steps
+
+    def pool_bytes(wl, cache):
+        tile = wl.page_size * wl.head_dim * (1 if cache == "fp8" else 2)
+        return wl.num_pages * wl.num_kv_heads * 2 * tile * wl.num_layers
+
+    ref = synth.concurrency_point(32, max_steps=total_steps)
+    budget = int(1.01 * pool_bytes(ref, "bf16"))
+    points = []
+    for cache in ("bf16", "fp8"):
+        for B in SWEEP_BATCHES:
+            wl = synth.concurrency_point(B, max_steps=total_steps)
+            need = pool_bytes(wl, cache)
+            pt = {"cache": cache, "batch": B, "pool_GB": round(need / 1e9, 3)}
+            if need > budget:
+                pt["fits"] = False
+                points.append(pt)
+                log(args, f"{cache} B={B}: pools need {need / 1e9:.2f} GB > budget")
+                continue
+            st = sd.DeviceState(wl, kv, cache=cache, device=dev)
+            seq_lens = [st.seq_lens(i).contiguous() for i in range(total_steps)]
+            inputs = [[(sd.q_bits_device(wl, l, i, dev), sd.new_token_bits_device(wl, l, "k", i, dev),
+                        sd.new_token_bits_device(wl, l, "v", i, dev))
+                       for l in range(wl.num_layers)] for i in range(total_steps)]
+            outs = [torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+                    for _ in range(wl.num_layers)]
+            n = kv.paged_decode_attn_workspace_bytes(B, wl.num_q_heads, wl.num_kv_heads,
+                                                     wl.max_seq_len, 0)
+            ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+            cd = kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16
+            sm = 1.0 / math.sqrt(wl.head_dim)
+
+            def step(i):
+                kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens[i],
+                                  st.abort)
+                for l in range(wl.num_layers):
+                    q, kn, vn = inputs[i][l]
+                    kv.paged_decode_attn_append(q, kn, vn, st.k_pool[l], st.v_pool[l],
+                                                st.k_scale[l], st.v_scale[l], st.block_table,
+                                                seq_lens[i], wl.max_seq_len, outs[l], sm,
+                                                workspace=ws, abort=st.abort, cache_dtype=cd)
+
+            for i in range(args.warmup):
+                step(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(args.steps):
+                step(args.warmup + i)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.steps
+            byts = sum(step_bytes(wl, wl.seq_lens_at(args.warmup + i), cache, True)["total"]
+                       for i in range(args.steps)) / args.steps
+            pt.update(fits=True, ms_per_step=round(ms, 4),
+                      seq_steps_per_s=round(B / ms * 1e3, 1), GBps=round(byts / ms / 1e6, 1))
+            points.append(pt)
+            log(args, f"{cache} B={B}: {ms:.3f} ms/step, {B / ms * 1e3:.0f} seq-steps/s, "
+                      f"{byts / ms / 1e6:.0f} GB/s")
+            del st, inputs, outs, ws
+            torch.cuda.empty_cache()
+    best = {c: max((p["seq_steps_per_s"] for p in points if p["cache"] == c and p["fits"]),
+                   default=None) for c in ("bf16", "fp8")}
+    res = {
+        "metric": "decode seq-steps/s, BF16 vs FP8 cache, 1..64 requests under one pool budget",
+        "mode": "sweep", "value": best["fp8"], "unit": "seq-steps/s", "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "e4m3 / bf16", "data": "synthetic",
+        "config": {"workload": "headline length draw (8192 + U[0,1000]), first B requests, "
+                               "8 layers, 64 q / 8 KV heads, tag check on, fused append",
+                   "pool_budget_GB": round(budget / 1e9, 3)},
+        "best": best,
+        "fp8_over_best_bf16": round(best["fp8"] / best["bf16"], 3) if best["bf16"] else None,
+        "points": points,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.mode == "copy":
         copy_calibration(args)
         return
-    if args.mode == "ingest":
+    if args.mode in ("ingest", "sweep"):
         if args.gpus != 1:
             print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
                   file=sys.stderr)
             sys.exit(2)
-        ingest_bench(args)
+        (ingest_bench if args.mode == "ingest" else sweep_bench)(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

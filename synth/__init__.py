@@ -340,6 +340,18 @@ def c4_headline(max_steps: int = 1) -> Workload:
                   q_sigma=1.0, garbage_tail=False, rng=rng)
 
 
+def concurrency_point(batch: int, max_steps: int = 1) -> Workload:
+    """The first ``batch`` requests of the headline batch's length draw
+    (8192 + uniform [0, 1000]), GQA 64/8, 8 layers: one point of the BF16 vs
+    FP8 concurrency sweep."""
+    rng = _rng(3)
+    L = (8192 + rng.integers(0, 1000, size=64, endpoint=True))[:batch]
+    return _build(f"concurrency_b{batch}", 5, batch=batch, layers=8, hq=64, hkv=8, d=128,
+                  page=16, seq_lens0=L - 1, max_steps=max_steps,
+                  pool_pages=lambda total: total + batch, k_sigma=1.0, v_sigma=0.5,
+                  q_sigma=1.0, garbage_tail=False, rng=np.random.default_rng(1005 + batch))
+
+
 def c5_skewed(max_steps: int = 2) -> Workload:
     """16 sequences, ctx log-uniform in [512, 131072] (two at 131072), 1 layer.
 
