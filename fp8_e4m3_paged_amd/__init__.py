@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
 plus ``decode_step``, which enqueues one decode step (tag check, then per
 layer append and attention) in the order the operations require, and
 ``ingest_layer``, which calibrates one layer's scales and writes its prompts.
+``PagePool`` wraps the host page pool and tag tracker of include/kvpool.h
+(kv_pool_create, kv_pool_alloc, kv_pool_free, kv_pool_tags,
+kv_pool_record_check, kv_pool_get_stats, kv_pool_destroy).
 """
 
 from __future__ import annotations
@@ -28,7 +31,11 @@ __all__ = [
     "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_workspace_bytes",
     "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
     "kv_amax_accumulate", "kv_scales_from_amax", "kv_ingest_prefill", "ingest_layer",
+    "PagePool", "KV_ERR_EXHAUSTED", "KV_ERR_STATE",
 ]
+
+KV_ERR_EXHAUSTED = -7
+KV_ERR_STATE = -8
 
 KV_CACHE_FP8_E4M3 = 0
 KV_CACHE_BF16 = 1
@@ -74,6 +81,13 @@ _SIGS = {
                                                 _P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _I,
                                                 _I, _P, ctypes.c_size_t, _P]),
     "kv_amax_accumulate": (ctypes.c_int, [_P, _L, _I, _I, _P, _P]),
+    "kv_pool_create": (ctypes.c_int, [_I, _I, ctypes.c_uint32, ctypes.POINTER(_P)]),
+    "kv_pool_destroy": (None, [_P]),
+    "kv_pool_alloc": (ctypes.c_int, [_P, _I, _P, _P]),
+    "kv_pool_free": (ctypes.c_int, [_P, _P, _I]),
+    "kv_pool_tags": (ctypes.c_int, [_P, _P]),
+    "kv_pool_record_check": (ctypes.c_int, [_P, _P, _I]),
+    "kv_pool_get_stats": (ctypes.c_int, [_P, _P]),
     "kv_scales_from_amax": (ctypes.c_int, [_P, _I, _P, _P]),
     "kv_ingest_prefill": (ctypes.c_int, [_P, _P, _L, _P, _P, _I, _I, _P, _I, _I, _P, _P, _P, _P,
                                          _I, _I, _I, _I, _P, _P]),
@@ -387,3 +401,71 @@ def ingest_layer(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, v_poo
     kv_ingest_prefill(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, v_pool,
                       max_seq_len, k_scale, v_scale, abort=abort, cache_dtype=cache_dtype,
                       stream=stream)
+
+
+class _PoolStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "num_pages", "free_pages", "pages_allocated", "pages_freed", "checks",
+        "requests_checked", "requests_aborted")]
+
+
+class PagePool:
+    """Host page pool and tag tracker (include/kvpool.h). ``tracked=False`` is
+    the no-op tracker: tags stay 0 and recorded checks count nothing.
+
+    Arrays are numpy (host memory); ``tags()`` returns the uint32 tag of every
+    page, ready to be copied into the device pool_tags that kv_verify_tags reads.
+    """
+
+    def __init__(self, num_pages: int, tracked: bool = True, seed: int = 0):
+        self._lib = load()
+        h = _P()
+        _check("kv_pool_create", self._lib.kv_pool_create(int(num_pages), int(bool(tracked)),
+                                                          int(seed) & 0xFFFFFFFF, ctypes.byref(h)))
+        self._h = h
+        self.num_pages = int(num_pages)
+        self.tracked = bool(tracked)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.kv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def alloc(self, n: int):
+        """n free pages (LIFO) -> (page ids int32[n], their tags uint32[n])."""
+        import numpy as np
+        pages = np.empty(max(int(n), 0), np.int32)      # n < 0 is refused by the library
+        tags = np.empty(max(int(n), 0), np.uint32)
+        _check("kv_pool_alloc", self._lib.kv_pool_alloc(self._h, int(n), pages.ctypes.data,
+                                                        tags.ctypes.data))
+        return pages, tags
+
+    def free(self, pages):
+        """Return pages to the pool; each one's tag is bumped (tracked pools)."""
+        import numpy as np
+        p = np.ascontiguousarray(pages, dtype=np.int32)
+        _check("kv_pool_free", self._lib.kv_pool_free(self._h, p.ctypes.data, p.size))
+
+    def tags(self):
+        import numpy as np
+        t = np.empty(self.num_pages, np.uint32)
+        _check("kv_pool_tags", self._lib.kv_pool_tags(self._h, t.ctypes.data))
+        return t
+
+    def record_check(self, abort):
+        """Count one tag check's outcome (abort flags on the host)."""
+        import numpy as np
+        a = np.ascontiguousarray(abort, dtype=np.uint8)
+        _check("kv_pool_record_check", self._lib.kv_pool_record_check(self._h, a.ctypes.data,
+                                                                      a.size))
+
+    def stats(self) -> dict:
+        st = _PoolStats()
+        _check("kv_pool_get_stats", self._lib.kv_pool_get_stats(self._h, ctypes.byref(st)))
+        d = {n: getattr(st, n) for n, _ in _PoolStats._fields_}
+        d["mismatch_rate"] = (d["requests_aborted"] / d["requests_checked"]
+                              if d["requests_checked"] else 0.0)
+        return d

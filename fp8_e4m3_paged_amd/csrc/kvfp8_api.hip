@@ -142,6 +142,8 @@ const char* kv_status_str(int status) {
         case KV_ERR_WORKSPACE: return "KV_ERR_WORKSPACE: workspace missing or too small";
         case KV_ERR_LAUNCH: return "KV_ERR_LAUNCH: HIP reported an error when enqueueing";
         case KV_ERR_ALIGN: return "KV_ERR_ALIGN: a pointer is not aligned as required";
+        case KV_ERR_EXHAUSTED: return "KV_ERR_EXHAUSTED: not enough free pages in the pool";
+        case KV_ERR_STATE: return "KV_ERR_STATE: page not allocated (double free or bad id)";
         default: return "unknown kv_status";
     }
 }

@@ -98,7 +98,9 @@ typedef enum {
     KV_ERR_UNSUPPORTED = -3, /* head_dim/page_size/group size/partition not handled */
     KV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required             */
     KV_ERR_LAUNCH = -5,      /* HIP reported an error when enqueueing               */
-    KV_ERR_ALIGN = -6        /* a pointer is not aligned as required                */
+    KV_ERR_ALIGN = -6,       /* a pointer is not aligned as required                */
+    KV_ERR_EXHAUSTED = -7,   /* page pool: fewer free pages than requested          */
+    KV_ERR_STATE = -8        /* page pool: freeing a page that is not allocated     */
 } kv_status;
 
 typedef enum { KV_CACHE_FP8_E4M3 = 0, KV_CACHE_BF16 = 1 } kv_cache_dtype;

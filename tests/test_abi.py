@@ -16,14 +16,15 @@ from synth import device as sd
 from tests.helpers import OFFSETS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvfp8.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 LIB = os.path.join(ROOT, "fp8_e4m3_paged_amd", "libkvfp8.so")
 
 OK, NULL, SHAPE, UNSUP, WORKSPACE, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
 
@@ -41,7 +42,9 @@ def test_header_declares_the_entry_points():
     for n in ["kv_verify_tags", "kv_append_quant", "kv_append_bf16", "paged_decode_attn",
               "paged_decode_attn_workspace_bytes", "paged_decode_attn_partition_tokens",
               "paged_decode_attn_append", "kv_amax_accumulate", "kv_scales_from_amax",
-              "kv_ingest_prefill", "kv_status_str"]:
+              "kv_ingest_prefill", "kv_status_str", "kv_pool_create", "kv_pool_destroy",
+              "kv_pool_alloc", "kv_pool_free", "kv_pool_tags", "kv_pool_record_check",
+              "kv_pool_get_stats"]:
         assert n in names
 
 
@@ -53,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import fp8_e4m3_paged_amd as k
-    for s in (OK, NULL, SHAPE, UNSUP, WORKSPACE, LAUNCH, ALIGN):
+    for s in (OK, NULL, SHAPE, UNSUP, WORKSPACE, LAUNCH, ALIGN, -7, -8):
         assert k.kv_status_str(s).startswith("KV_")
     assert "unknown" in k.kv_status_str(42)
 
