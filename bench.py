@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # for the kernel sources they were taken on (sha256 prefix of decode_attn.hip
 # + kv_device.h). See profiles/attn_partition_kernel_c4_hbm_counters.md.
 COUNTER_TRAFFIC = {
-    "source_sha": "2874c5eee2c00aef",
+    "source_sha": "c72d71fc1d40911a",
     "workload": "c4_headline",
     "read_bytes": 1.144e9,
     "write_bytes": 2.490e6,
