@@ -16,10 +16,12 @@ computes, in float64 numpy:
   attention over the pages with dequantize-on-read and a plain softmax.
 * ``ingest`` -- the prefill handoff into the decode cache: per-KV-head amax
   and scale calibration, and the page-by-page write of whole prompts.
+* ``weights`` -- weight-only quantized decode GEMV: INT4 and FP8 e4m3
+  weights with per-(row, 128-input group) scales, and the float64 product.
 
 The pages this follows are the five web reports of Cloudflare's FP8 KV-cache /
 page-tag post (remio.ai it/pt/ko, iitog.ru, manulx.blog). Each function names
 the page and section it follows.
 """
 
-from . import e4m3, ingest, paged  # noqa: F401
+from . import e4m3, ingest, paged, weights  # noqa: F401
