@@ -74,10 +74,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--quiet", action="store_true")
-    ap.add_argument("--mode", default="step", choices=["step", "copy", "ingest", "sweep"],
+    ap.add_argument("--mode", default="step", choices=["step", "copy", "ingest", "sweep", "gemv"],
                     help="copy: time a plain device copy of --copy-mib MiB (counter "
                          "calibration); ingest: the prefill handoff of one layer's prompts; "
-                         "sweep: BF16 vs FP8 decode at 1..64 requests under one pool budget")
+                         "sweep: BF16 vs FP8 decode at 1..64 requests under one pool budget; "
+                         "gemv: INT4 vs FP8 weight-only decode GEMV at 1..64 tokens")
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
 
@@ -409,17 +410,94 @@ def sweep_bench(args):
     print(json.dumps(res), flush=True)
 
 
+# One decode layer's dense weight stream: (rows n, inputs k) of the attention
+# output projection, the fused gate + up projection and the down projection
+# of a hidden-8192, FFN-14336 transformer layer.
+GEMV_LAYER = ((8192, 8192), (28672, 8192), (8192, 14336))
+
+
+def gemv_bench(args):
+    """INT4 vs FP8 e4m3 weight-only decode GEMV (wq_gemv) over one layer's
+    weight stream at 1, 8, 16, 32 and 64 tokens: time per layer, tokens/s,
+    and HBM GB/s of the algorithmic bytes (codes, scales, activations, y)."""
+    import numpy as np
+    import torch
+
+    import fp8_e4m3_paged_amd as kv
+
+    kv.load()
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    mats = {}
+    for fmt in (kv.WQ_INT4, kv.WQ_FP8_E4M3):
+        mats[fmt] = []
+        for n, k in GEMV_LAYER:
+            w = (torch.randn((n, k), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            packed = torch.empty(kv.wq_packed_bytes(n, k, fmt), dtype=torch.uint8, device=dev)
+            scales = torch.empty(n * (k // 128), dtype=torch.float32, device=dev)
+            kv.wq_quantize_pack(w, packed, scales, fmt)
+            mats[fmt].append((n, k, packed, scales))
+            del w
+    torch.cuda.synchronize()
+    points, largest = [], None
+    for fmt, name in ((kv.WQ_FP8_E4M3, "fp8"), (kv.WQ_INT4, "int4")):
+        for M in (1, 8, 16, 32, 64):
+            xs = [(torch.randn((M, k), generator=gen, device=dev)).to(torch.bfloat16)
+                  for _, k in GEMV_LAYER]
+            ys = [torch.zeros((M, n), dtype=torch.float32, device=dev) for n, _ in GEMV_LAYER]
+
+            def layer():
+                for (n, k, packed, scales), x, y in zip(mats[fmt], xs, ys):
+                    kv.wq_gemv(x, packed, scales, y, n, fmt)
+
+            for _ in range(max(1, args.warmup)):
+                layer()
+            torch.cuda.synchronize()
+            ms = _events_ms(layer, max(1, args.steps))
+            byts = sum(p.numel() + s.numel() * 4 + M * k * 2 + 2 * M * n * 4
+                       for (n, k, p, s) in mats[fmt])
+            points.append({"weights": name, "tokens": M, "us_per_layer": round(ms * 1e3, 2),
+                           "tokens_per_s": round(M / ms * 1e3, 1),
+                           "GBps": round(byts / ms / 1e6, 1)})
+            log(args, f"{name} M={M}: {ms * 1e3:.1f} us/layer, {byts / ms / 1e6:.0f} GB/s")
+            if name == "int4" and M == 1:
+                n, k, p, s = mats[fmt][1]                 # the largest matrix alone
+                x1, y1 = xs[1], ys[1]
+                t1 = _events_ms(lambda: kv.wq_gemv(x1, p, s, y1, n, fmt), max(1, args.steps))
+                b1 = p.numel() + s.numel() * 4 + k * 2 + 2 * n * 4
+                largest = {"bound": "hbm", "kernel": f"wq_gemv_kernel<INT4> {n}x{k}, 1 token",
+                           "achieved": round(b1 / t1 / 1e6, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(b1 / t1 / 1e6 / HBM_PEAK_GBS, 4),
+                           "traffic": None, "avg_launch_us": round(t1 * 1e3, 2),
+                           "algorithmic_bytes_per_launch": b1}
+    sp = {M: round(next(p["tokens_per_s"] for p in points if p["weights"] == "int4" and p["tokens"] == M)
+                   / next(p["tokens_per_s"] for p in points if p["weights"] == "fp8" and p["tokens"] == M), 3)
+          for M in (1, 8, 16, 32, 64)}
+    res = {
+        "metric": "weight-only decode GEMV over one layer's weights: tokens/s, INT4 vs FP8",
+        "mode": "gemv", "value": next(p["tokens_per_s"] for p in points
+                                      if p["weights"] == "int4" and p["tokens"] == 1),
+        "unit": "tokens/s", "higher_is_better": True, "dtype": "int4 / e4m3 weights, bf16 x",
+        "data": "synthetic", "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": "one layer: " + ", ".join(f"{n}x{k}" for n, k in GEMV_LAYER),
+                   "group": 128},
+        "roofline": largest, "int4_over_fp8": sp, "points": points,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.mode == "copy":
         copy_calibration(args)
         return
-    if args.mode in ("ingest", "sweep"):
+    if args.mode in ("ingest", "sweep", "gemv"):
         if args.gpus != 1:
             print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported",
                   file=sys.stderr)
             sys.exit(2)
-        (ingest_bench if args.mode == "ingest" else sweep_bench)(args)
+        {"ingest": ingest_bench, "sweep": sweep_bench, "gemv": gemv_bench}[args.mode](args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

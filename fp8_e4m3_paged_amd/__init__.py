@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
     paged_decode_attn_append, paged_decode_attn_workspace_bytes,
     paged_decode_attn_partition_tokens, kv_amax_accumulate,
     kv_scales_from_amax, kv_ingest_prefill, kv_status_str
+and the weight-only quantized decode GEMV: wq_packed_bytes, wq_quantize_pack,
+wq_gemv;
 plus ``decode_step``, which enqueues one decode step (tag check, then per
 layer append and attention) in the order the operations require, and
 ``ingest_layer``, which calibrates one layer's scales and writes its prompts.
@@ -32,7 +34,11 @@ __all__ = [
     "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
     "kv_amax_accumulate", "kv_scales_from_amax", "kv_ingest_prefill", "ingest_layer",
     "PagePool", "KV_ERR_EXHAUSTED", "KV_ERR_STATE",
+    "WQ_INT4", "WQ_FP8_E4M3", "wq_packed_bytes", "wq_quantize_pack", "wq_gemv",
 ]
+
+WQ_INT4 = 0
+WQ_FP8_E4M3 = 1
 
 KV_ERR_EXHAUSTED = -7
 KV_ERR_STATE = -8
@@ -81,6 +87,9 @@ _SIGS = {
                                                 _P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _I,
                                                 _I, _P, ctypes.c_size_t, _P]),
     "kv_amax_accumulate": (ctypes.c_int, [_P, _L, _I, _I, _P, _P]),
+    "wq_packed_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "wq_quantize_pack": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
+    "wq_gemv": (ctypes.c_int, [_P, _I, _P, _P, _I, _I, _I, _P, _P]),
     "kv_pool_create": (ctypes.c_int, [_I, _I, ctypes.c_uint32, ctypes.POINTER(_P)]),
     "kv_pool_destroy": (None, [_P]),
     "kv_pool_alloc": (ctypes.c_int, [_P, _I, _P, _P]),
@@ -469,3 +478,35 @@ class PagePool:
         d["mismatch_rate"] = (d["requests_aborted"] / d["requests_checked"]
                               if d["requests_checked"] else 0.0)
         return d
+
+
+def wq_packed_bytes(n, k, fmt=WQ_INT4):
+    return int(load().wq_packed_bytes(int(n), int(k), int(fmt)))
+
+
+def wq_quantize_pack(w, packed, scales, fmt=WQ_INT4, stream=None):
+    """Quantize bf16 weights w [n][k] into packed codes (uint8, wq_packed_bytes)
+    and fp32 scales [n / 16][k / 128][16] (layouts in include/kvfp8.h)."""
+    d = _dt()
+    if w.dim() != 2:
+        raise ValueError("w must be [n][k]")
+    n, k = w.shape
+    if packed.numel() * packed.element_size() < wq_packed_bytes(n, k, fmt):
+        raise ValueError("packed buffer too small")
+    if scales.numel() != n * (k // 128):
+        raise ValueError("scales must hold n * k / 128 floats")
+    st = load().wq_quantize_pack(_ptr(w, "w", d["bf16"]), n, k, int(fmt), _ptr(packed, "packed"),
+                                 _ptr(scales, "scales", d["f32"]), _stream(stream))
+    _check("wq_quantize_pack", st)
+
+
+def wq_gemv(x, packed, scales, y, n, fmt=WQ_INT4, stream=None):
+    """y[m][n] += x[m] . dequant(W)[n] (y fp32 [m][n] holds zeros or a bias)."""
+    d = _dt()
+    if x.dim() != 2 or y.dim() != 2 or y.shape[0] != x.shape[0] or y.shape[1] != n:
+        raise ValueError("x must be [m][k] and y [m][n]")
+    m, k = x.shape
+    st = load().wq_gemv(_ptr(x, "x", d["bf16"]), m, _ptr(packed, "packed"),
+                        _ptr(scales, "scales", d["f32"]), int(n), k, int(fmt),
+                        _ptr(y, "y", d["f32"]), _stream(stream))
+    _check("wq_gemv", st)

@@ -17,7 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvfp8.so")
-SOURCES = ["kv_cache_ops.hip", "decode_attn.hip", "ingest.hip", "kvfp8_api.hip", "page_pool.cpp"]
+SOURCES = ["kv_cache_ops.hip", "decode_attn.hip", "ingest.hip", "gemv.hip", "kvfp8_api.hip", "page_pool.cpp"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,350 @@
+// Weight-only quantized decode GEMV: y[m][n] += sum_k x[m][k] * q[n][k] * s[n][k / 128]
+// with INT4 or FP8 e4m3 weight codes q and one fp32 scale per (row, 128-input
+// group), bf16 activations x. Decode streams the weights from HBM for every
+// token, so fewer weight bytes give each token sooner (remio.ai/it "Il serving
+// di modelli più piccoli di Cloudflare riduce la memoria, ma la sicurezza
+// diventa la prova decisiva", section "La compressione dei pesi GLM modifica
+// il compromesso tra le fasi"); the codes are expanded before the product.
+//
+//  * packed layout (documented in kvfp8.h): block (nt, g) = rows 16 nt ..
+//    16 nt + 15, inputs 128 g .. 128 g + 127; lane l of a wavefront owns the
+//    16-byte chunk(s) at 16 l (+ 1 KiB) holding exactly its A operands of the
+//    four 16x16x32 bf16 MFMAs over the group (row l % 16, inputs
+//    32 c + 8 (l / 16) + 0..7 of slice c), so each load is a coalesced 1 KiB;
+//  * integer codes become bf16 exactly (|q| <= 8) and e4m3 codes through the
+//    exact hardware decode; the MFMA sums one group in fp32 and the group's
+//    row scale multiplies that partial (the products themselves are exact);
+//  * grid: a workgroup = 4 wavefronts = 4 consecutive 16-row tiles over one
+//    range of input groups; the activations of that range pass through LDS
+//    in double-buffered chunks loaded by the whole workgroup, and each
+//    chunk's codes are loaded into registers one chunk ahead; ranges are
+//    split so the grid fills the chip, and partial sums are added to y with
+//    hardware fp32 atomics (y must hold zeros or a bias on entry).
+#include <algorithm>
+
+#include "kv_device.h"
+#include "kv_launch.h"
+
+namespace kvfp8 {
+
+constexpr int kWGroup = 128;       // inputs per scale group
+constexpr int kGemvWaves = 4;
+
+// ---------------------------------------------------------------------------
+// quantize + pack
+// ---------------------------------------------------------------------------
+// One wavefront per (16-row tile, group): lane (r = l % 16, j = l / 16) holds
+// the 32 values of row r at inputs 32 c + 8 j + i (c, i < 8 | 4); the group's
+// amax of row r is reduced over the 4 lanes r, r + 16, r + 32, r + 48.
+template <bool INT4>
+__global__ __launch_bounds__(256) void wq_pack_kernel(const uint16_t* __restrict__ w, int32_t n,
+                                                      int32_t k, uint8_t* __restrict__ packed,
+                                                      float* __restrict__ scales) {
+    const int groups = k / kWGroup;
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+    if (item >= static_cast<int64_t>(n / 16) * groups) return;
+    const int nt = static_cast<int>(item / groups);
+    const int g = static_cast<int>(item % groups);
+    const int lane = threadIdx.x % 64;
+    const int r = lane % 16, j = lane / 16;
+    const uint16_t* row = w + static_cast<size_t>(16 * nt + r) * k + kWGroup * g + 8 * j;
+    u32x4 raw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(row + 32 * c);
+    uint32_t amax = 0;                                       // bf16 magnitude bits
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            amax = max(amax, raw[c][e] & 0x7FFFu);
+            amax = max(amax, (raw[c][e] >> 16) & 0x7FFFu);
+        }
+    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 16)));
+    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 32)));
+    const float a = __uint_as_float(amax << 16);
+    const float s = a > 0.0f ? a / (INT4 ? 7.0f : 448.0f) : 1.0f;
+    const size_t blk = static_cast<size_t>(nt) * groups + g;
+    if (j == 0) scales[blk * 16 + r] = s;
+    if constexpr (INT4) {
+        uint32_t d[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t bits = (raw[c][i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+                // round-to-odd quotient, then half-to-even to an integer: exact (24 >= 4 + 2)
+                const float qf = rintf(div_round_odd(bf16_bits_to_float(bits), s));
+                const int q = static_cast<int>(fminf(fmaxf(qf, -8.0f), 7.0f));
+                word |= (static_cast<uint32_t>(q) & 0xFu) << (4 * i);
+            }
+            d[c] = word;
+        }
+        *reinterpret_cast<u32x4*>(packed + blk * 1024 + 16 * lane) = u32x4{d[0], d[1], d[2], d[3]};
+    } else {
+        uint32_t d[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t lo = raw[c][2 * h], hi = raw[c][2 * h + 1];
+                d[2 * c + h] = encode4_e4m3(div_round_odd(bf16_bits_to_float(lo & 0xFFFF), s),
+                                            div_round_odd(bf16_bits_to_float(lo >> 16), s),
+                                            div_round_odd(bf16_bits_to_float(hi & 0xFFFF), s),
+                                            div_round_odd(bf16_bits_to_float(hi >> 16), s));
+            }
+        // chunk 0 (at 16 l) holds slices 0, 1; chunk 1 (at 1024 + 16 l) slices 2, 3
+        uint8_t* base = packed + blk * 2048 + 16 * lane;
+        *reinterpret_cast<u32x4*>(base) = u32x4{d[0], d[1], d[2], d[3]};
+        *reinterpret_cast<u32x4*>(base + 1024) = u32x4{d[4], d[5], d[6], d[7]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GEMV
+// ---------------------------------------------------------------------------
+// 8 signed nibbles (little-endian) -> 8 bf16, exactly. The sign extension is
+// written as shifts of a signed int (the bitfield-extract builtin's result
+// was converted as unsigned by this compiler).
+__device__ __forceinline__ int nibble_s(uint32_t w, int i) {
+    return static_cast<int32_t>(w << (28 - 4 * i)) >> 28;
+}
+
+__device__ __forceinline__ bf16x8 int4x8_to_bf16(uint32_t w) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const float a = static_cast<float>(nibble_s(w, i));
+        const float b = static_cast<float>(nibble_s(w, i + 1));
+        const bf16x2 p = __builtin_convertvector((f32x2{a, b}), bf16x2);
+        r[i] = p[0];
+        r[i + 1] = p[1];
+    }
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo_w, uint32_t hi_w) {
+    bf16x2 p0, p1, p2, p3;
+    decode4_bf16(lo_w, p0, p1);
+    decode4_bf16(hi_w, p2, p3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Groups of inputs per LDS chunk of activations, by m-tile count: the chunk
+// (MT * 16 rows x CG * 128 inputs, double-buffered) stays within ~68 KiB.
+// Chunk and grid sizes (measured on the decode layer shapes): with one m-tile
+// (<= 16 tokens) short chunks and many workgroups keep the most weight bytes
+// in flight; with more tokens fewer splits of the inputs cut the re-staged
+// activations and the atomic adds.
+#ifndef KVFP8_GEMV_CG1
+#define KVFP8_GEMV_CG1 2          // groups per chunk with one m-tile
+#endif
+#ifndef KVFP8_GEMV_TARGET_WGS1
+#define KVFP8_GEMV_TARGET_WGS1 2048   // up to 8 tokens
+#endif
+#ifndef KVFP8_GEMV_TARGET_WGS
+#define KVFP8_GEMV_TARGET_WGS 768     // 9 .. 16 tokens
+#endif
+#ifndef KVFP8_GEMV_TARGET_WGS3
+#define KVFP8_GEMV_TARGET_WGS3 512    // more than 16 tokens
+#endif
+template <int MT>
+struct GemvChunk {
+    static constexpr int CG = MT == 1 ? KVFP8_GEMV_CG1 : (MT == 2 ? 4 : 2);
+    static constexpr int ROW = CG * kWGroup + 8;      // halves per LDS row (16-byte pad)
+    static constexpr int PIECES = MT * 16 * CG * 16;  // 16-byte pieces per chunk
+    static_assert(PIECES % (kGemvWaves * 64) == 0, "pieces per thread");
+    static constexpr int PER_THREAD = PIECES / (kGemvWaves * 64);
+};
+
+template <bool INT4>
+struct GroupCodes {
+    u32x4 w[INT4 ? 1 : 2];
+};
+
+template <bool INT4, int MT>
+__global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
+    const uint16_t* __restrict__ x, int32_t m_rows, const uint8_t* __restrict__ packed,
+    const float* __restrict__ scales, int32_t n, int32_t k, float* __restrict__ y,
+    int32_t groups_per_wg) {
+    using C = GemvChunk<MT>;
+    constexpr int CG = C::CG;
+    __shared__ uint16_t xs[2][MT * 16][C::ROW];
+
+    const int groups = k / kWGroup;
+    const int n_tiles = n / 16;
+    const int n_groups_rows = (n_tiles + kGemvWaves - 1) / kGemvWaves;   // 64-row groups
+    const int wg_row = blockIdx.x % n_groups_rows;
+    const int wg_k = blockIdx.x / n_groups_rows;
+    const int wave = threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
+    const int nt = wg_row * kGemvWaves + wave;
+    // a wave past the last tile still joins the chunk loads and barriers
+    const bool active = nt < n_tiles;
+    const int g0 = wg_k * groups_per_wg;
+    const int g1 = min(groups, g0 + groups_per_wg);
+    const int n_chunks = (g1 - g0 + CG - 1) / CG;
+    const int col = lane % 16;          // B: token m within the m-tile; C: column
+    const int jg = lane / 16;           // B: input sub-slice; C: row group of 4
+
+    // activation chunk ci -> registers (zeros past the rows or groups), then LDS
+    u32x4 xr[C::PER_THREAD];
+    const auto load_x = [&](int ci) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < C::PER_THREAD; ++u) {
+            const int p = threadIdx.x + kGemvWaves * 64 * u;
+            const int row = p / (CG * 16), c8 = p % (CG * 16);
+            const int g = g0 + ci * CG + c8 / 16;
+            xr[u] = (row < m_rows && g < g1)
+                        ? *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(row) * k +
+                                                          static_cast<size_t>(kWGroup) * (g0 + ci * CG) + 8 * c8)
+                        : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    const auto store_x = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < C::PER_THREAD; ++u) {
+            const int p = threadIdx.x + kGemvWaves * 64 * u;
+            const int row = p / (CG * 16), c8 = p % (CG * 16);
+            *reinterpret_cast<u32x4*>(&xs[buf][row][8 * c8]) = xr[u];
+        }
+    };
+    // codes and scales of chunk ci (groups past g1 are not loaded)
+    GroupCodes<INT4> wc[CG];
+    f32x4 sc[CG];
+    const auto load_w = [&](int ci, GroupCodes<INT4> (&w)[CG], f32x4 (&s)[CG]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < CG; ++q) {
+            const int g = g0 + ci * CG + q;
+            if (active && g < g1) {
+                const size_t blk = static_cast<size_t>(nt) * groups + g;
+                if constexpr (INT4) {
+                    w[q].w[0] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(packed + blk * 1024 + 16 * lane));
+                } else {
+                    w[q].w[0] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(packed + blk * 2048 + 16 * lane));
+                    w[q].w[1] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(packed + blk * 2048 + 1024 + 16 * lane));
+                }
+                s[q] = *reinterpret_cast<const f32x4*>(scales + blk * 16 + 4 * jg);
+            }
+        }
+    };
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (n_chunks > 0) {
+        load_x(0);
+        load_w(0, wc, sc);
+        store_x(0);
+    }
+    __syncthreads();
+    for (int ci = 0; ci < n_chunks; ++ci) {
+        const int buf = ci & 1;
+        const bool more = ci + 1 < n_chunks;                  // uniform over the workgroup
+        GroupCodes<INT4> wn[CG];
+        f32x4 sn[CG];
+        if (more) {                                           // next chunk in flight
+            load_x(ci + 1);
+            load_w(ci + 1, wn, sn);
+        }
+        if (active) {
+#pragma unroll
+            for (int q = 0; q < CG; ++q) {
+                if (g0 + ci * CG + q >= g1) break;            // uniform
+                bf16x8 A[4];
+                if constexpr (INT4) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) A[c] = int4x8_to_bf16(wc[q].w[0][c]);
+                } else {
+                    A[0] = e4m3x8_to_bf16(wc[q].w[0][0], wc[q].w[0][1]);
+                    A[1] = e4m3x8_to_bf16(wc[q].w[0][2], wc[q].w[0][3]);
+                    A[2] = e4m3x8_to_bf16(wc[q].w[1][0], wc[q].w[1][1]);
+                    A[3] = e4m3x8_to_bf16(wc[q].w[1][2], wc[q].w[1][3]);
+                }
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const u32x4 xb = *reinterpret_cast<const u32x4*>(
+                            &xs[buf][16 * t + col][kWGroup * q + 32 * c + 8 * jg]);
+                        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            A[c], __builtin_bit_cast(bf16x8, xb), part, 0, 0, 0);
+                    }
+                    acc[t] += sc[q] * part;     // rows 4 jg + i of the tile carry scale sc[q][i]
+                }
+            }
+        }
+        if (more) {
+            store_x(buf ^ 1);                  // the other buffer: last read before the barrier
+#pragma unroll
+            for (int q = 0; q < CG; ++q) {
+                wc[q] = wn[q];
+                sc[q] = sn[q];
+            }
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+    // C layout: lane holds rows 16 nt + 4 jg + i, column 16 t + col
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int m = 16 * t + col;
+        if (m >= m_rows) continue;
+        float* yr = y + static_cast<size_t>(m) * n + 16 * nt + 4 * jg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(yr + i, acc[t][i]);
+    }
+}
+
+size_t wq_packed_bytes(int32_t n, int32_t k, bool int4) {
+    return static_cast<size_t>(n) * k / (int4 ? 2 : 1);
+}
+
+hipError_t launch_wq_pack(bool int4, const uint16_t* w, int32_t n, int32_t k, uint8_t* packed,
+                          float* scales, hipStream_t stream) {
+    const int64_t items = static_cast<int64_t>(n / 16) * (k / kWGroup);
+    if (items == 0) return hipSuccess;
+    const dim3 grid(static_cast<uint32_t>((items + 3) / 4));
+    if (int4)
+        hipLaunchKernelGGL(wq_pack_kernel<true>, grid, dim3(256), 0, stream, w, n, k, packed, scales);
+    else
+        hipLaunchKernelGGL(wq_pack_kernel<false>, grid, dim3(256), 0, stream, w, n, k, packed, scales);
+    return hipGetLastError();
+}
+
+// y += W x for m_rows <= 64 (callers split larger batches).
+hipError_t launch_wq_gemv(bool int4, const uint16_t* x, int32_t m_rows, const uint8_t* packed,
+                          const float* scales, int32_t n, int32_t k, float* y,
+                          hipStream_t stream) {
+    if (m_rows == 0 || n == 0 || k == 0) return hipSuccess;
+    const int groups = k / kWGroup;
+    const int64_t row_groups = (n / 16 + kGemvWaves - 1) / kGemvWaves;
+    // split the input groups so the grid holds ~4 workgroups per CU, at least 2 groups each
+    const int mt = (m_rows + 15) / 16;
+    const int64_t target = m_rows <= 8 ? KVFP8_GEMV_TARGET_WGS1
+                           : m_rows <= 16 ? KVFP8_GEMV_TARGET_WGS : KVFP8_GEMV_TARGET_WGS3;
+    int64_t splits = (target + row_groups - 1) / row_groups;
+    splits = std::min<int64_t>(splits, std::max(1, groups / 2));
+    const int per = static_cast<int>((groups + splits - 1) / splits);
+    splits = (groups + per - 1) / per;
+    const dim3 grid(static_cast<uint32_t>(row_groups * splits));
+#define KVFP8_GEMV(I4, MTV)                                                                     \
+    hipLaunchKernelGGL((wq_gemv_kernel<I4, MTV>), grid, dim3(kGemvWaves * 64), 0, stream, x,    \
+                       m_rows, packed, scales, n, k, y, per)
+    if (int4) {
+        if (mt == 1) KVFP8_GEMV(true, 1); else if (mt == 2) KVFP8_GEMV(true, 2);
+        else if (mt == 3) KVFP8_GEMV(true, 3); else KVFP8_GEMV(true, 4);
+    } else {
+        if (mt == 1) KVFP8_GEMV(false, 1); else if (mt == 2) KVFP8_GEMV(false, 2);
+        else if (mt == 3) KVFP8_GEMV(false, 3); else KVFP8_GEMV(false, 4);
+    }
+#undef KVFP8_GEMV
+    return hipGetLastError();
+}
+
+}  // namespace kvfp8

@@ -59,4 +59,13 @@ hipError_t launch_ingest(bool fp8, const uint16_t* k_rows, const uint16_t* v_row
                          void* k_pool, void* v_pool, int32_t num_pages, int32_t num_kv_heads,
                          const uint8_t* abort, hipStream_t stream);
 
+size_t wq_packed_bytes(int32_t n, int32_t k, bool int4);
+
+hipError_t launch_wq_pack(bool int4, const uint16_t* w, int32_t n, int32_t k, uint8_t* packed,
+                          float* scales, hipStream_t stream);
+
+hipError_t launch_wq_gemv(bool int4, const uint16_t* x, int32_t m_rows, const uint8_t* packed,
+                          const float* scales, int32_t n, int32_t k, float* y,
+                          hipStream_t stream);
+
 }  // namespace kvfp8

@@ -303,4 +303,43 @@ int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
         v_pool, num_pages, num_kv_heads, abort, static_cast<hipStream_t>(stream)));
 }
 
+size_t wq_packed_bytes(int32_t n, int32_t k, int32_t format) {
+    if (n < 0 || k < 0 || n % 16 || k % 128 || (format != WQ_INT4 && format != WQ_FP8_E4M3))
+        return 0;
+    return kvfp8::wq_packed_bytes(n, k, format == WQ_INT4);
+}
+
+int wq_quantize_pack(const void* w, int32_t n, int32_t k, int32_t format, void* packed,
+                     float* scales, void* stream) {
+    if (n < 0 || k < 0) return KV_ERR_SHAPE;
+    if (n % 16 || k % 128) return KV_ERR_UNSUPPORTED;
+    if (format != WQ_INT4 && format != WQ_FP8_E4M3) return KV_ERR_UNSUPPORTED;
+    if (n == 0 || k == 0) return KV_OK;
+    if (!w || !packed || !scales) return KV_ERR_NULL;
+    if (misaligned(w, 16) || misaligned(packed, 16) || misaligned(scales, 16)) return KV_ERR_ALIGN;
+    return launch_status(kvfp8::launch_wq_pack(format == WQ_INT4, static_cast<const uint16_t*>(w),
+                                               n, k, static_cast<uint8_t*>(packed), scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int wq_gemv(const void* x, int32_t m, const void* packed, const float* scales, int32_t n,
+            int32_t k, int32_t format, float* y, void* stream) {
+    if (m < 0 || n < 0 || k < 0) return KV_ERR_SHAPE;
+    if (n % 16 || k % 128) return KV_ERR_UNSUPPORTED;
+    if (format != WQ_INT4 && format != WQ_FP8_E4M3) return KV_ERR_UNSUPPORTED;
+    if (m == 0 || n == 0 || k == 0) return KV_OK;
+    if (!x || !packed || !scales || !y) return KV_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(packed, 16) || misaligned(scales, 16) || misaligned(y, 16))
+        return KV_ERR_ALIGN;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t m0 = 0; m0 < m; m0 += 64) {            // 64 activation rows per launch
+        const int32_t rows = m - m0 < 64 ? m - m0 : 64;
+        const int r = launch_status(kvfp8::launch_wq_gemv(
+            format == WQ_INT4, static_cast<const uint16_t*>(x) + static_cast<size_t>(m0) * k, rows,
+            static_cast<const uint8_t*>(packed), scales, n, k, y + static_cast<size_t>(m0) * n, st));
+        if (r != KV_OK) return r;
+    }
+    return KV_OK;
+}
+
 }  // extern "C"

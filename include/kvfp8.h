@@ -321,6 +321,55 @@ int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
                       void* k_pool, void* v_pool, int32_t num_pages, int32_t num_kv_heads,
                       int32_t head_dim, int32_t page_size, const uint8_t* abort, void* stream);
 
+/*
+ * Weight-only quantized decode GEMV. The pages compress GLM's weights from
+ * FP8 to INT4 for decode, where the weights are streamed from HBM for every
+ * token and fewer bytes give each token sooner; the codes are expanded before
+ * the product (remio.ai/it, section "La compressione dei pesi GLM modifica il
+ * compromesso tra le fasi"). Formats (this library's reading; the pages give
+ * only "four-bit integer"): weights W [n][k] in bf16 are quantized per row and
+ * per group of 128 inputs with one fp32 scale s:
+ *   WQ_INT4:      q = clamp(RNE(w / s), -8, 7) of the exact quotient, s = amax / 7
+ *   WQ_FP8_E4M3:  q = E4M3(w / s) (the KV encoder), s = amax / 448
+ * (s = 1.0 for an all-zero group; weights must be finite), and the product is
+ *   y[m][n] += sum_k x[m][k] * q[n][k] * s[n][k / 128]
+ * for bf16 activations x [m][k] and fp32 y [m][n].
+ *
+ * Packed layout (MFMA operand order), block (nt, g) = rows 16 nt .. 16 nt + 15,
+ * inputs 128 g .. 128 g + 127, blocks ordered nt-major: block index
+ * b = nt * (k / 128) + g. Element (row 16 nt + r, input 128 g + 32 c + 8 j + i),
+ * r < 16, c < 4, j < 4, i < 8, with lane l = 16 j + r:
+ *   WQ_INT4:     byte 1024 b + 16 l + 4 c + i / 2, nibble i % 2 (low first),
+ *                two's complement;
+ *   WQ_FP8_E4M3: byte 2048 b + 1024 (c / 2) + 16 l + 8 (c % 2) + i.
+ * Scales: fp32 [n / 16][k / 128][16], element (b, r) = s of row 16 nt + r.
+ */
+#define WQ_INT4 0
+#define WQ_FP8_E4M3 1
+
+/* Bytes of the packed codes for an n x k matrix (0 if n % 16, k % 128 or the
+ * format is unsupported). Scales take n * (k / 128) * 4 bytes. */
+size_t wq_packed_bytes(int32_t n, int32_t k, int32_t format);
+
+/*
+ * Quantize bf16 weights w [n][k] (row-major, device) into packed codes and
+ * scales (layouts above). Requires n % 16 == 0, k % 128 == 0. Errors:
+ * KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ */
+int wq_quantize_pack(const void* w, int32_t n, int32_t k, int32_t format, void* packed,
+                     float* scales, void* stream);
+
+/*
+ * y[m][n] += x[m][:] . dequant(W)[n][:] for m rows of bf16 activations x
+ * [m][k] and packed weights (any m; 64 rows per launch). y must hold zeros or
+ * a bias on entry: partial sums over ranges of inputs are added with fp32
+ * atomics, so the last bits of y may differ between runs. All pointers
+ * 16-byte aligned. Errors: KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_NULL,
+ * KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ */
+int wq_gemv(const void* x, int32_t m, const void* packed, const float* scales, int32_t n,
+            int32_t k, int32_t format, float* y, void* stream);
+
 /* Human-readable name of a kv_status value (static string, never NULL). */
 const char* kv_status_str(int status);
 

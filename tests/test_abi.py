@@ -44,7 +44,7 @@ def test_header_declares_the_entry_points():
               "paged_decode_attn_append", "kv_amax_accumulate", "kv_scales_from_amax",
               "kv_ingest_prefill", "kv_status_str", "kv_pool_create", "kv_pool_destroy",
               "kv_pool_alloc", "kv_pool_free", "kv_pool_tags", "kv_pool_record_check",
-              "kv_pool_get_stats"]:
+              "kv_pool_get_stats", "wq_packed_bytes", "wq_quantize_pack", "wq_gemv"]:
         assert n in names
 
 
@@ -191,6 +191,25 @@ def test_ingest_entry_points_reject_bad_arguments(lib):
     assert ingest_call(lib, row_start=None) == NULL
     assert ingest_call(lib, k_pool=A + 4) == ALIGN
     assert ingest_call(lib, batch=0, k_rows=None) == OK
+
+
+def test_weight_gemv_entry_points_reject_bad_arguments(lib):
+    assert lib.wq_packed_bytes(64, 256, 0) == 64 * 256 // 2
+    assert lib.wq_packed_bytes(64, 256, 1) == 64 * 256
+    assert lib.wq_packed_bytes(60, 256, 0) == 0 and lib.wq_packed_bytes(64, 200, 1) == 0
+    assert lib.wq_packed_bytes(64, 256, 5) == 0
+    assert lib.wq_quantize_pack(A, 60, 256, 0, A, A, None) == UNSUP      # rows % 16
+    assert lib.wq_quantize_pack(A, 64, 100, 0, A, A, None) == UNSUP      # inputs % 128
+    assert lib.wq_quantize_pack(A, 64, 256, 2, A, A, None) == UNSUP      # format
+    assert lib.wq_quantize_pack(A, -16, 256, 0, A, A, None) == SHAPE
+    assert lib.wq_quantize_pack(None, 64, 256, 0, A, A, None) == NULL
+    assert lib.wq_quantize_pack(A, 64, 256, 0, A + 4, A, None) == ALIGN
+    assert lib.wq_quantize_pack(None, 0, 256, 0, None, None, None) == OK
+    assert lib.wq_gemv(A, 4, A, A, 64, 256, 0, None, None) == NULL
+    assert lib.wq_gemv(A, 4, A, A, 64, 256, 0, A + 8, None) == ALIGN
+    assert lib.wq_gemv(A, -1, A, A, 64, 256, 0, A, None) == SHAPE
+    assert lib.wq_gemv(A, 4, A, A, 72, 256, 0, A, None) == UNSUP
+    assert lib.wq_gemv(None, 0, None, None, 64, 256, 1, None, None) == OK
 
 
 def test_workspace_and_partition_sizing(lib):

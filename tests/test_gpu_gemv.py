@@ -1,0 +1,125 @@
+"""GPU parity of the weight-only quantized decode GEMV (wq_quantize_pack,
+wq_gemv) against the oracle in oracle/weights.py: codes and scales bit for
+bit (unpacked through the layout formulas of include/kvfp8.h, written out
+here independently), the product within a tolerance derived from fp32
+accumulation of exact products."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import weights
+from tests.gpu_harness import DEV, say
+
+pytestmark = pytest.mark.gpu
+G = 128
+# fp32 sums of exact bf16 x int products, 128 per group, then scaled groups:
+# relative error well below 1e-5 of the result's norm
+REL_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import fp8_e4m3_paged_amd as k
+    k.load()
+    return k
+
+
+def _index_maps(n, k, fmt):
+    """Byte offset (and nibble) of every element (row, input), from the header's formulas."""
+    rows = np.arange(n)[:, None]
+    cols = np.arange(k)[None, :]
+    nt, r = rows // 16, rows % 16
+    g, kk = cols // G, cols % G
+    c, j, i = kk // 32, (kk % 32) // 8, kk % 8
+    b = nt * (k // G) + g
+    lane = 16 * j + r
+    if fmt == 0:
+        return 1024 * b + 16 * lane + 4 * c + i // 2, i % 2
+    return 2048 * b + 1024 * (c // 2) + 16 * lane + 8 * (c % 2) + i, None
+
+
+def _unpack(packed, n, k, fmt):
+    off, nib = _index_maps(n, k, fmt)
+    byte = packed[off]
+    if fmt == 0:
+        v = (byte >> (4 * nib)) & 0xF
+        return np.where(v >= 8, v - 16, v).astype(np.int8)
+    return byte
+
+
+def _weights(rng, n, k):
+    w = rng.normal(0, 0.03, size=(n, k)).astype(np.float32)
+    bits = (w.view(np.uint32) >> 16).astype(np.uint16)
+    # an all-zero group, and a group of exact multiples with ties (2.5 s, 3.5 s, ...)
+    bits[0, :G] = 0
+    if n > 1 and k >= 2 * G:
+        ties = np.array([7.0, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5] * (G // 8)) * 2.0 ** -6
+        bits[1, G:2 * G] = (ties.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return bits
+
+
+def _pack(kv, wb, fmt):
+    n, k = wb.shape
+    w = torch.from_numpy(wb.view(np.int16)).to(DEV)
+    packed = torch.zeros(kv.wq_packed_bytes(n, k, fmt), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(n * (k // G), dtype=torch.float32, device=DEV)
+    kv.wq_quantize_pack(w, packed, scales, fmt)
+    torch.cuda.synchronize()
+    return packed, scales
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("n,k", [(16, 128), (64, 256), (80, 384), (1024, 1024)])
+def test_pack_codes_and_scales_bit_exact(kv, fmt, n, k):
+    wb = _weights(np.random.default_rng(n + k + fmt), n, k)
+    packed, scales = _pack(kv, wb, fmt)
+    q_o, s_o = weights.quantize_int4(wb) if fmt == 0 else weights.quantize_fp8(wb)
+    got_s = scales.cpu().numpy().reshape(n // 16, k // G, 16).transpose(0, 2, 1).reshape(n, k // G)
+    assert np.array_equal(got_s.view(np.uint32), s_o.view(np.uint32))
+    got_q = _unpack(packed.cpu().numpy(), n, k, fmt)
+    assert np.array_equal(got_q, q_o)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 33, 64, 70])
+def test_gemv_against_oracle(kv, fmt, m):
+    n, k = 320, 1024
+    rng = np.random.default_rng(100 + m + fmt)
+    wb = _weights(rng, n, k)
+    packed, scales = _pack(kv, wb, fmt)
+    q_o, s_o = weights.quantize_int4(wb) if fmt == 0 else weights.quantize_fp8(wb)
+    wd = weights.dequant_int4(q_o, s_o) if fmt == 0 else weights.dequant_fp8(q_o, s_o)
+    xb = (rng.normal(0, 1, size=(m, k)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bias = rng.normal(0, 1, size=(m, n)).astype(np.float32)
+    y = torch.from_numpy(bias.copy()).to(DEV)
+    kv.wq_gemv(torch.from_numpy(xb.view(np.int16)).to(DEV), packed, scales, y, n, fmt)
+    torch.cuda.synchronize()
+    want = bias.astype(np.float64) + weights.gemv(xb, wd)
+    got = y.cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert rel <= REL_TOL, f"fmt {fmt} m {m}: rel_l2 {rel:.2e}"
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_gemv_full_size_sampled_rows(kv, fmt):
+    """8192 x 8192 weights, 16 tokens, in the launch configuration the
+    benchmark times; rows sampled for the oracle (codes checked for them)."""
+    n = k = 8192
+    rng = np.random.default_rng(7 + fmt)
+    wb = _weights(rng, n, k)
+    packed, scales = _pack(kv, wb, fmt)
+    xb = (rng.normal(0, 1, size=(16, k)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = torch.zeros((16, n), dtype=torch.float32, device=DEV)
+    kv.wq_gemv(torch.from_numpy(xb.view(np.int16)).to(DEV), packed, scales, y, n, fmt)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 17, 4095, 8191] + rng.integers(0, n, 11).tolist())
+    q_o, s_o = weights.quantize_int4(wb[rows]) if fmt == 0 else weights.quantize_fp8(wb[rows])
+    wd = weights.dequant_int4(q_o, s_o) if fmt == 0 else weights.dequant_fp8(q_o, s_o)
+    want = weights.gemv(xb, wd)
+    got = y.cpu().numpy()[:, rows].astype(np.float64)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert rel <= REL_TOL
+    allq = _unpack(packed.cpu().numpy(), n, k, fmt)
+    assert np.array_equal(allq[rows], q_o)
+    say(f"gemv fmt {fmt} 8192x8192 m=16: sampled rows rel_l2 {rel:.2e}")
