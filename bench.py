@@ -73,6 +73,9 @@ def parse():
                     help="also time as many steps with the no-op tracker (no tag check)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
+    ap.add_argument("--graph", default="off", choices=["on", "off"],
+                    help="time the steps as captured HIP graphs (one per step, captured "
+                         "before timing) instead of eager launches (measured slower here)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--mode", default="step", choices=["step", "copy", "ingest", "sweep", "gemv"],
                     help="copy: time a plain device copy of --copy-mib MiB (counter "
@@ -559,7 +562,7 @@ def main():
     ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps * wl.num_layers)]
 
-    def run_step(s, timed_slot=None, check=verify):
+    def run_step(s, timed_slot=None, check=verify, stream=stream):
         abort = st.abort if check else None
         if check:
             kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens[s],
@@ -600,12 +603,27 @@ def main():
         assert int(st.abort.sum().item()) == 0, "no request of this workload may abort"
     log(args, f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
-    # pass 1: the timed steps
+    # pass 1: the timed steps (as HIP graphs: one per step, each holding the
+    # tag check and the layers' launches with that step's tensors, captured
+    # before the timed region; replaying them is the same work with the
+    # launch overhead between kernels taken out)
+    graphs = None
+    if args.graph == "on":
+        graphs = []
+        for i in range(args.steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(args.warmup + i, stream=torch.cuda.current_stream())
+            graphs.append(g)
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        run_step(args.warmup + i)
+        if graphs is not None:
+            graphs[i].replay()
+        else:
+            run_step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(end)
@@ -637,11 +655,22 @@ def main():
     if measure_noop:
         # the same number of steps with the no-op tracker: no tag check, abort = NULL
         a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        base3 = args.warmup + 2 * args.steps
+        graphs3 = None
+        if args.graph == "on":                   # timed the same way as pass 1
+            graphs3 = []
+            for i in range(args.steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    run_step(base3 + i, check=False, stream=torch.cuda.current_stream())
+                graphs3.append(g)
         torch.cuda.synchronize()
         a2.record(stream)
-        base3 = args.warmup + 2 * args.steps
         for i in range(args.steps):
-            run_step(base3 + i, check=False)
+            if graphs3 is not None:
+                graphs3[i].replay()
+            else:
+                run_step(base3 + i, check=False)
         b2.record(stream)
         torch.cuda.synchronize()
         off_ms = a2.elapsed_time(b2)
@@ -691,6 +720,7 @@ def main():
             "page_size": wl.page_size, "mean_ctx": round(float(wl.seq_lens0.mean()) + 1, 1),
             "cache": cache, "verify": verify, "partition_tokens": pt_eff,
             "append": "fused into the attention launch" if fused else "separate launch",
+            "launch": "HIP graph per step" if args.graph == "on" else "eager",
         },
         "roofline": {
             "bound": "hbm",
