@@ -102,15 +102,17 @@ def test_gemv_against_oracle(kv, fmt, m):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-def test_gemv_full_size_sampled_rows(kv, fmt):
-    """8192 x 8192 weights, 16 tokens, in the launch configuration the
-    benchmark times; rows sampled for the oracle (codes checked for them)."""
+@pytest.mark.parametrize("m", [1, 16])
+def test_gemv_full_size_sampled_rows(kv, fmt, m):
+    """8192 x 8192 weights, 1 token (the small-batch kernel) and 16 tokens,
+    in the launch configurations the benchmark times; rows sampled for the
+    oracle (codes checked for them)."""
     n = k = 8192
     rng = np.random.default_rng(7 + fmt)
     wb = _weights(rng, n, k)
     packed, scales = _pack(kv, wb, fmt)
-    xb = (rng.normal(0, 1, size=(16, k)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
-    y = torch.zeros((16, n), dtype=torch.float32, device=DEV)
+    xb = (rng.normal(0, 1, size=(m, k)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = torch.zeros((m, n), dtype=torch.float32, device=DEV)
     kv.wq_gemv(torch.from_numpy(xb.view(np.int16)).to(DEV), packed, scales, y, n, fmt)
     torch.cuda.synchronize()
     rows = np.array([0, 1, 17, 4095, 8191] + rng.integers(0, n, 11).tolist())
@@ -122,4 +124,4 @@ def test_gemv_full_size_sampled_rows(kv, fmt):
     assert rel <= REL_TOL
     allq = _unpack(packed.cpu().numpy(), n, k, fmt)
     assert np.array_equal(allq[rows], q_o)
-    say(f"gemv fmt {fmt} 8192x8192 m=16: sampled rows rel_l2 {rel:.2e}")
+    say(f"gemv fmt {fmt} 8192x8192 m={m}: sampled rows rel_l2 {rel:.2e}")
