@@ -14,7 +14,12 @@
 //    builds exactly the 16-byte chunks that the tile layout places at
 //    16 * lane (+ 1 KiB per chunk), so every store is a full, coalesced
 //    16-byte write of the 2 KiB (FP8) or 4 KiB (BF16) tile; slots past the
-//    prompt's end are written as zeros.
+//    prompt's end are written as zeros. FP8 codes are those of the exact
+//    quotient x / s; a wavefront whose head scale and values allow it
+//    (almost always) forms them from the reciprocal and a Newton step
+//    instead of an IEEE division, which made the writer ALU-bound.
+#include <type_traits>
+
 #include "kv_device.h"
 #include "kv_launch.h"
 
@@ -75,6 +80,68 @@ __global__ void scales_kernel(const float* __restrict__ amax, int32_t n, float* 
 // ---------------------------------------------------------------------------
 // ingest
 // ---------------------------------------------------------------------------
+// The same codes as encode4_e4m3(div_round_odd(x_i, s)), without a division,
+// for scales s in [2^-63, 2^63] with inv = 1 / s, and |x_i| <= 2^63 (so NaN
+// and infinities are excluded and no quotient overflows):
+//  * y0 = |x| inv is within ~2 ulp of the exact quotient; one Newton step
+//    y1 = y0 + (|x| - y0 s) inv is then within one ulp of it (a faithful
+//    rounding), and the remainder |x| - y1 s of a faithful quotient is
+//    exactly representable, so its fma is exact;
+//  * as in div_round_odd, a negative remainder steps the magnitude down one
+//    ulp and any nonzero one sets the last bit (round-to-odd); the 448 clamp
+//    and the sign of x are applied to the bits, then the hardware converts.
+// In that range every quotient that can round to a nonzero code stays a
+// normal float with a normal remainder; smaller ones round to zero however
+// they are approximated.
+__device__ __forceinline__ bool recip_quotient_ok(float s) {
+    return s >= 0x1p-63f && s <= 0x1p63f;
+}
+constexpr uint16_t kRecipMaxMagBits = 0x5F00;      // bf16 magnitude bits of 2^63
+
+__device__ __forceinline__ float quot_round_odd_clamped(float x, float s, float inv) {
+    const float ax = fabsf(x);
+    const float y0 = ax * inv;
+    const float y1 = fmaf(fmaf(-y0, s, ax), inv, y0);
+    const uint32_t rb = __float_as_uint(fmaf(-y1, s, ax));         // exact remainder
+    uint32_t u = __float_as_uint(y1) + static_cast<uint32_t>(static_cast<int32_t>(rb) >> 31);
+    u |= min(rb, 1u);
+    u = min(u, 0x43E00000u);                                        // 448.0f
+    return __uint_as_float(u | (__float_as_uint(x) & 0x80000000u));
+}
+
+__device__ __forceinline__ uint32_t encode4_e4m3_recip(float x0, float x1, float x2, float x3,
+                                                       float s, float inv) {
+    const uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32(quot_round_odd_clamped(x0, s, inv),
+                                                        quot_round_odd_clamped(x1, s, inv), 0u, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(quot_round_odd_clamped(x2, s, inv),
+                                           quot_round_odd_clamped(x3, s, inv), pk, true);
+}
+
+// Running maximum of the magnitude bits of packed bf16 pairs (two 16-bit
+// lanes), to check |x| <= 2^63 for a whole block before taking the
+// reciprocal path.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 bf16x2_max_mag(u16x2 m, uint32_t w) {
+    return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
+}
+__device__ __forceinline__ bool bf16x2_recip_range(u16x2 m) {
+    return m[0] <= kRecipMaxMagBits && m[1] <= kRecipMaxMagBits;
+}
+
+// Four floats x_i -> the e4m3 codes of x_i / s: through the reciprocal when
+// RECIP (the caller checked recip_quotient_ok(s) and |x_i| <= 2^63), else
+// by division.
+template <bool RECIP>
+__device__ __forceinline__ uint32_t quant4_e4m3(float x0, float x1, float x2, float x3, float s,
+                                                float inv) {
+    if constexpr (RECIP) {
+        return encode4_e4m3_recip(x0, x1, x2, x3, s, inv);
+    } else {
+        return encode4_e4m3(div_round_odd(x0, s), div_round_odd(x1, s), div_round_odd(x2, s),
+                            div_round_odd(x3, s));
+    }
+}
+
 constexpr int kIngestWaves = 4;
 // One head's K rows, then its V rows, staged in LDS per wavefront (16 tokens
 // x 128 bf16), rows padded to 272 bytes so V's transposed reads (4 token
@@ -90,6 +157,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Whether every lane of the wavefront holds only |x| <= 2^63 among one
+// head's rows (no NaN or infinity): then the reciprocal encoder is exact.
+__device__ __forceinline__ bool wave_recip_range(const u32x4 (&w)[4]) {
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = bf16x2_max_mag(m, w[k][e]);
+    return __builtin_amdgcn_ballot_w64(!bf16x2_recip_range(m)) == 0;
 }
 
 template <bool FP8>
@@ -163,22 +241,28 @@ __global__ __launch_bounds__(kIngestWaves * 64) void ingest_kernel(
         stage(kw);
         if constexpr (FP8) {
             const float ks = k_scale[g];
+            const float kinv = 1.0f / ks;
+            const auto encode_k = [&](auto recip) __attribute__((always_inline)) {
+                constexpr bool R = decltype(recip)::value;
 #pragma unroll
-            for (int h = 0; h < NCH; ++h) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 16 * h]);
-                const u32x4 b2 = *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 16 * h + 8]);
-                const uint32_t w[8] = {a[0], a[1], a[2], a[3], b2[0], b2[1], b2[2], b2[3]};
-                uint32_t c[4];
+                for (int h = 0; h < NCH; ++h) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 16 * h]);
+                    const u32x4 b2 = *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 16 * h + 8]);
+                    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b2[0], b2[1], b2[2], b2[3]};
+                    uint32_t c[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = w[2 * e], hi = w[2 * e + 1];
-                    c[e] = encode4_e4m3(div_round_odd(bf16_bits_to_float(lo & 0xFFFF), ks),
-                                        div_round_odd(bf16_bits_to_float(lo >> 16), ks),
-                                        div_round_odd(bf16_bits_to_float(hi & 0xFFFF), ks),
-                                        div_round_odd(bf16_bits_to_float(hi >> 16), ks));
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = w[2 * e], hi = w[2 * e + 1];
+                        c[e] = quant4_e4m3<R>(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u),
+                                              __uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u),
+                                              ks, kinv);
+                    }
+                    *reinterpret_cast<u32x4*>(kt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
                 }
-                *reinterpret_cast<u32x4*>(kt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
-            }
+            };
+            // one uniform branch per head: the scale is the wave's, the range is voted on
+            if (recip_quotient_ok(ks) && wave_recip_range(kw)) encode_k(std::true_type{});
+            else encode_k(std::false_type{});
         } else {
 #pragma unroll
             for (int h = 0; h < NCH; ++h)
@@ -190,20 +274,25 @@ __global__ __launch_bounds__(kIngestWaves * 64) void ingest_kernel(
         stage(vw);
         if constexpr (FP8) {
             const float vs = v_scale[g];
+            const float vinv = 1.0f / vs;
+            const auto encode_v = [&](auto recip) __attribute__((always_inline)) {
+                constexpr bool R = decltype(recip)::value;
 #pragma unroll
-            for (int h = 0; h < NCH; ++h) {
-                uint32_t c[4];
+                for (int h = 0; h < NCH; ++h) {
+                    uint32_t c[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {               // dword e: dim 64 h + 16 e + m
-                    const int d = 64 * h + 16 * e + m;
-                    float y[4];
+                    for (int e = 0; e < 4; ++e) {           // dword e: dim 64 h + 16 e + m
+                        const int d = 64 * h + 16 * e + m;
+                        float x[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        y[r] = div_round_odd(bf16_bits_to_float(sx[4 * jg + r][d]), vs);
-                    c[e] = encode4_e4m3(y[0], y[1], y[2], y[3]);
+                        for (int r = 0; r < 4; ++r) x[r] = bf16_bits_to_float(sx[4 * jg + r][d]);
+                        c[e] = quant4_e4m3<R>(x[0], x[1], x[2], x[3], vs, vinv);
+                    }
+                    *reinterpret_cast<u32x4*>(vt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
                 }
-                *reinterpret_cast<u32x4*>(vt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
-            }
+            };
+            if (recip_quotient_ok(vs) && wave_recip_range(vw)) encode_v(std::true_type{});
+            else encode_v(std::false_type{});
         } else {
 #pragma unroll
             for (int h = 0; h < NCH; ++h) {

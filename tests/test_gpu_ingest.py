@@ -281,3 +281,84 @@ def test_ingest_full_size_headline_prompts(kv):
         wv[:L] = e4m3.quantize(vb, vsh[g])
         assert np.array_equal(gk, wk) and np.array_equal(gv, wv), (b, g)
         say(f"full-size ingest: request {b} (L={L}) head {g}: {n} pages bit-exact")
+
+
+def _trap_scales(rng, count=2):
+    """Scales s = fp32(amax / 448) (amax a random bf16) with the positive bf16
+    values x whose plain fp32 quotient x / s lands exactly on an e4m3
+    midpoint although the exact one does not, so that rounding the fp32
+    quotient gives the wrong code: a scan of every finite pattern."""
+    from oracle import e4m3
+    pos = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    x32 = e4m3.bf16_bits_to_f64(pos).astype(np.float32)
+    found = []
+    for abits in rng.integers(0x3D4C, 0x4248, size=64).astype(np.uint16):
+        s = np.float32(e4m3.bf16_bits_to_f64(np.array([abits]))[0] / 448.0)
+        with np.errstate(over="ignore"):
+            naive = e4m3.encode((x32 / s).astype(np.float64))
+        traps = pos[e4m3.quantize(pos, s) != naive]
+        if traps.size:
+            found.append((traps.size, s, traps))
+    found.sort(key=lambda t: -t[0])
+    assert len(found) >= count
+    return [(s, traps) for _, s, traps in found[:count]]
+
+
+def test_ingest_reciprocal_and_division_paths_bit_exact(kv):
+    """The FP8 page writer encodes a (page, head) tile without a division
+    when the head's scale lies in [2^-63, 2^63] and every value of the tile
+    is at most 2^63 in magnitude, and by division otherwise. This case mixes
+    both on purpose, and every byte of both pools must equal the oracle's:
+    clean tiles; one NaN, one infinity and one finite 2^70 confined to single
+    tiles; scales on and just past both ends of the range and FLT_MIN; and
+    two heads full of values (and their one-ulp neighbours) for which a
+    plain fp32 quotient rounds to the wrong code."""
+    rng = np.random.default_rng(31)
+    hkv = 8
+    lens = np.array([48, 40, 33, 16, 64, 7], np.int32)
+    need = -(-lens // P)
+    pool_pages = int(need.sum()) + 6
+    perm = rng.permutation(pool_pages).astype(np.int32)
+    bt = np.full((lens.size, int(need.max()) + 1), -1, np.int32)
+    off = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    n_rows = int(lens.sum())
+    kr = _random_bf16(rng, (n_rows, hkv, 128), specials=False)
+    vr = _random_bf16(rng, (n_rows, hkv, 128), specials=False)
+    ks = ingest.scales_from_amax(ingest.amax_finite(kr))
+    vs = ingest.scales_from_amax(ingest.amax_finite(vr))
+    ks[0], ks[1], ks[7] = 2.0 ** -63, 2.0 ** -64, 2.0 ** 63
+    vs[2], vs[6] = 2.0 ** 64, np.finfo(np.float32).tiny
+    vs[4] = np.nextafter(np.float32(2.0 ** -63), np.float32(0))
+    # midpoint traps in K head 4 and V head 3: trap values with random signs, their
+    # neighbours one ulp either side, and plain values
+    for (arr, sc, g), (s, traps) in zip(((kr, ks, 4), (vr, vs, 3)), _trap_scales(rng)):
+        sc[g] = s
+        t = rng.choice(traps, size=n_rows * 128).astype(np.int32)
+        t += rng.choice(np.array([-1, 0, 0, 0, 1]), size=t.size)
+        t |= rng.integers(0, 2, size=t.size) << 15
+        plain = rng.random(t.size) < 0.25
+        arr[:, g, :] = np.where(plain, arr[:, g, :].reshape(-1), t).astype(np.uint16).reshape(n_rows, 128)
+    # tile-local specials: (request, page, head, which)
+    for b, j, g, which, val in ((1, 1, 2, "k", 0x7FC0), (2, 0, 5, "v", 0x7F80),
+                                (3, 0, 1, "k", 0x6280), (0, 2, 6, "v", 0xFFC1)):
+        row = starts[b] + j * P + 3
+        (kr if which == "k" else vr)[row, g, 17] = val
+    kt = rng.integers(0, 256, (pool_pages, hkv, 2048)).astype(np.uint8)
+    vt = rng.integers(0, 256, (pool_pages, hkv, 2048)).astype(np.uint8)
+    c = dict(lens=lens, bt=bt, starts=starts, kr=kr, vr=vr, ks=ks.astype(np.float32),
+             vs=vs.astype(np.float32), kt=kt, vt=vt)
+    gk, gv = _run_ingest(kv, c, "fp8")
+    wk, wv = _oracle_ingest(c, "fp8")
+    for name, g_, w_ in (("K", gk, wk), ("V", gv, wv)):
+        bad = np.argwhere(g_ != w_)
+        assert bad.size == 0, f"{name}: {len(bad)} bytes differ, first at {bad[:3].tolist()}"
+    # the trap heads do hold values where a plain fp32 quotient rounds wrongly
+    from oracle import e4m3
+    for arr, s in ((kr[:, 4, :], ks[4]), (vr[:, 3, :], vs[3])):
+        naive = e4m3.encode((e4m3.bf16_bits_to_f64(arr).astype(np.float32) / s).astype(np.float64))
+        assert np.count_nonzero(naive != e4m3.quantize(arr, s)) > 100
+    say("ingest fp8: reciprocal and division paths, whole pools bit-exact")
