@@ -37,35 +37,56 @@ __device__ __forceinline__ uint32_t finite_mag_max(uint32_t m, uint32_t w) {
     return hi < 0x7F80u ? max(m, hi) : m;
 }
 
-// Grid-stride over the 16-byte vectors of x; the stride is a multiple of
-// 16 * hkv, so vector v always belongs to head (v / 16) % hkv and each thread
-// keeps one running maximum (bf16 magnitude bits).
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Grid-stride over the 16-byte vectors of x, one load in flight per lane per
+// step (measured faster than several 8 MiB apart); the stride is a multiple
+// of 16 * hkv, so vector v always belongs to head (v / 16) % hkv and each
+// thread keeps one running maximum. The maximum is taken first over all
+// magnitudes as packed 16-bit lanes (two instructions per word); only a
+// thread whose maximum is an Inf or NaN pattern scans its vectors again
+// skipping those. The 16 groups of 16 lanes of a workgroup are combined per
+// head in LDS, then one atomic max per head and workgroup (non-negative
+// floats order like their bits).
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const u32x4* __restrict__ x,
                                                             int64_t n_vec, int32_t hkv,
                                                             uint32_t* __restrict__ amax_bits) {
     const int64_t first = static_cast<int64_t>(blockIdx.x) * kAmaxThreads + threadIdx.x;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kAmaxThreads;
-    const int g = static_cast<int>((first / 16) % hkv);
-    uint32_t m = 0;
-    int64_t v = first;
-    for (; v + 3 * stride < n_vec; v += 4 * stride) {
-        u32x4 w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = __builtin_nontemporal_load(x + v + u * stride);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = finite_mag_max(m, w[u][e]);
-    }
-    for (; v < n_vec; v += stride) {
+    u16x2 mm = {0, 0};
+    for (int64_t v = first; v < n_vec; v += stride) {
         const u32x4 w = __builtin_nontemporal_load(x + v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) m = finite_mag_max(m, w[e]);
+        for (int e = 0; e < 4; ++e)
+            mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, w[e] & 0x7FFF7FFFu));
+    }
+    uint32_t m = max(static_cast<uint32_t>(mm[0]), static_cast<uint32_t>(mm[1]));
+    if (m >= 0x7F80u) {                    // rare: this thread saw +-Inf or NaN
+        m = 0;
+        for (int64_t v = first; v < n_vec; v += stride) {
+            const u32x4 w = x[v];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = finite_mag_max(m, w[e]);
+        }
     }
     // the 16 lanes of a group cover one 256-byte head row segment: same head
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o)));
-    if ((threadIdx.x & 15) == 0 && m != 0) atomicMax(amax_bits + g, m << 16);
+    constexpr int kGroups = kAmaxThreads / 16;
+    __shared__ uint32_t sm[kGroups];
+    if ((threadIdx.x & 15) == 0) sm[threadIdx.x / 16] = m;
+    __syncthreads();
+    if (threadIdx.x < kGroups) {
+        // group q's head is (16 blockIdx + q) % hkv; the first group of each head combines
+        const int q = threadIdx.x;
+        const int base = static_cast<int>((static_cast<int64_t>(blockIdx.x) * kGroups) % hkv);
+        const int gq = (base + q) % hkv;
+        if (q < hkv) {
+            uint32_t r = 0;
+            for (int j = q; j < kGroups; j += hkv) r = max(r, sm[j]);
+            if (r != 0) atomicMax(amax_bits + gq, r << 16);
+        }
+    }
 }
 
 __global__ void scales_kernel(const float* __restrict__ amax, int32_t n, float* __restrict__ out) {
@@ -120,7 +141,6 @@ __device__ __forceinline__ uint32_t encode4_e4m3_recip(float x0, float x1, float
 // Running maximum of the magnitude bits of packed bf16 pairs (two 16-bit
 // lanes), to check |x| <= 2^63 for a whole block before taking the
 // reciprocal path.
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u16x2 bf16x2_max_mag(u16x2 m, uint32_t w) {
     return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
 }
@@ -325,7 +345,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t n_rows, int32_t hkv, float* am
     const int64_t n_vec = n_rows * hkv * (kDim / 8);
     if (n_vec == 0) return hipSuccess;
     int64_t wgs = (n_vec + 4 * kAmaxThreads - 1) / (4 * kAmaxThreads);
-    wgs = wgs < 2048 ? wgs : 2048;
+    wgs = wgs < 2048 ? wgs : 2048;                // measured best of 1024 .. 16384
     wgs = (wgs + hkv - 1) / hkv * hkv;            // stride a multiple of 16 * hkv
     hipLaunchKernelGGL(amax_kernel, dim3(static_cast<uint32_t>(wgs)), dim3(kAmaxThreads), 0,
                        stream, reinterpret_cast<const u32x4*>(x), n_vec, hkv,
