@@ -47,13 +47,37 @@ COUNTER_TRAFFIC = {
 }
 
 
-def kernel_source_sha() -> str:
+# The same for the prefill page writer (ingest_kernel<FP8>, one layer of the
+# headline prompts; profiles/ingest_kernel_c4_prompts.md) and the INT4 GEMV
+# roofline kernel (28672x8192, one token; profiles/wq_gemv_int4_1token.md).
+INGEST_COUNTER_TRAFFIC = {
+    "sources": ("ingest.hip", "kv_device.h"),
+    "source_sha": "1b0956465e5e6822",
+    "read_bytes": 2.2815e9,
+    "write_bytes": 1.1406e9,
+}
+GEMV_COUNTER_TRAFFIC = {
+    "sources": ("gemv.hip", "kv_device.h"),
+    "source_sha": "9352bdb8905703f4",
+    "read_bytes": 1.24975e8,
+    "write_bytes": 2.294e6,
+}
+
+
+def kernel_source_sha(files=("decode_attn.hip", "kv_device.h")) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode_attn.hip", "kv_device.h"):
+    for f in files:
         with open(os.path.join(ROOT, "fp8_e4m3_paged_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def counter_traffic(entry):
+    """Calibrated HBM bytes per launch, or None once the kernel source changed."""
+    if kernel_source_sha(entry["sources"]) != entry["source_sha"]:
+        return None
+    return int(entry["read_bytes"] + entry["write_bytes"])
 
 
 def parse():
@@ -83,6 +107,8 @@ def parse():
                          "sweep: BF16 vs FP8 decode at 1..64 requests under one pool budget; "
                          "gemv: INT4 vs FP8 weight-only decode GEMV at 1..64 tokens")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--gemv-tokens", default="1,8,16,32,64",
+                    help="--mode gemv: comma-separated token counts (the roofline needs 1)")
     return ap.parse_args()
 
 
@@ -207,6 +233,21 @@ def copy_calibration(args):
           flush=True)
 
 
+def _per_call_ms(fn, reps):
+    """Mean milliseconds of one fn() call: a HIP event pair on the current
+    stream around each call, so host-side pauses between calls (which leave
+    the GPU idle) are not counted in a per-kernel figure."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
 def _events_ms(fn, reps):
     """Mean milliseconds of fn() over reps calls, HIP events on the current stream."""
     import torch
@@ -277,8 +318,8 @@ def ingest_bench(args):
     torch.cuda.synchronize()
     reps = max(1, args.steps)
     t_handoff = _events_ms(handoff, reps)
-    t_ingest = _events_ms(ingest_only, reps)
-    t_amax = _events_ms(amax_only, reps)
+    t_ingest = _per_call_ms(ingest_only, reps)
+    t_amax = _per_call_ms(amax_only, reps)
     t_append = _events_ms(bulk_append, max(1, reps // 4))
 
     n_tok = int(wl.seq_lens0.sum())
@@ -307,7 +348,9 @@ def ingest_bench(args):
                      "achieved": round(ingest_bytes / t_ingest / 1e6, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ingest_bytes / t_ingest / 1e6 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(t_ingest * 1e3, 2),
+                     "traffic": (counter_traffic(INGEST_COUNTER_TRAFFIC)
+                                 if fp8 and wl.name == "c4_headline" else None),
+                     "avg_launch_us": round(t_ingest * 1e3, 2),
                      "algorithmic_bytes_per_launch": ingest_bytes},
         "amax_kernel": {"GBps": round(2 * n_tok * row_bytes / 2 / t_amax / 1e6, 1),
                         "avg_launch_us": round(t_amax * 1e3, 2)} if fp8 else None,
@@ -444,8 +487,12 @@ def gemv_bench(args):
             del w
     torch.cuda.synchronize()
     points, largest = [], None
+    token_counts = [int(t) for t in args.gemv_tokens.split(",")]
+    if 1 not in token_counts or any(not 1 <= t <= 4096 for t in token_counts):
+        print("--gemv-tokens: counts in 1..4096, including 1", file=sys.stderr)
+        sys.exit(2)
     for fmt, name in ((kv.WQ_FP8_E4M3, "fp8"), (kv.WQ_INT4, "int4")):
-        for M in (1, 8, 16, 32, 64):
+        for M in token_counts:
             xs = [(torch.randn((M, k), generator=gen, device=dev)).to(torch.bfloat16)
                   for _, k in GEMV_LAYER]
             ys = [torch.zeros((M, n), dtype=torch.float32, device=dev) for n, _ in GEMV_LAYER]
@@ -467,16 +514,18 @@ def gemv_bench(args):
             if name == "int4" and M == 1:
                 n, k, p, s = mats[fmt][1]                 # the largest matrix alone
                 x1, y1 = xs[1], ys[1]
-                t1 = _events_ms(lambda: kv.wq_gemv(x1, p, s, y1, n, fmt), max(1, args.steps))
+                t1 = _per_call_ms(lambda: kv.wq_gemv(x1, p, s, y1, n, fmt), max(1, args.steps))
                 b1 = p.numel() + s.numel() * 4 + k * 2 + 2 * n * 4
                 largest = {"bound": "hbm", "kernel": f"wq_gemv_kernel<INT4> {n}x{k}, 1 token",
                            "achieved": round(b1 / t1 / 1e6, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(b1 / t1 / 1e6 / HBM_PEAK_GBS, 4),
-                           "traffic": None, "avg_launch_us": round(t1 * 1e3, 2),
+                           "traffic": counter_traffic(GEMV_COUNTER_TRAFFIC)
+                           if (n, k) == (28672, 8192) else None,
+                           "avg_launch_us": round(t1 * 1e3, 2),
                            "algorithmic_bytes_per_launch": b1}
     sp = {M: round(next(p["tokens_per_s"] for p in points if p["weights"] == "int4" and p["tokens"] == M)
                    / next(p["tokens_per_s"] for p in points if p["weights"] == "fp8" and p["tokens"] == M), 3)
-          for M in (1, 8, 16, 32, 64)}
+          for M in token_counts}
     res = {
         "metric": "weight-only decode GEMV over one layer's weights: tokens/s, INT4 vs FP8",
         "mode": "gemv", "value": next(p["tokens_per_s"] for p in points
