@@ -73,10 +73,13 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const uint16_t* __restrict
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t bits = (raw[c][i / 2] >> (16 * (i % 2))) & 0xFFFFu;
-                // round-to-odd quotient, then half-to-even to an integer: exact (24 >= 4 + 2)
+                // round-to-odd quotient, then half-to-even to an integer: exact (24 >= 4 + 2);
+                // |w / s| <= amax / fp32(amax / 7) < 7.5, so -8 never occurs and the clamp
+                // to [-7, 7] changes nothing
                 const float qf = rintf(div_round_odd(bf16_bits_to_float(bits), s));
-                const int q = static_cast<int>(fminf(fmaxf(qf, -8.0f), 7.0f));
-                word |= (static_cast<uint32_t>(q) & 0xFu) << (4 * i);
+                const float qc = fminf(fmaxf(qf, -7.0f), 7.0f);
+                const uint32_t nib = (qc < 0.0f ? 8u : 0u) | static_cast<uint32_t>(fabsf(qc));
+                word |= nib << (8 * (i % 4) + 4 * (i / 4));       // sign-magnitude nibble
             }
             d[c] = word;
         }
@@ -103,24 +106,23 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 // GEMV
 // ---------------------------------------------------------------------------
-// 8 signed nibbles (little-endian) -> 8 bf16, exactly. The sign extension is
-// written as shifts of a signed int (the bitfield-extract builtin's result
-// was converted as unsigned by this compiler).
-__device__ __forceinline__ int nibble_s(uint32_t w, int i) {
-    return static_cast<int32_t>(w << (28 - 4 * i)) >> 28;
-}
-
+// One packed dword of 8 sign-magnitude nibbles (value i in byte i % 4, low
+// nibble for i < 4) -> 8 bf16, exactly. A byte permute looks up the e4m3
+// codes of the magnitudes 0..7 (8-entry table in two registers), the sign
+// bits are ORed into bit 7, and the hardware decode turns the e4m3 codes into
+// bf16 (integers up to 7 are exact in both). About 1.5 VALU instructions per
+// weight, against 2.5 for bit-field extract, int-to-float and pack.
 __device__ __forceinline__ bf16x8 int4x8_to_bf16(uint32_t w) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-        const float a = static_cast<float>(nibble_s(w, i));
-        const float b = static_cast<float>(nibble_s(w, i + 1));
-        const bf16x2 p = __builtin_convertvector((f32x2{a, b}), bf16x2);
-        r[i] = p[0];
-        r[i + 1] = p[1];
-    }
-    return r;
+    constexpr uint32_t kCodes0123 = 0x44403800u;     // e4m3 of 3, 2, 1, 0 (bytes 3..0)
+    constexpr uint32_t kCodes4567 = 0x4E4C4A48u;     // e4m3 of 7, 6, 5, 4
+    const uint32_t lo = __builtin_amdgcn_perm(kCodes4567, kCodes0123, w & 0x07070707u) |
+                        ((w << 4) & 0x80808080u);    // values 0..3
+    const uint32_t hi = __builtin_amdgcn_perm(kCodes4567, kCodes0123, (w >> 4) & 0x07070707u) |
+                        (w & 0x80808080u);           // values 4..7
+    bf16x2 p0, p1, p2, p3;
+    decode4_bf16(lo, p0, p1);
+    decode4_bf16(hi, p2, p3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo_w, uint32_t hi_w) {

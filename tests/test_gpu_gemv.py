@@ -35,7 +35,7 @@ def _index_maps(n, k, fmt):
     b = nt * (k // G) + g
     lane = 16 * j + r
     if fmt == 0:
-        return 1024 * b + 16 * lane + 4 * c + i // 2, i % 2
+        return 1024 * b + 16 * lane + 4 * c + i % 4, i // 4
     return 2048 * b + 1024 * (c // 2) + 16 * lane + 8 * (c % 2) + i, None
 
 
@@ -44,7 +44,8 @@ def _unpack(packed, n, k, fmt):
     byte = packed[off]
     if fmt == 0:
         v = (byte >> (4 * nib)) & 0xF
-        return np.where(v >= 8, v - 16, v).astype(np.int8)
+        assert not np.any(v == 8), "negative zero code"
+        return np.where(v >= 8, -(v & 7), v).astype(np.int8)
     return byte
 
 

@@ -106,3 +106,23 @@ def test_one_hot_activation_reads_a_column(fmt):
     x[0, 200] = 0x3F80                                      # 1.0
     y = weights.gemv(x, wd)
     assert np.array_equal(y[0], wd[:, 200])
+
+
+def test_int4_codes_never_reach_minus_8():
+    """|w / s| <= amax / fp32(amax / 7) < 7.5 for every finite bf16 amax, so
+    the INT4 codes stay in [-7, 7] and the fourth bit is free for a sign
+    (the packed format is sign-magnitude). Exhaustive over the amax patterns;
+    then groups whose most negative value is -amax, quantized by the oracle."""
+    a_bits = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)     # every positive finite
+    amax = e4m3.bf16_bits_to_f64(a_bits)
+    s = (amax / 7.0).astype(np.float32).astype(np.float64)
+    ratio = [Fraction(float(a)) / Fraction(float(t)) for a, t in zip(amax[::97], s[::97])]
+    assert max(ratio) < Fraction(15, 2)
+    assert np.all(amax / s < 7.5 * (1 - 1e-12))
+    rng = np.random.default_rng(7)
+    pick = a_bits[rng.choice(a_bits.size, size=4 * 64, replace=False)]
+    w = _rand_w(rng, 4 * 64, G)
+    w[:, 0] = pick | 0x8000                                     # -amax somewhere in each group
+    w[:, 1:] = np.where((w[:, 1:] & 0x7FFF) > pick[:, None], w[:, 1:] & 0x8000, w[:, 1:])
+    q, _ = weights.quantize_int4(w)
+    assert q.min() == -7 and q.max() <= 7
