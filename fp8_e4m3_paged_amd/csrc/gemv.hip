@@ -11,15 +11,20 @@
 //    16-byte chunk(s) at 16 l (+ 1 KiB) holding exactly its A operands of the
 //    four 16x16x32 bf16 MFMAs over the group (row l % 16, inputs
 //    32 c + 8 (l / 16) + 0..7 of slice c), so each load is a coalesced 1 KiB;
-//  * integer codes become bf16 exactly (|q| <= 8) and e4m3 codes through the
-//    exact hardware decode; the MFMA sums one group in fp32 and the group's
-//    row scale multiplies that partial (the products themselves are exact);
+//  * integer codes (sign-magnitude, |q| <= 7) become bf16 exactly through an
+//    e4m3 lookup and the hardware decode, e4m3 codes through the decode
+//    alone; the MFMA sums one group in fp32 and the group's row scale
+//    multiplies that partial (the products themselves are exact);
 //  * grid: a workgroup = 4 wavefronts = 4 consecutive 16-row tiles over one
-//    range of input groups; the activations of that range pass through LDS
-//    in double-buffered chunks loaded by the whole workgroup, and each
-//    chunk's codes are loaded into registers one chunk ahead; ranges are
-//    split so the grid fills the chip, and partial sums are added to y with
-//    hardware fp32 atomics (y must hold zeros or a bias on entry).
+//    range of input groups; ranges are split so the grid fills the chip, and
+//    partial sums are added to y with hardware fp32 atomics (y must hold
+//    zeros or a bias on entry);
+//  * 1 .. 8 tokens (wq_gemv_small_kernel): the range's activations are staged
+//    in LDS once, then each wavefront streams its codes through a 3-deep
+//    register pipeline with no further barrier;
+//  * 9 .. 64 tokens (wq_gemv_kernel): the activations pass through LDS in
+//    double-buffered chunks loaded by the whole workgroup, each chunk's codes
+//    one chunk ahead in registers.
 #include <algorithm>
 
 #include "kv_device.h"
@@ -303,6 +308,118 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// GEMV for 1 .. 8 tokens: no per-chunk barrier. The workgroup stages the
+// activations of its whole input range (real rows only; m_rows x ng x 256 B
+// of dynamic LDS) once, then every wavefront streams its tile's codes and
+// scales through a 3-deep register pipeline while it reads its B operands
+// from LDS (a separate counter from the code loads, so the waits for the
+// codes never wait on activations). Columns of the B operand past the real
+// tokens read row 0: their output columns are discarded, so no zero rows are
+// stored.
+// ---------------------------------------------------------------------------
+constexpr int kSmallMaxRows = 8;
+constexpr int kSmallMaxGroups = 16;     // 8 rows x 16 groups: 33 KiB of LDS
+
+template <bool INT4>
+struct GroupTile {
+    u32x4 w[INT4 ? 1 : 2];
+    f32x4 s;
+};
+
+template <bool INT4>
+__global__ __launch_bounds__(kGemvWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
+                          const uint8_t* __restrict__ packed, const float* __restrict__ scales,
+                          int32_t n, int32_t k, float* __restrict__ y, int32_t groups_per_wg) {
+    extern __shared__ uint16_t xs_dyn[];
+    constexpr int BLK = INT4 ? 1024 : 2048;                // code bytes per (tile, group)
+    const int groups = k / kWGroup;
+    const int n_tiles = n / 16;
+    const int n_groups_rows = (n_tiles + kGemvWaves - 1) / kGemvWaves;
+    const int wg_row = blockIdx.x % n_groups_rows;
+    const int wg_k = blockIdx.x / n_groups_rows;
+    const int wave = threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
+    const int nt = wg_row * kGemvWaves + wave;
+    const int g0 = wg_k * groups_per_wg;
+    const int ng = min(groups, g0 + groups_per_wg) - g0;  // 1 .. kSmallMaxGroups
+    const int row_h = ng * kWGroup + 8;                    // halves per LDS row (16-byte pad)
+
+    // activations of rows 0 .. m_rows - 1, inputs 128 g0 .. 128 (g0 + ng): 16-byte pieces
+    const int per_row = ng * 16;
+    for (int p = threadIdx.x; p < m_rows * per_row; p += kGemvWaves * 64) {
+        const int row = p / per_row, c8 = p % per_row;
+        *reinterpret_cast<u32x4*>(xs_dyn + row * row_h + 8 * c8) = *reinterpret_cast<const u32x4*>(
+            x + static_cast<size_t>(row) * k + static_cast<size_t>(kWGroup) * g0 + 8 * c8);
+    }
+    __syncthreads();
+    if (nt >= n_tiles) return;                             // no barrier below
+
+    const int col = lane % 16;                             // B: token; C: column
+    const int jg = lane / 16;                              // B: input sub-slice; C: row group of 4
+    const uint16_t* xb_base = xs_dyn + (col < m_rows ? col : 0) * row_h + 8 * jg;
+    const size_t blk0 = static_cast<size_t>(nt) * groups + g0;
+    const uint8_t* cbase = packed + blk0 * BLK + 16 * lane;
+    const float* sbase = scales + blk0 * 16 + 4 * jg;
+
+    const auto issue = [&](GroupTile<INT4>& t, int i) __attribute__((always_inline)) {
+        const uint8_t* cp = cbase + static_cast<size_t>(i) * BLK;
+        t.w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp));
+        if constexpr (!INT4) t.w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp + 1024));
+        t.s = *reinterpret_cast<const f32x4*>(sbase + static_cast<size_t>(i) * 16);
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const auto proc = [&](const GroupTile<INT4>& t, int i) __attribute__((always_inline)) {
+        bf16x8 A[4];
+        if constexpr (INT4) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) A[c] = int4x8_to_bf16(t.w[0][c]);
+        } else {
+            A[0] = e4m3x8_to_bf16(t.w[0][0], t.w[0][1]);
+            A[1] = e4m3x8_to_bf16(t.w[0][2], t.w[0][3]);
+            A[2] = e4m3x8_to_bf16(t.w[1][0], t.w[1][1]);
+            A[3] = e4m3x8_to_bf16(t.w[1][2], t.w[1][3]);
+        }
+        f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 xb = *reinterpret_cast<const u32x4*>(xb_base + kWGroup * i + 32 * c);
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[c], __builtin_bit_cast(bf16x8, xb),
+                                                           part, 0, 0, 0);
+        }
+        acc += t.s * part;                 // rows 4 jg + r of the tile carry scale s[r]
+    };
+    // 3-deep pipeline: the steady-state loop issues unconditionally (i + 5 < ng);
+    // the last 1 .. 5 groups are handled with uniform conditions.
+    GroupTile<INT4> t0, t1, t2;
+    issue(t0, 0);
+    if (ng > 1) issue(t1, 1);
+    if (ng > 2) issue(t2, 2);
+    int i = 0;
+    for (; i + 5 < ng; i += 3) {
+        proc(t0, i);
+        issue(t0, i + 3);
+        proc(t1, i + 1);
+        issue(t1, i + 4);
+        proc(t2, i + 2);
+        issue(t2, i + 5);
+    }
+    proc(t0, i);
+    if (i + 3 < ng) issue(t0, i + 3);
+    if (i + 1 < ng) proc(t1, i + 1);
+    if (i + 4 < ng) issue(t1, i + 4);
+    if (i + 2 < ng) proc(t2, i + 2);
+    if (i + 3 < ng) proc(t0, i + 3);
+    if (i + 4 < ng) proc(t1, i + 4);
+
+    if (col < m_rows) {
+        float* yr = y + static_cast<size_t>(col) * n + 16 * nt + 4 * jg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(yr + r, acc[r]);
+    }
+}
+
 size_t wq_packed_bytes(int32_t n, int32_t k, bool int4) {
     return static_cast<size_t>(n) * k / (int4 ? 2 : 1);
 }
@@ -334,6 +451,22 @@ hipError_t launch_wq_gemv(bool int4, const uint16_t* x, int32_t m_rows, const ui
     splits = std::min<int64_t>(splits, std::max(1, groups / 2));
     const int per = static_cast<int>((groups + splits - 1) / splits);
     splits = (groups + per - 1) / per;
+    if (m_rows <= kSmallMaxRows) {
+        // at most kSmallMaxGroups input groups per range (the activations of a range
+        // are staged whole)
+        int64_t sp = std::max<int64_t>(splits, (groups + kSmallMaxGroups - 1) / kSmallMaxGroups);
+        const int per_s = static_cast<int>((groups + sp - 1) / sp);
+        sp = (groups + per_s - 1) / per_s;
+        const dim3 grid_s(static_cast<uint32_t>(row_groups * sp));
+        const size_t lds = static_cast<size_t>(m_rows) * (per_s * kWGroup + 8) * sizeof(uint16_t);
+        if (int4)
+            hipLaunchKernelGGL(wq_gemv_small_kernel<true>, grid_s, dim3(kGemvWaves * 64), lds, stream,
+                               x, m_rows, packed, scales, n, k, y, per_s);
+        else
+            hipLaunchKernelGGL(wq_gemv_small_kernel<false>, grid_s, dim3(kGemvWaves * 64), lds, stream,
+                               x, m_rows, packed, scales, n, k, y, per_s);
+        return hipGetLastError();
+    }
     const dim3 grid(static_cast<uint32_t>(row_groups * splits));
 #define KVFP8_GEMV(I4, MTV)                                                                     \
     hipLaunchKernelGGL((wq_gemv_kernel<I4, MTV>), grid, dim3(kGemvWaves * 64), 0, stream, x,    \

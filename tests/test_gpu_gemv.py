@@ -83,10 +83,13 @@ def test_pack_codes_and_scales_bit_exact(kv, fmt, n, k):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("m", [1, 5, 16, 17, 33, 64, 70])
-def test_gemv_against_oracle(kv, fmt, m):
-    n, k = 320, 1024
-    rng = np.random.default_rng(100 + m + fmt)
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 16, 17, 33, 64, 70])
+@pytest.mark.parametrize("n,k", [(320, 1024), (336, 1152)])
+def test_gemv_against_oracle(kv, fmt, m, n, k):
+    """1 .. 8 tokens take the small-batch kernel, more the chunked one; 336 x
+    1152 has a last group of 64 rows with one tile and input ranges of
+    unequal length."""
+    rng = np.random.default_rng(100 + m + fmt + n)
     wb = _weights(rng, n, k)
     packed, scales = _pack(kv, wb, fmt)
     q_o, s_o = weights.quantize_int4(wb) if fmt == 0 else weights.quantize_fp8(wb)
