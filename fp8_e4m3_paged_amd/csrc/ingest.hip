@@ -18,6 +18,7 @@
 //    quotient x / s; a wavefront whose head scale and values allow it
 //    (almost always) forms them from the reciprocal and a Newton step
 //    instead of an IEEE division, which made the writer ALU-bound.
+#include <algorithm>
 #include <type_traits>
 
 #include "kv_device.h"
@@ -190,16 +191,16 @@ __device__ __forceinline__ bool wave_recip_range(const u32x4 (&w)[4]) {
     return __builtin_amdgcn_ballot_w64(!bf16x2_recip_range(m)) == 0;
 }
 
+// Page j of request b (one workgroup; each wavefront takes KV heads wave,
+// wave + 4, ... and uses only its own LDS block).
 template <bool FP8>
-__global__ __launch_bounds__(kIngestWaves * 64) void ingest_kernel(
-    const uint16_t* __restrict__ k_rows, const uint16_t* __restrict__ v_rows,
+__device__ __forceinline__ void ingest_page(
+    int b, int j, const uint16_t* __restrict__ k_rows, const uint16_t* __restrict__ v_rows,
     int64_t n_rows, const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_lens,
-    int32_t max_seq_len, int32_t max_pages, const int32_t* __restrict__ block_table,
-    int32_t bt_stride, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    int32_t max_seq_len, const int32_t* __restrict__ block_table, int32_t bt_stride,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int32_t num_pages, int32_t hkv,
-    const uint8_t* __restrict__ abort) {
-    const int b = blockIdx.x / max_pages;
-    const int j = blockIdx.x % max_pages;
+    const uint8_t* __restrict__ abort, uint16_t (*sx)[kVRowHalves]) {
     const int L = seq_lens[b];
     if (abort != nullptr && abort[b] != 0) return;
     if (L <= 0 || L > max_seq_len || (static_cast<int64_t>(L) + kPage - 1) / kPage > bt_stride)
@@ -219,8 +220,6 @@ __global__ __launch_bounds__(kIngestWaves * 64) void ingest_kernel(
     const int jg = lane / 16;         // K: 32-dim group; V: group of 4 tokens
     constexpr int T = FP8 ? kTileFp8 : kTileBf16;
     constexpr int NCH = T / 1024;     // 16-byte chunks per lane per tile
-    __shared__ uint16_t sx_all[kIngestWaves][kPage][kVRowHalves];
-    uint16_t (*sx)[kVRowHalves] = sx_all[wave];
 
     const uint16_t* kbase = k_rows + row0 * row_elems;
     const uint16_t* vbase = v_rows + row0 * row_elems;
@@ -340,6 +339,29 @@ __global__ __launch_bounds__(kIngestWaves * 64) void ingest_kernel(
     }
 }
 
+// Grid-stride over the (request, page) items, so any batch x max_pages fits
+// a launch (most items of short prompts exit at once); the LDS blocks are
+// per wavefront and every head ends with its reads complete, so items follow
+// one another without a workgroup barrier.
+constexpr int64_t kIngestMaxWgs = 65536;
+
+template <bool FP8>
+__global__ __launch_bounds__(kIngestWaves * 64) void ingest_kernel(
+    const uint16_t* __restrict__ k_rows, const uint16_t* __restrict__ v_rows,
+    int64_t n_rows, const int32_t* __restrict__ row_start, const int32_t* __restrict__ seq_lens,
+    int32_t batch, int32_t max_seq_len, int32_t max_pages, const int32_t* __restrict__ block_table,
+    int32_t bt_stride, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int32_t num_pages, int32_t hkv,
+    const uint8_t* __restrict__ abort) {
+    __shared__ uint16_t sx_all[kIngestWaves][kPage][kVRowHalves];
+    const int64_t n_items = static_cast<int64_t>(batch) * max_pages;
+    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x)
+        ingest_page<FP8>(static_cast<int>(item / max_pages), static_cast<int>(item % max_pages),
+                         k_rows, v_rows, n_rows, row_start, seq_lens, max_seq_len, block_table,
+                         bt_stride, k_scale, v_scale, k_pool, v_pool, num_pages, hkv, abort,
+                         sx_all[threadIdx.x / 64]);
+}
+
 hipError_t launch_amax(const uint16_t* x, int64_t n_rows, int32_t hkv, float* amax_inout,
                        hipStream_t stream) {
     const int64_t n_vec = n_rows * hkv * (kDim / 8);
@@ -368,15 +390,16 @@ hipError_t launch_ingest(bool fp8, const uint16_t* k_rows, const uint16_t* v_row
                          hipStream_t stream) {
     const int32_t max_pages = (max_seq_len + kPage - 1) / kPage;
     if (batch == 0 || max_pages == 0) return hipSuccess;
-    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(batch) * max_pages));
+    const dim3 grid(static_cast<uint32_t>(
+        std::min<int64_t>(static_cast<int64_t>(batch) * max_pages, kIngestMaxWgs)));
     if (fp8) {
         hipLaunchKernelGGL(ingest_kernel<true>, grid, dim3(kIngestWaves * 64), 0, stream, k_rows,
-                           v_rows, n_rows, row_start, seq_lens, max_seq_len, max_pages, block_table,
+                           v_rows, n_rows, row_start, seq_lens, batch, max_seq_len, max_pages, block_table,
                            bt_stride, k_scale, v_scale, static_cast<uint8_t*>(k_pool),
                            static_cast<uint8_t*>(v_pool), num_pages, num_kv_heads, abort);
     } else {
         hipLaunchKernelGGL(ingest_kernel<false>, grid, dim3(kIngestWaves * 64), 0, stream, k_rows,
-                           v_rows, n_rows, row_start, seq_lens, max_seq_len, max_pages, block_table,
+                           v_rows, n_rows, row_start, seq_lens, batch, max_seq_len, max_pages, block_table,
                            bt_stride, nullptr, nullptr, static_cast<uint8_t*>(k_pool),
                            static_cast<uint8_t*>(v_pool), num_pages, num_kv_heads, abort);
     }

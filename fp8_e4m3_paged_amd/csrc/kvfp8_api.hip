@@ -15,6 +15,12 @@ inline bool misaligned(const void* p, uintptr_t a) {
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_LAUNCH; }
 
+// A launch holds at most 2^32 - 1 work-items; sizes that would need more are
+// refused (KV_ERR_SHAPE) before anything is enqueued.
+inline bool grid_fits(int64_t workgroups, int64_t threads) {
+    return workgroups <= 0xFFFFFFFFLL / threads;
+}
+
 int check_append_common(const void* k_new, const void* v_new, const int32_t* tok_seq,
                         const int32_t* tok_pos, int32_t n_tok, const int32_t* block_table,
                         int32_t bt_stride, int32_t batch, const void* k_pool, const void* v_pool,
@@ -23,6 +29,7 @@ int check_append_common(const void* k_new, const void* v_new, const int32_t* tok
     if (n_tok < 0 || bt_stride < 0 || batch < 0 || num_pages < 0 || num_kv_heads <= 0)
         return KV_ERR_SHAPE;
     if (head_dim != KV_HEAD_DIM || page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
+    if (!grid_fits(n_tok, 256)) return KV_ERR_SHAPE;     // one row of workgroups per token
     if (n_tok == 0) return KV_OK;
     if (!k_new || !v_new || !tok_seq || !tok_pos || !block_table || !k_pool || !v_pool)
         return KV_ERR_NULL;
@@ -78,6 +85,13 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
     const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
                                                           partition_tokens);
     if (pt <= 0) return KV_ERR_UNSUPPORTED;
+    const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
+    if (parts64 > KV_MAX_PARTITIONS) return KV_ERR_UNSUPPORTED;
+    // shared-mode grid: one workgroup of up to 8 wavefronts per (partition,
+    // request, KV head); the reduce: one of 512 threads per (request, query head)
+    if (!grid_fits(parts64 * batch * num_kv_heads, 512)) return KV_ERR_SHAPE;
+    if (parts64 > 1 && !grid_fits(static_cast<int64_t>(batch) * num_q_heads, 512))
+        return KV_ERR_SHAPE;
     if (batch == 0) return KV_OK;
     const bool fp8 = cache_dtype == KV_CACHE_FP8_E4M3;
     if (!q || !out || !seq_lens || !block_table || !k_pool || !v_pool) return KV_ERR_NULL;
@@ -88,11 +102,7 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
         misaligned(v_pool, 16) || misaligned(seq_lens, 4) || misaligned(block_table, 4) ||
         (k_scale && misaligned(k_scale, 4)) || (v_scale && misaligned(v_scale, 4)))
         return KV_ERR_ALIGN;
-    const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
-    if (parts64 > KV_MAX_PARTITIONS) return KV_ERR_UNSUPPORTED;
     const int32_t parts = static_cast<int32_t>(parts64);
-    const int64_t blocks = parts64 * batch * num_kv_heads;
-    if (blocks > 0x7FFFFFFFLL) return KV_ERR_SHAPE;
     const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
                                                           head_dim, max_seq_len, pt);
     if (parts > 1) {
@@ -153,6 +163,7 @@ int kv_verify_tags(const uint32_t* pool_tags, int32_t num_pages, const int32_t* 
                    int32_t batch, int32_t page_size, uint8_t* abort_out, void* stream) {
     if (batch < 0 || num_pages < 0 || bt_stride < 0) return KV_ERR_SHAPE;
     if (page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
+    if (!grid_fits(batch, 1024)) return KV_ERR_SHAPE;     // one 1024-thread workgroup per request
     if (batch == 0) return KV_OK;
     if (!block_table || !expected_tags || !seq_lens || !abort_out) return KV_ERR_NULL;
     if (!pool_tags && num_pages > 0) return KV_ERR_NULL;
@@ -286,8 +297,6 @@ int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
         return KV_ERR_SHAPE;
     if (head_dim != KV_HEAD_DIM || page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
     if (cache_dtype != KV_CACHE_FP8_E4M3 && cache_dtype != KV_CACHE_BF16) return KV_ERR_UNSUPPORTED;
-    const int64_t max_pages = (static_cast<int64_t>(max_seq_len) + KV_PAGE_SIZE - 1) / KV_PAGE_SIZE;
-    if (max_pages * batch > 0x7FFFFFFFLL) return KV_ERR_SHAPE;
     if (batch == 0 || max_seq_len == 0) return KV_OK;
     const bool fp8 = cache_dtype == KV_CACHE_FP8_E4M3;
     if (!row_start || !seq_lens || !block_table || !k_pool || !v_pool) return KV_ERR_NULL;
@@ -314,6 +323,8 @@ int wq_quantize_pack(const void* w, int32_t n, int32_t k, int32_t format, void* 
     if (n < 0 || k < 0) return KV_ERR_SHAPE;
     if (n % 16 || k % 128) return KV_ERR_UNSUPPORTED;
     if (format != WQ_INT4 && format != WQ_FP8_E4M3) return KV_ERR_UNSUPPORTED;
+    // one wavefront per (16-row tile, 128-input group), 4 per workgroup
+    if (!grid_fits((static_cast<int64_t>(n / 16) * (k / 128) + 3) / 4, 256)) return KV_ERR_SHAPE;
     if (n == 0 || k == 0) return KV_OK;
     if (!w || !packed || !scales) return KV_ERR_NULL;
     if (misaligned(w, 16) || misaligned(packed, 16) || misaligned(scales, 16)) return KV_ERR_ALIGN;
@@ -327,6 +338,8 @@ int wq_gemv(const void* x, int32_t m, const void* packed, const float* scales, i
     if (m < 0 || n < 0 || k < 0) return KV_ERR_SHAPE;
     if (n % 16 || k % 128) return KV_ERR_UNSUPPORTED;
     if (format != WQ_INT4 && format != WQ_FP8_E4M3) return KV_ERR_UNSUPPORTED;
+    // at most one workgroup per (64-row group, 128-input group)
+    if (!grid_fits(static_cast<int64_t>((n / 16 + 3) / 4) * (k / 128), 256)) return KV_ERR_SHAPE;
     if (m == 0 || n == 0 || k == 0) return KV_OK;
     if (!x || !packed || !scales || !y) return KV_ERR_NULL;
     if (misaligned(x, 16) || misaligned(packed, 16) || misaligned(scales, 16) || misaligned(y, 16))

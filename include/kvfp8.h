@@ -94,7 +94,8 @@ extern "C" {
 typedef enum {
     KV_OK = 0,
     KV_ERR_NULL = -1,        /* a required pointer is NULL                          */
-    KV_ERR_SHAPE = -2,       /* a size is negative or inconsistent                  */
+    KV_ERR_SHAPE = -2,       /* a size is negative or inconsistent, or so large that
+                                one launch would exceed 2^32 - 1 work-items        */
     KV_ERR_UNSUPPORTED = -3, /* head_dim/page_size/group size/partition not handled */
     KV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required             */
     KV_ERR_LAUNCH = -5,      /* HIP reported an error when enqueueing               */
@@ -126,8 +127,9 @@ typedef enum { KV_CACHE_FP8_E4M3 = 0, KV_CACHE_BF16 = 1 } kv_cache_dtype;
  * pool_tags [num_pages], block_table/expected_tags [batch][bt_stride],
  * seq_lens [batch]: read. abort_out uint8 [batch]: written.
  * Errors: KV_ERR_NULL (any pointer NULL while batch > 0), KV_ERR_SHAPE
- * (batch, num_pages or bt_stride negative), KV_ERR_UNSUPPORTED (page_size
- * != 16), KV_ERR_ALIGN. batch == 0 enqueues nothing.
+ * (batch, num_pages or bt_stride negative, or batch > 4,194,303: one
+ * 1024-thread workgroup per request), KV_ERR_UNSUPPORTED (page_size != 16),
+ * KV_ERR_ALIGN. batch == 0 enqueues nothing.
  */
 int kv_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
                    const int32_t* block_table, const uint32_t* expected_tags,
@@ -150,8 +152,9 @@ int kv_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
  * k_new, v_new: bf16 [n_tok][num_kv_heads][head_dim], read.
  * k_scale, v_scale: fp32 [num_kv_heads] of this layer, read.
  * k_pool, v_pool: this layer's FP8 pools (layout above), written at targets.
- * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED (head_dim != 128,
- * page_size != 16), KV_ERR_ALIGN. n_tok == 0 enqueues nothing.
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE (also n_tok > 16,777,215),
+ * KV_ERR_UNSUPPORTED (head_dim != 128, page_size != 16), KV_ERR_ALIGN.
+ * n_tok == 0 enqueues nothing.
  */
 int kv_append_quant(const void* k_new, const void* v_new,
                     const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok,
@@ -214,7 +217,9 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * [head_dim], fully written. k_scale/v_scale: fp32 [num_kv_heads] (may be
  * NULL for the BF16 cache). workspace: device memory of at least
  * paged_decode_attn_workspace_bytes(...) bytes (may be NULL when that is 0).
- * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED (also when
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE (also when partitions x batch x
+ * num_kv_heads exceeds 8,388,607, or, with more than one partition, batch x
+ * num_q_heads does), KV_ERR_UNSUPPORTED (also when
  * ceil(max_seq_len / partition_tokens) exceeds KV_MAX_PARTITIONS, or for a
  * negative or non-finite sm_scale),
  * KV_ERR_WORKSPACE, KV_ERR_ALIGN, KV_ERR_LAUNCH.
@@ -311,8 +316,10 @@ int kv_scales_from_amax(const float* amax, int32_t n, float* scale_out, void* st
  * i.e. the same codes kv_append_quant writes for those tokens, in whole tiles
  * with full 16-byte stores. Other requests and pages are not touched.
  * k_scale, v_scale: fp32 [num_kv_heads], positive normal (FP8; ignored and
- * may be NULL for BF16). cache_dtype selects the pool format. Errors:
- * KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ * may be NULL for BF16). cache_dtype selects the pool format. Any batch x
+ * ceil(max_seq_len / 16) is accepted (the kernel loops over the pages).
+ * Errors: KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_NULL, KV_ERR_ALIGN,
+ * KV_ERR_LAUNCH.
  */
 int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
                       const int32_t* row_start, const int32_t* seq_lens, int32_t batch,
@@ -357,7 +364,8 @@ size_t wq_packed_bytes(int32_t n, int32_t k, int32_t format);
 /*
  * Quantize bf16 weights w [n][k] (row-major, device) into packed codes and
  * scales (layouts above). Requires n % 16 == 0, k % 128 == 0. Errors:
- * KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ * KV_ERR_SHAPE (also (n / 16) x (k / 128) > 67,108,860), KV_ERR_UNSUPPORTED,
+ * KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_LAUNCH.
  */
 int wq_quantize_pack(const void* w, int32_t n, int32_t k, int32_t format, void* packed,
                      float* scales, void* stream);
@@ -367,8 +375,8 @@ int wq_quantize_pack(const void* w, int32_t n, int32_t k, int32_t format, void* 
  * [m][k] and packed weights (any m; 64 rows per launch). y must hold zeros or
  * a bias on entry: partial sums over ranges of inputs are added with fp32
  * atomics, so the last bits of y may differ between runs. All pointers
- * 16-byte aligned. Errors: KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_NULL,
- * KV_ERR_ALIGN, KV_ERR_LAUNCH.
+ * 16-byte aligned. Errors: KV_ERR_SHAPE (also ceil(n / 64) x (k / 128) >
+ * 16,777,215), KV_ERR_UNSUPPORTED, KV_ERR_NULL, KV_ERR_ALIGN, KV_ERR_LAUNCH.
  */
 int wq_gemv(const void* x, int32_t m, const void* packed, const float* scales, int32_t n,
             int32_t k, int32_t format, float* y, void* stream);

@@ -29,12 +29,37 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
 
 
+# Entry points that enqueue GPU work. The cases below pass fake device
+# addresses, so every one of them must be refused by validation; a call that
+# got through would launch a kernel on those addresses. On a host without a
+# GPU such a call returns KV_ERR_LAUNCH, which the proxy turns into a failure.
+LAUNCHING = {"kv_verify_tags", "kv_append_quant", "kv_append_bf16", "paged_decode_attn",
+             "paged_decode_attn_append", "kv_amax_accumulate", "kv_scales_from_amax",
+             "kv_ingest_prefill", "wq_quantize_pack", "wq_gemv"}
+
+
+class _NoLaunch:
+    def __init__(self, real):
+        self._real = real
+
+    def __getattr__(self, name):
+        fn = getattr(self._real, name)
+        if name not in LAUNCHING:
+            return fn
+
+        def checked(*args):
+            status = fn(*args)
+            assert status != LAUNCH, f"{name}{args}: passed validation and reached a launch"
+            return status
+        return checked
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
         pytest.fail("libkvfp8.so not built: run python -m fp8_e4m3_paged_amd.build")
     import fp8_e4m3_paged_amd as k
-    return k.load()
+    return _NoLaunch(k.load())
 
 
 def test_header_declares_the_entry_points():
@@ -184,7 +209,8 @@ def test_ingest_entry_points_reject_bad_arguments(lib):
     assert ingest_call(lib, page_size=32) == UNSUP
     assert ingest_call(lib, cache_dtype=3) == UNSUP
     assert ingest_call(lib, n_rows=-1) == SHAPE
-    assert ingest_call(lib, batch=1 << 20, max_seq_len=1 << 30) == SHAPE   # grid too large
+    assert ingest_call(lib, num_pages=-1) == SHAPE
+    assert ingest_call(lib, bt_stride=-3) == SHAPE
     assert ingest_call(lib, k_scale=None) == NULL                          # FP8 needs scales
     # BF16 takes no scales: NULL passes the pointer checks (stopped here by the alignment one)
     assert ingest_call(lib, cache_dtype=1, k_scale=None, v_scale=None, v_pool=A + 4) == ALIGN
@@ -243,3 +269,30 @@ def test_device_hash_twin_matches_host_on_cpu_torch():
         for i in range(4):
             b, t = int(seq[i]), int(pos[i])
             assert np.array_equal(got[i], wl.kv_bits(0, kind, b, t, t + 1)[0])
+
+
+def test_launch_size_limits_are_refused_before_anything_is_enqueued(lib):
+    """One launch holds at most 2^32 - 1 work-items: sizes that would need more
+    return KV_ERR_SHAPE. Each limit is probed just above (refused) and just
+    below, where the call must get past the size check and stop at a later
+    one (a NULL pointer or a small workspace), so nothing is ever launched."""
+    # tag check: one 1024-thread workgroup per request
+    assert verify(lib, batch=4_194_304) == SHAPE
+    assert verify(lib, batch=4_194_303, block_table=None) == NULL
+    # append: one row of 256-thread workgroups per token
+    assert append(lib, n_tok=16_777_216) == SHAPE
+    assert append(lib, n_tok=16_777_215, k_pool=None) == NULL
+    # attention: one workgroup (<= 512 threads) per (partition, request, KV head)
+    assert attn(lib, batch=1_048_577) == SHAPE                 # one partition, 8 KV heads
+    assert attn(lib, batch=1_048_575, q=None) == NULL
+    # ... and the reduce, one 512-thread workgroup per (request, query head)
+    assert attn(lib, batch=600_000, num_q_heads=16, num_kv_heads=1, max_seq_len=1024,
+                partition_tokens=512) == SHAPE
+    assert attn(lib, batch=500_000, num_q_heads=16, num_kv_heads=1, max_seq_len=1024,
+                partition_tokens=512, workspace_bytes=16) == WORKSPACE
+    # weight packing: one wavefront per (16-row tile, 128-input group)
+    assert lib.wq_quantize_pack(A, 16_777_216, 8192, 0, A, A, None) == SHAPE
+    assert lib.wq_quantize_pack(None, 16_777_216, 8064, 0, A, A, None) == NULL
+    # GEMV: at most one workgroup per (64-row group, 128-input group)
+    assert lib.wq_gemv(A, 1, A, A, 16_777_216, 8192, 0, A, None) == SHAPE
+    assert lib.wq_gemv(None, 1, A, A, 16_777_216, 8064, 0, A, None) == NULL

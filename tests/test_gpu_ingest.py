@@ -164,6 +164,18 @@ def test_ingest_whole_pool_bit_exact(kv, cache):
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_ingest_loops_over_more_pages_than_workgroups(kv, cache):
+    """max_seq_len = 131072 gives 12 x 8192 (request, page) items, more than
+    the 65,536 workgroups one launch uses, so workgroups take several items
+    (almost all past their prompt's end); the pools must be the same."""
+    c = _ingest_case(np.random.default_rng(23), cache)
+    gk, gv = _run_ingest(kv, c, cache, max_seq_len=131072)
+    wk, wv = _oracle_ingest(c, cache, max_seq_len=131072)
+    assert np.array_equal(gk, wk), f"{cache} K pool"
+    assert np.array_equal(gv, wv), f"{cache} V pool"
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
 def test_ingest_refusals(kv, cache):
     """Aborted requests, an out-of-pool page (skipped alone), rows outside the
     inputs and lengths over max_seq_len or beyond the table row write nothing."""
