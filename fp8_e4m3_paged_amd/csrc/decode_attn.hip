@@ -648,17 +648,22 @@ void attn_partition_kernel(
 // Wave-mode kernel for short partitions (<= 2048 tokens): every wavefront
 // works alone on whole partitions, so no wavefront's pipeline is starved by
 // sharing a short partition, and the grid is persistent. The (request,
-// partition, KV head) items that have work are numbered request by request,
-// KV head fastest (the 4 wavefronts of a workgroup then read neighbouring
-// tiles of the same pages); each workgroup first builds the per-request
-// prefix of partition counts in LDS, then wavefront w of the grid takes items
-// w, w + W, w + 2W, ... (W = all wavefronts of the grid), finding each item's
-// request by binary search. Aborted, empty or unmappable requests have no
-// items (the reduction writes their zeros), and no workgroup is launched
-// only to find it has nothing to do. Each item writes its partial straight
-// from registers; its page ids sit in two registers per lane (page k in lane
-// k % 64 of register k / 64) and are broadcast with readlane.
+// KV head, partition) items that have work are numbered request by request,
+// then KV head, then partition; each workgroup first builds the per-request
+// prefix of partition counts in LDS, then wavefront w of the W in the grid
+// takes the contiguous range of items [w I / W, (w + 1) I / W), finding each
+// item's request by binary search. Consecutive partitions of one (request,
+// KV head) in that range, up to kRunPages pages, are streamed as one run: one
+// register pipeline and one online softmax, so the pipeline fills and drains
+// once per run instead of once per partition. The run's partial goes to its
+// first partition's slot and the other slots are marked empty (max -inf, sum
+// 0), which the reduction weighs 0. Aborted, empty or unmappable requests
+// have no items (the reduction writes their zeros), and no workgroup is
+// launched only to find it has nothing to do. A run's page ids sit in three
+// registers per lane (page k in lane k % 64 of register k / 64) and are
+// broadcast with readlane.
 constexpr int kWaveModeMaxBatch = 4096;     // LDS: 2 * batch + 1 ints
+constexpr int kRunPages = 192;              // pages of one run (three id registers)
 
 template <bool FP8, bool APPEND>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -722,32 +727,43 @@ void attn_wave_kernel(
         }
         __syncthreads();
     }
+    // items (partitions with work) in request, KV head, partition order; each
+    // wavefront takes a contiguous range of about n_items / n_waves of them
     const int64_t n_items = static_cast<int64_t>(sm_pre[batch]) * hkv;
-    const int64_t w_stride = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int64_t n_waves = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int64_t w_id = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const int64_t it_end = n_items * (w_id + 1) / n_waves;
+    const int run_cap = max(1, kRunPages / (part_tokens / kPage));   // partitions per run
 
-    for (int64_t item = static_cast<int64_t>(blockIdx.x) * kWaves + wave; item < n_items;
-         item += w_stride) {
-        const int g = static_cast<int>(item % hkv);
-        const int pidx = static_cast<int>(item / hkv);
-        int lo = 0, hi = batch - 1;                            // last b with pre[b] <= pidx
+    for (int64_t it = n_items * w_id / n_waves; it < it_end;) {
+        int lo = 0, hi = batch - 1;                            // last b with pre[b] * hkv <= it
         while (lo < hi) {
             const int mid = (lo + hi + 1) / 2;
-            if (sm_pre[mid] <= pidx) lo = mid;
+            if (static_cast<int64_t>(sm_pre[mid]) * hkv <= it) lo = mid;
             else hi = mid - 1;
         }
         const int b = __builtin_amdgcn_readfirstlane(lo);
-        const int p = __builtin_amdgcn_readfirstlane(pidx - sm_pre[b]);
         const int L = __builtin_amdgcn_readfirstlane(sm_len[b]);
+        const int parts_b = (L + part_tokens - 1) / part_tokens;
+        const int local = static_cast<int>(it - static_cast<int64_t>(sm_pre[b]) * hkv);
+        const int g = __builtin_amdgcn_readfirstlane(local / parts_b);
+        const int p = __builtin_amdgcn_readfirstlane(local % parts_b);
+        // the run: partitions p .. p + n - 1 of (b, g), streamed as one sequence
+        const int n = static_cast<int>(
+            min(min(it_end - it, static_cast<int64_t>(parts_b - p)), static_cast<int64_t>(run_cap)));
+        it += n;
         const int t_begin = p * part_tokens;
-        const int t_end = min(L, t_begin + part_tokens);
+        const int t_end = min(L, (p + n) * part_tokens);
         const int pg0 = t_begin / kPage;
-        const int npg = (t_end + kPage - 1) / kPage - pg0;     // 1 .. 128
+        const int npg = (t_end + kPage - 1) / kPage - pg0;     // 1 .. kRunPages
 
         const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
         const int32_t id0 = lane < npg ? bt_row[lane] : 0;
         const int32_t id1 = lane + 64 < npg ? bt_row[lane + 64] : 0;
+        const int32_t id2 = lane + 128 < npg ? bt_row[lane + 128] : 0;
         const bool bad = __builtin_amdgcn_ballot_w64((id0 < 0 || id0 >= num_pages) ||
-                                                     (id1 < 0 || id1 >= num_pages)) != 0;
+                                                     (id1 < 0 || id1 >= num_pages) ||
+                                                     (id2 < 0 || id2 >= num_pages)) != 0;
 
         const size_t q_row = static_cast<size_t>(b) * hq + g * group;
         float m_run = -INFINITY;
@@ -759,8 +775,14 @@ void attn_wave_kernel(
             bf16x8 qop[4];
             load_q_operand(qop, q, q_row, group, col, jgrp);
             const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
+            // page_idx is wave-uniform: read the lane of each register and choose among
+            // the scalars (a choice among the registers themselves became a stack array)
             const auto tile_of = [&](int page_idx) __attribute__((always_inline)) -> size_t {
-                const int id = __builtin_amdgcn_readlane(page_idx < 64 ? id0 : id1, page_idx % 64);
+                const int l = page_idx % 64;
+                const int a = __builtin_amdgcn_readlane(id0, l);
+                const int c = __builtin_amdgcn_readlane(id1, l);
+                const int e = __builtin_amdgcn_readlane(id2, l);
+                const int id = page_idx < 64 ? a : (page_idx < 128 ? c : e);
                 return static_cast<size_t>(id) * hkv + g;
             };
             const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
@@ -771,6 +793,8 @@ void attn_wave_kernel(
         float l_tot = l_run + __shfl_xor(l_run, 16);
         l_tot += __shfl_xor(l_tot, 32);
         if (col < group) {
+            // the run's partial goes to its first partition's slot; the others of the
+            // run get weight 0 (max -inf, sum 0) and the reduction skips them
             const size_t pslot = (q_row + col) * n_parts + p;
             float* dst = part_acc + pslot * kDim + 4 * jgrp;
 #pragma unroll
@@ -778,6 +802,10 @@ void attn_wave_kernel(
             if (jgrp == 0) {
                 part_ml[2 * pslot] = m_run;
                 part_ml[2 * pslot + 1] = bad ? -1.f : l_tot;
+                for (int k = 1; k < n; ++k) {
+                    part_ml[2 * (pslot + k)] = -INFINITY;
+                    part_ml[2 * (pslot + k) + 1] = 0.f;
+                }
             }
         }
     }
@@ -879,7 +907,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int i = base + grp + kGroups * k;
-            if (i < np) num += wts[i] * v[k];
+            if (i < np && wts[i] > 0.f) num += wts[i] * v[k];   // slots of weight 0 may hold stale bytes
         }
         base += kGroups * kBatch;
         if (base >= np) break;
