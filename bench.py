@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # for the kernel sources they were taken on (sha256 prefix of decode_attn.hip
 # + kv_device.h). See profiles/attn_partition_kernel_c4_hbm_counters.md.
 COUNTER_TRAFFIC = {
-    "source_sha": "c72d71fc1d40911a",
+    "source_sha": "61fe4323571d5c88",
     "workload": "c4_headline",
     "read_bytes": 1.144e9,
     "write_bytes": 2.490e6,
@@ -52,8 +52,8 @@ COUNTER_TRAFFIC = {
 # roofline kernel (28672x8192, one token; profiles/wq_gemv_int4_1token.md).
 INGEST_COUNTER_TRAFFIC = {
     "sources": ("ingest.hip", "kv_device.h"),
-    "source_sha": "1b0956465e5e6822",
-    "read_bytes": 2.2815e9,
+    "source_sha": "1ad0cc34a39d10cc",
+    "read_bytes": 2.2816e9,
     "write_bytes": 1.1406e9,
 }
 GEMV_COUNTER_TRAFFIC = {
