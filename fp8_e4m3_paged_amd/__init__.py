@@ -153,6 +153,41 @@ def _check(fn, status):
         raise KvError(fn, status)
 
 
+def _tile_bytes(fp8):
+    """Bytes of one (page, KV head) tile: 16 tokens x 128 dims of e4m3 or bf16."""
+    return PAGE_SIZE * HEAD_DIM * (1 if fp8 else 2)
+
+
+def _check_pools(k_pool, v_pool, hkv, fp8):
+    """The kernels address whole tiles, so each pool must be [num_pages][num_kv_heads]
+    followed by exactly one tile per (page, head)."""
+    if k_pool.dim() < 2 or tuple(k_pool.shape) != tuple(v_pool.shape) or k_pool.shape[1] != hkv:
+        raise ValueError("k_pool / v_pool must be alike, [num_pages][num_kv_heads][...]")
+    per = k_pool.element_size()
+    for s in k_pool.shape[2:]:
+        per *= s
+    if per != _tile_bytes(fp8):
+        raise ValueError(f"pools must hold {_tile_bytes(fp8)} bytes per (page, KV head), "
+                         f"not {per}")
+
+
+def _check_requests(batch, seq_lens, block_table, abort=None):
+    if seq_lens.numel() != batch:
+        raise ValueError(f"seq_lens must hold {batch} lengths")
+    if block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError(f"block_table must be [{batch}][bt_stride]")
+    if abort is not None and abort.numel() != batch:
+        raise ValueError(f"abort must hold {batch} flags")
+
+
+def _check_scales(k_scale, v_scale, hkv, fp8):
+    if not fp8:
+        return
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t is not None and t.numel() != hkv:
+            raise ValueError(f"{name} must hold {hkv} scales (one per KV head)")
+
+
 def _dt():
     import torch
     return dict(
@@ -192,11 +227,15 @@ def _append(fp8, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, 
     if k_new.dim() != 3 or k_new.shape != v_new.shape or k_new.shape[0] != n_tok:
         raise ValueError("k_new / v_new must be [n_tok][num_kv_heads][head_dim]")
     hkv, hd = k_new.shape[1], k_new.shape[2]
-    if k_pool.shape[:2] != v_pool.shape[:2] or k_pool.shape[1] != hkv:
-        raise ValueError("pools must be [num_pages][num_kv_heads][...]")
+    _check_pools(k_pool, v_pool, hkv, fp8)
     num_pages = k_pool.shape[0]
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [batch][bt_stride]")
     if batch is None:
         batch = block_table.shape[0]
+    if block_table.shape[0] != batch or (abort is not None and abort.numel() != batch):
+        raise ValueError(f"block_table rows and abort must match batch {batch}")
+    _check_scales(k_scale, v_scale, hkv, fp8)
     lib = load()
     if fp8:
         st = lib.kv_append_quant(
@@ -256,11 +295,14 @@ def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens
         raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
     batch, hq, hd = q.shape
     hkv = k_pool.shape[1]
+    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
+    _check_pools(k_pool, v_pool, hkv, fp8)
+    _check_requests(batch, seq_lens, block_table, abort)
+    _check_scales(k_scale, v_scale, hkv, fp8)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _ptr(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
     st = load().paged_decode_attn(
         _ptr(q, "q", d["bf16"]), int(cache_dtype),
         _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
@@ -287,11 +329,14 @@ def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, 
     hkv = k_pool.shape[1]
     if k_new.shape != (batch, hkv, hd) or v_new.shape != k_new.shape:
         raise ValueError("k_new / v_new must be [batch][num_kv_heads][head_dim]")
+    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
+    _check_pools(k_pool, v_pool, hkv, fp8)
+    _check_requests(batch, seq_lens, block_table, abort)
+    _check_scales(k_scale, v_scale, hkv, fp8)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _ptr(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
     st = load().paged_decode_attn_append(
         _ptr(q, "q", d["bf16"]), _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
         int(cache_dtype), _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
@@ -372,12 +417,13 @@ def kv_ingest_prefill(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, 
     if k_rows.dim() != 3 or v_rows.shape != k_rows.shape:
         raise ValueError("k_rows / v_rows must be [rows][num_kv_heads][head_dim]")
     n_rows, hkv, hd = k_rows.shape
-    if k_pool.shape[:2] != v_pool.shape[:2] or k_pool.shape[1] != hkv:
-        raise ValueError("pools must be [num_pages][num_kv_heads][...]")
-    batch = seq_lens.numel()
-    if row_start.numel() != batch or block_table.shape[0] != batch:
-        raise ValueError("batch mismatch")
     fp8 = cache_dtype == KV_CACHE_FP8_E4M3
+    _check_pools(k_pool, v_pool, hkv, fp8)
+    batch = seq_lens.numel()
+    if row_start.numel() != batch:
+        raise ValueError("row_start must hold one row index per request")
+    _check_requests(batch, seq_lens, block_table, abort)
+    _check_scales(k_scale, v_scale, hkv, fp8)
     st = load().kv_ingest_prefill(
         _ptr(k_rows, "k_rows", d["bf16"]), _ptr(v_rows, "v_rows", d["bf16"]), n_rows,
         _ptr(row_start, "row_start", d["i32"]), _ptr(seq_lens, "seq_lens", d["i32"]), batch,
@@ -506,6 +552,10 @@ def wq_gemv(x, packed, scales, y, n, fmt=WQ_INT4, stream=None):
     if x.dim() != 2 or y.dim() != 2 or y.shape[0] != x.shape[0] or y.shape[1] != n:
         raise ValueError("x must be [m][k] and y [m][n]")
     m, k = x.shape
+    if packed.numel() * packed.element_size() < wq_packed_bytes(n, k, fmt):
+        raise ValueError("packed buffer smaller than the codes of an n x k matrix")
+    if scales.numel() != n * (k // 128):
+        raise ValueError("scales must hold n * k / 128 floats")
     st = load().wq_gemv(_ptr(x, "x", d["bf16"]), m, _ptr(packed, "packed"),
                         _ptr(scales, "scales", d["f32"]), int(n), k, int(fmt),
                         _ptr(y, "y", d["f32"]), _stream(stream))
