@@ -147,7 +147,10 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo_w, uint32_t hi_w) {
 #define KVFP8_GEMV_CG1 2          // groups per chunk with one m-tile
 #endif
 #ifndef KVFP8_GEMV_TARGET_WGS1
-#define KVFP8_GEMV_TARGET_WGS1 2048   // up to 8 tokens
+#define KVFP8_GEMV_TARGET_WGS1 2048   // up to 4 tokens
+#endif
+#ifndef KVFP8_GEMV_TARGET_WGS8
+#define KVFP8_GEMV_TARGET_WGS8 1024   // 5 .. 8 tokens
 #endif
 #ifndef KVFP8_GEMV_TARGET_WGS
 #define KVFP8_GEMV_TARGET_WGS 768     // 9 .. 16 tokens
@@ -445,7 +448,8 @@ hipError_t launch_wq_gemv(bool int4, const uint16_t* x, int32_t m_rows, const ui
     const int64_t row_groups = (n / 16 + kGemvWaves - 1) / kGemvWaves;
     // split the input groups so the grid holds ~4 workgroups per CU, at least 2 groups each
     const int mt = (m_rows + 15) / 16;
-    const int64_t target = m_rows <= 8 ? KVFP8_GEMV_TARGET_WGS1
+    const int64_t target = m_rows <= 4    ? KVFP8_GEMV_TARGET_WGS1
+                           : m_rows <= 8  ? KVFP8_GEMV_TARGET_WGS8
                            : m_rows <= 16 ? KVFP8_GEMV_TARGET_WGS : KVFP8_GEMV_TARGET_WGS3;
     int64_t splits = (target + row_groups - 1) / row_groups;
     splits = std::min<int64_t>(splits, std::max(1, groups / 2));
