@@ -19,10 +19,10 @@
 //    range of input groups; ranges are split so the grid fills the chip, and
 //    partial sums are added to y with hardware fp32 atomics (y must hold
 //    zeros or a bias on entry);
-//  * 1 .. 8 tokens (wq_gemv_small_kernel): the range's activations are staged
+//  * 1 .. 4 tokens (wq_gemv_small_kernel): the range's activations are staged
 //    in LDS once, then each wavefront streams its codes through a 3-deep
 //    register pipeline with no further barrier;
-//  * 9 .. 64 tokens (wq_gemv_kernel): the activations pass through LDS in
+//  * 5 .. 64 tokens (wq_gemv_kernel): the activations pass through LDS in
 //    double-buffered chunks loaded by the whole workgroup, each chunk's codes
 //    one chunk ahead in registers.
 #include <algorithm>
@@ -147,13 +147,10 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo_w, uint32_t hi_w) {
 #define KVFP8_GEMV_CG1 2          // groups per chunk with one m-tile
 #endif
 #ifndef KVFP8_GEMV_TARGET_WGS1
-#define KVFP8_GEMV_TARGET_WGS1 2048   // up to 4 tokens
-#endif
-#ifndef KVFP8_GEMV_TARGET_WGS8
-#define KVFP8_GEMV_TARGET_WGS8 1024   // 5 .. 8 tokens
+#define KVFP8_GEMV_TARGET_WGS1 2048   // up to 4 tokens (small-batch kernel)
 #endif
 #ifndef KVFP8_GEMV_TARGET_WGS
-#define KVFP8_GEMV_TARGET_WGS 768     // 9 .. 16 tokens
+#define KVFP8_GEMV_TARGET_WGS 768     // 5 .. 16 tokens
 #endif
 #ifndef KVFP8_GEMV_TARGET_WGS3
 #define KVFP8_GEMV_TARGET_WGS3 512    // more than 16 tokens
@@ -312,7 +309,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// GEMV for 1 .. 8 tokens: no per-chunk barrier. The workgroup stages the
+// GEMV for 1 .. 4 tokens: no per-chunk barrier. The workgroup stages the
 // activations of its whole input range (real rows only; m_rows x ng x 256 B
 // of dynamic LDS) once, then every wavefront streams its tile's codes and
 // scales through a 3-deep register pipeline while it reads its B operands
@@ -321,8 +318,15 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
 // tokens read row 0: their output columns are discarded, so no zero rows are
 // stored.
 // ---------------------------------------------------------------------------
-constexpr int kSmallMaxRows = 8;
-constexpr int kSmallMaxGroups = 16;     // 8 rows x 16 groups: 33 KiB of LDS
+// Up to 4 tokens (measured: from 5 tokens on the chunked kernel with 768
+// workgroups is faster, at 8 tokens 58 against 68 us per INT4 layer).
+#ifndef KVFP8_GEMV_SMALL_ROWS
+#define KVFP8_GEMV_SMALL_ROWS 4
+#endif
+constexpr int kSmallMaxRows = KVFP8_GEMV_SMALL_ROWS;
+// input groups per range whose activations are staged whole (4 rows x 16
+// groups: 16.5 KiB of LDS)
+__host__ __device__ constexpr int small_max_groups(int m_rows) { return m_rows <= 8 ? 16 : 8; }
 
 template <bool INT4>
 struct GroupTile {
@@ -346,7 +350,7 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
     const int lane = threadIdx.x % 64;
     const int nt = wg_row * kGemvWaves + wave;
     const int g0 = wg_k * groups_per_wg;
-    const int ng = min(groups, g0 + groups_per_wg) - g0;  // 1 .. kSmallMaxGroups
+    const int ng = min(groups, g0 + groups_per_wg) - g0;  // 1 .. small_max_groups(m_rows)
     const int row_h = ng * kWGroup + 8;                    // halves per LDS row (16-byte pad)
 
     // activations of rows 0 .. m_rows - 1, inputs 128 g0 .. 128 (g0 + ng): 16-byte pieces
@@ -448,17 +452,17 @@ hipError_t launch_wq_gemv(bool int4, const uint16_t* x, int32_t m_rows, const ui
     const int64_t row_groups = (n / 16 + kGemvWaves - 1) / kGemvWaves;
     // split the input groups so the grid holds ~4 workgroups per CU, at least 2 groups each
     const int mt = (m_rows + 15) / 16;
-    const int64_t target = m_rows <= 4    ? KVFP8_GEMV_TARGET_WGS1
-                           : m_rows <= 8  ? KVFP8_GEMV_TARGET_WGS8
+    const int64_t target = m_rows <= kSmallMaxRows ? KVFP8_GEMV_TARGET_WGS1
                            : m_rows <= 16 ? KVFP8_GEMV_TARGET_WGS : KVFP8_GEMV_TARGET_WGS3;
     int64_t splits = (target + row_groups - 1) / row_groups;
     splits = std::min<int64_t>(splits, std::max(1, groups / 2));
     const int per = static_cast<int>((groups + splits - 1) / splits);
     splits = (groups + per - 1) / per;
     if (m_rows <= kSmallMaxRows) {
-        // at most kSmallMaxGroups input groups per range (the activations of a range
-        // are staged whole)
-        int64_t sp = std::max<int64_t>(splits, (groups + kSmallMaxGroups - 1) / kSmallMaxGroups);
+        // at most small_max_groups input groups per range (the activations of a
+        // range are staged whole)
+        const int max_g = small_max_groups(m_rows);
+        int64_t sp = std::max<int64_t>(splits, (groups + max_g - 1) / max_g);
         const int per_s = static_cast<int>((groups + sp - 1) / sp);
         sp = (groups + per_s - 1) / per_s;
         const dim3 grid_s(static_cast<uint32_t>(row_groups * sp));

@@ -86,7 +86,7 @@ def test_pack_codes_and_scales_bit_exact(kv, fmt, n, k):
 @pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 16, 17, 33, 64, 70])
 @pytest.mark.parametrize("n,k", [(320, 1024), (336, 1152)])
 def test_gemv_against_oracle(kv, fmt, m, n, k):
-    """1 .. 8 tokens take the small-batch kernel, more the chunked one; 336 x
+    """1 .. 4 tokens take the small-batch kernel, more the chunked one; 336 x
     1152 has a last group of 64 rows with one tile and input ranges of
     unequal length."""
     rng = np.random.default_rng(100 + m + fmt + n)
