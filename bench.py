@@ -58,7 +58,7 @@ INGEST_COUNTER_TRAFFIC = {
 }
 GEMV_COUNTER_TRAFFIC = {
     "sources": ("gemv.hip", "kv_device.h"),
-    "source_sha": "677f68116962a2ca",
+    "source_sha": "9bb40110c444bfcb",
     "read_bytes": 1.24998e8,
     "write_bytes": 2.294e6,
 }
