@@ -38,9 +38,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
 # reads for a plain 1 GiB device copy (fetch x2.000, write x1.000); valid only
 # for the kernel sources they were taken on (sha256 prefix of decode_attn.hip
-# + kv_device.h). See profiles/attn_partition_kernel_c4_hbm_counters.md.
+# + kv_device.h + kv_launch.h). See profiles/attn_partition_kernel_c4_hbm_counters.md.
 COUNTER_TRAFFIC = {
-    "source_sha": "61fe4323571d5c88",
+    "source_sha": "d152b534b6a88752",
     "workload": "c4_headline",
     "read_bytes": 1.144e9,
     "write_bytes": 2.490e6,
@@ -65,7 +65,7 @@ GEMV_COUNTER_TRAFFIC = {
 }
 
 
-def kernel_source_sha(files=("decode_attn.hip", "kv_device.h")) -> str:
+def kernel_source_sha(files=("decode_attn.hip", "kv_device.h", "kv_launch.h")) -> str:
     import hashlib
     h = hashlib.sha256()
     for f in files:

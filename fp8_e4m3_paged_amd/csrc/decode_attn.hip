@@ -508,6 +508,57 @@ __device__ __forceinline__ bool request_ok(const int32_t* __restrict__ seq_lens,
            (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
 }
 
+// LDS floats of the wavefront merge: [NW][16] maxima, [NW][16] sums and
+// [NW][group][kAccStride] unnormalised outputs.
+__host__ __device__ constexpr int merge_floats(int nw, int group) {
+    return 2 * nw * 16 + nw * group * kAccStride;
+}
+
+// Combine the online-softmax states (m, l, acc) of the NW wavefronts that
+// shared one stretch of a (request, KV head) through LDS at `sm` (laid out as
+// merge_floats says). For every query head qh of the group and every 4 dims d,
+// store(qh, d, M, lt, o) receives the combined maximum M (log2 units), the
+// normaliser lt and the unnormalised output o (weighted by 2^(m_w - M)).
+// Starts with a barrier after the LDS writes; callers that write the area
+// again afterwards must synchronise first.
+template <int NW, typename Store>
+__device__ __forceinline__ void merge_waves(float* sm, int wave, int lane, int group, float m_run,
+                                            float l_tot, const f32x4 (&acc_o)[8], Store&& store) {
+    float* sm_m = sm;
+    float* sm_l = sm_m + NW * 16;
+    float* sm_acc = sm_l + NW * 16;
+    const int col = lane % 16;
+    const int jgrp = lane / 16;
+    if (jgrp == 0) {
+        sm_m[wave * 16 + col] = m_run;
+        sm_l[wave * 16 + col] = l_tot;
+    }
+    if (col < group) {
+        float* row = sm_acc + (wave * group + col) * kAccStride;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            *reinterpret_cast<f32x4*>(row + 16 * c + 4 * jgrp) = acc_o[c];
+    }
+    __syncthreads();
+    for (int it = wave * 64 + lane; it < group * (kDim / 4); it += NW * 64) {
+        const int qh = it / (kDim / 4);
+        const int d = (it % (kDim / 4)) * 4;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float lt = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = exp2f(sm_m[w * 16 + qh] - M_use);
+            lt += f * sm_l[w * 16 + qh];
+            o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
+        }
+        store(qh, d, M, lt, o);
+    }
+}
+
 // Shared-mode partition kernel. Grid: blockIdx.x = (p * batch + b) * hkv + g;
 // the NW wavefronts of the workgroup share partition p of (b, g) (pairs w,
 // w + NW, ...) and merge in LDS. NW = 4, or 8 when the grid has at most one
@@ -531,12 +582,8 @@ void attn_partition_kernel(
     extern __shared__ float smem[];
     constexpr int kThreads = NW * 64;
     const int group = hq / hkv;
-    // LDS: [wave][16] max, [wave][16] sum, [wave][group][kAccStride] output,
-    // then the page ids of the partition.
-    float* sm_m = smem;
-    float* sm_l = sm_m + NW * 16;
-    float* sm_acc = sm_l + NW * 16;
-    int32_t* sm_ids = reinterpret_cast<int32_t*>(sm_acc + NW * group * kAccStride);
+    // LDS: the merge area, then the page ids of the partition
+    int32_t* sm_ids = reinterpret_cast<int32_t*>(smem + merge_floats(NW, group));
 
     const int bid = blockIdx.x;
     const int g = bid % hkv;
@@ -602,68 +649,60 @@ void attn_partition_kernel(
     l_tot += __shfl_xor(l_tot, 32);
 
     // ---- merge the NW wavefronts -----------------------------------------
-    if (jgrp == 0) {
-        sm_m[wave * 16 + col] = m_run;
-        sm_l[wave * 16 + col] = l_tot;
-    }
-    if (col < group) {
-        float* row = sm_acc + (wave * group + col) * kAccStride;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-            *reinterpret_cast<f32x4*>(row + 16 * c + 4 * jgrp) = acc_o[c];
-    }
-    __syncthreads();
-
     const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
-    for (int it = tid; it < group * (kDim / 4); it += kThreads) {
-        const int qh = it / (kDim / 4);
-        const int d = (it % (kDim / 4)) * 4;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + qh]);
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        float lt = 0.f;
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float f = exp2f(sm_m[w * 16 + qh] - M_use);
-            lt += f * sm_l[w * 16 + qh];
-            o += f * *reinterpret_cast<const f32x4*>(sm_acc + (w * group + qh) * kAccStride + d);
-        }
+    merge_waves<NW>(smem, wave, lane, group, m_run, l_tot, acc_o,
+                    [&](int qh, int d, float M, float lt, const f32x4& o) {
         if (n_parts == 1) {
             f32x4 r = {0.f, 0.f, 0.f, 0.f};
             if (!bad && lt > 0.f) r = o * (vs / lt);
             *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
         } else {
-            const size_t pslot = (q_row + qh) * n_parts + p;
+            const size_t pslot = (q_row + qh) * partial_slots(n_parts) + p;
             *reinterpret_cast<f32x4*>(part_acc + pslot * kDim + d) = o;
             if (d == 0) {
                 part_ml[2 * pslot] = M;
                 part_ml[2 * pslot + 1] = bad ? -1.f : lt;
             }
         }
-    }
+    });
 }
 
-// Wave-mode kernel for short partitions (<= 2048 tokens): every wavefront
-// works alone on whole partitions, so no wavefront's pipeline is starved by
-// sharing a short partition, and the grid is persistent. The (request,
-// KV head, partition) items that have work are numbered request by request,
-// then KV head, then partition; each workgroup first builds the per-request
-// prefix of partition counts in LDS, then wavefront w of the W in the grid
-// takes the contiguous range of items [w I / W, (w + 1) I / W), finding each
-// item's request by binary search. Consecutive partitions of one (request,
-// KV head) in that range, up to kRunPages pages, are streamed as one run: one
-// register pipeline and one online softmax, so the pipeline fills and drains
-// once per run instead of once per partition. The run's partial goes to its
-// first partition's slot and the other slots are marked empty (max -inf, sum
-// 0), which the reduction weighs 0. Aborted, empty or unmappable requests
-// have no items (the reduction writes their zeros), and no workgroup is
-// launched only to find it has nothing to do. A run's page ids sit in three
-// registers per lane (page k in lane k % 64 of register k / 64) and are
-// broadcast with readlane.
+// Persistent kernel for short partitions (<= 2048 tokens), used when there
+// are enough of them to give every CU work. The (request, KV head, page)
+// units of the requests that have work are numbered request by request, then
+// KV head, then page; each workgroup first builds the per-request prefix of
+// page counts in LDS, then workgroup j of the G that share the work takes
+// the contiguous range of units [j U / G, (j + 1) U / G), so the split is even
+// to within a page. G is the grid size, lowered if needed so that every range
+// holds at least one partition's worth of pages. A range is streamed as runs,
+// one per (request, KV head) it touches, cut into pieces of at most
+// kCoopRunPages pages that end on partition boundaries. The four wavefronts
+// share each piece as in the shared kernel (page pairs w, w + 4, ...), merge
+// through LDS and write one partial.
+//
+// Where the partials go: a piece owns the slot of every partition whose first
+// page it streams, and the piece that reaches the end of a (request, KV head)
+// also owns the extra slot after its last partition, so every slot of a
+// request is owned by exactly one piece. A piece writes its partial to the
+// first slot it owns and marks the others empty (max -inf, sum 0), which the
+// reduction weighs 0. Only a workgroup's first piece can start inside a
+// partition; since a range holds at least one partition's worth of pages and
+// a piece reaches at least the second partition boundary after its start,
+// such a piece streams the next partition's first page, or else ends the
+// (request, KV head) inside its last partition and takes the extra slot.
+// Aborted, empty or unmappable requests have no units (the reduction writes
+// their zeros).
 constexpr int kWaveModeMaxBatch = 4096;     // LDS: 2 * batch + 1 ints
-constexpr int kRunPages = 192;              // pages of one run (three id registers)
+constexpr int kCoopRunPages = 512;          // pages of one piece (LDS page ids)
+static_assert(kCoopRunPages >= 2 * (kWaveModeMaxTokens / kPage) - 1,
+              "a piece starting inside a partition must reach the next partition's start");
+
+// Dynamic LDS of the persistent kernel: the merge area, the piece's page ids,
+// then the per-request prefix and lengths.
+__host__ __device__ constexpr size_t coop_lds_bytes(int group, int batch) {
+    return sizeof(float) * merge_floats(kWaves, group) +
+           sizeof(int32_t) * (kCoopRunPages + 2 * static_cast<size_t>(batch) + 1);
+}
 
 template <bool FP8, bool APPEND>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -677,18 +716,21 @@ void attn_wave_kernel(
     float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv, int32_t num_pages,
     int32_t part_tokens, int32_t n_parts) {
     constexpr int kThreads = kWaves * 64;
-    extern __shared__ int32_t wsm[];
-    int32_t* sm_pre = wsm;                  // [batch + 1] partitions before request b
-    int32_t* sm_len = wsm + batch + 1;      // [batch] seq_lens
+    extern __shared__ float smem[];
+    const int group = hq / hkv;
+    int32_t* sm_ids = reinterpret_cast<int32_t*>(smem + merge_floats(kWaves, group));
+    int32_t* sm_pre = sm_ids + kCoopRunPages;   // [batch + 1] pages before request b
+    int32_t* sm_len = sm_pre + batch + 1;       // [batch] seq_lens
     __shared__ int32_t sm_wsum[kWaves];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
     const int col = lane % 16;
     const int jgrp = lane / 16;
-    const int group = hq / hkv;
+    const int ppp = part_tokens / kPage;    // pages per partition
+    const int64_t n_slots = partial_slots(n_parts);
 
-    // ---- per-request partition counts and their exclusive prefix ---------
+    // ---- per-request page counts and their exclusive prefix --------------
     {
         const int per = (batch + kThreads - 1) / kThreads;     // contiguous requests per thread
         const int b0 = tid * per;
@@ -699,7 +741,7 @@ void attn_wave_kernel(
             const int L = seq_lens[b];
             sm_len[b] = L;
             if (request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride))
-                local += (L + part_tokens - 1) / part_tokens;
+                local += (L + kPage - 1) / kPage;
         }
         int incl = local;                                      // inclusive scan in the wave
 #pragma unroll
@@ -718,7 +760,7 @@ void attn_wave_kernel(
             sm_pre[b] = run;
             const int L = sm_len[b];
             if (request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride))
-                run += (L + part_tokens - 1) / part_tokens;
+                run += (L + kPage - 1) / kPage;
         }
         if (tid == kThreads - 1) {
             int total = 0;
@@ -727,15 +769,14 @@ void attn_wave_kernel(
         }
         __syncthreads();
     }
-    // items (partitions with work) in request, KV head, partition order; each
-    // wavefront takes a contiguous range of about n_items / n_waves of them
-    const int64_t n_items = static_cast<int64_t>(sm_pre[batch]) * hkv;
-    const int64_t n_waves = static_cast<int64_t>(gridDim.x) * kWaves;
-    const int64_t w_id = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-    const int64_t it_end = n_items * (w_id + 1) / n_waves;
-    const int run_cap = max(1, kRunPages / (part_tokens / kPage));   // partitions per run
+    // units in request, KV head, page order; workgroup j takes [j U / G, (j + 1) U / G)
+    const int64_t n_units = static_cast<int64_t>(sm_pre[batch]) * hkv;
+    const int64_t n_groups = min(static_cast<int64_t>(gridDim.x), max<int64_t>(1, n_units / ppp));
+    const int64_t blk = blockIdx.x;
+    if (blk >= n_groups) return;                               // the whole workgroup
+    const int64_t u_end = n_units * (blk + 1) / n_groups;
 
-    for (int64_t it = n_items * w_id / n_waves; it < it_end;) {
+    for (int64_t it = n_units * blk / n_groups; it < u_end;) {
         int lo = 0, hi = batch - 1;                            // last b with pre[b] * hkv <= it
         while (lo < hi) {
             const int mid = (lo + hi + 1) / 2;
@@ -744,26 +785,30 @@ void attn_wave_kernel(
         }
         const int b = __builtin_amdgcn_readfirstlane(lo);
         const int L = __builtin_amdgcn_readfirstlane(sm_len[b]);
-        const int parts_b = (L + part_tokens - 1) / part_tokens;
+        const int npg_b = (L + kPage - 1) / kPage;
         const int local = static_cast<int>(it - static_cast<int64_t>(sm_pre[b]) * hkv);
-        const int g = __builtin_amdgcn_readfirstlane(local / parts_b);
-        const int p = __builtin_amdgcn_readfirstlane(local % parts_b);
-        // the run: partitions p .. p + n - 1 of (b, g), streamed as one sequence
-        const int n = static_cast<int>(
-            min(min(it_end - it, static_cast<int64_t>(parts_b - p)), static_cast<int64_t>(run_cap)));
-        it += n;
-        const int t_begin = p * part_tokens;
-        const int t_end = min(L, (p + n) * part_tokens);
-        const int pg0 = t_begin / kPage;
-        const int npg = (t_end + kPage - 1) / kPage - pg0;     // 1 .. kRunPages
+        const int g = __builtin_amdgcn_readfirstlane(local / npg_b);
+        const int k0 = __builtin_amdgcn_readfirstlane(local % npg_b);
+        // the piece: pages k0 .. k_end - 1 of (b, g)
+        const int cap = (k0 + kCoopRunPages) / ppp * ppp;
+        const int k_end = static_cast<int>(
+            min(min(static_cast<int64_t>(npg_b), static_cast<int64_t>(cap)), k0 + (u_end - it)));
+        const int npg = k_end - k0;                            // 1 .. kCoopRunPages
+        it += npg;
+        const int t_begin = k0 * kPage;
+        const int t_end = min(L, k_end * kPage);
 
-        const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
-        const int32_t id0 = lane < npg ? bt_row[lane] : 0;
-        const int32_t id1 = lane + 64 < npg ? bt_row[lane + 64] : 0;
-        const int32_t id2 = lane + 128 < npg ? bt_row[lane + 128] : 0;
-        const bool bad = __builtin_amdgcn_ballot_w64((id0 < 0 || id0 >= num_pages) ||
-                                                     (id1 < 0 || id1 >= num_pages) ||
-                                                     (id2 < 0 || id2 >= num_pages)) != 0;
+        // page ids -> LDS; an id outside the pool poisons the request
+        int bad = 0;
+        {
+            const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + k0;
+            for (int k = tid; k < npg; k += kThreads) {
+                const int32_t id = bt_row[k];
+                bad |= (id < 0 || id >= num_pages);
+                sm_ids[k] = id;
+            }
+        }
+        bad = __syncthreads_or(bad);
 
         const size_t q_row = static_cast<size_t>(b) * hq + g * group;
         float m_run = -INFINITY;
@@ -775,159 +820,152 @@ void attn_wave_kernel(
             bf16x8 qop[4];
             load_q_operand(qop, q, q_row, group, col, jgrp);
             const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
-            // page_idx is wave-uniform: read the lane of each register and choose among
-            // the scalars (a choice among the registers themselves became a stack array)
             const auto tile_of = [&](int page_idx) __attribute__((always_inline)) -> size_t {
-                const int l = page_idx % 64;
-                const int a = __builtin_amdgcn_readlane(id0, l);
-                const int c = __builtin_amdgcn_readlane(id1, l);
-                const int e = __builtin_amdgcn_readlane(id2, l);
-                const int id = page_idx < 64 ? a : (page_idx < 128 ? c : e);
+                const int id = __builtin_amdgcn_readfirstlane(sm_ids[page_idx]);
                 return static_cast<size_t>(id) * hkv + g;
             };
             const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
-            stream_share<FP8, APPEND>(tile_of, k_pool, v_pool, npg, pg0, 0, 1, t_begin, t_end, L,
-                                      lane, jgrp, s_scale, qop, k_new + new_row, v_new + new_row,
-                                      k_scale + g, v_scale + g, m_run, l_run, acc_o);
+            stream_share<FP8, APPEND>(tile_of, k_pool, v_pool, npg, k0, wave, kWaves, t_begin,
+                                      t_end, L, lane, jgrp, s_scale, qop, k_new + new_row,
+                                      v_new + new_row, k_scale + g, v_scale + g, m_run, l_run,
+                                      acc_o);
         }
         float l_tot = l_run + __shfl_xor(l_run, 16);
         l_tot += __shfl_xor(l_tot, 32);
-        if (col < group) {
-            // the run's partial goes to its first partition's slot; the others of the
-            // run get weight 0 (max -inf, sum 0) and the reduction skips them
-            const size_t pslot = (q_row + col) * n_parts + p;
-            float* dst = part_acc + pslot * kDim + 4 * jgrp;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc_o[c];
-            if (jgrp == 0) {
-                part_ml[2 * pslot] = m_run;
-                part_ml[2 * pslot + 1] = bad ? -1.f : l_tot;
-                for (int k = 1; k < n; ++k) {
-                    part_ml[2 * (pslot + k)] = -INFINITY;
-                    part_ml[2 * (pslot + k) + 1] = 0.f;
+        // owned slots: partitions first_own .. end_own - 1 (their first page is in
+        // [k0, k_end)), and the extra slot np_b when the piece ends the (b, g)
+        const int first_own = (k0 + ppp - 1) / ppp;
+        const int end_own = (k_end + ppp - 1) / ppp;
+        const int np_b = (npg_b + ppp - 1) / ppp;
+        const bool owns_extra = k_end == npg_b;
+        const int dst = first_own < end_own ? first_own : np_b;
+        merge_waves<kWaves>(smem, wave, lane, group, m_run, l_tot, acc_o,
+                            [&](int qh, int d, float M, float lt, const f32x4& o) {
+            const size_t row = (q_row + qh) * n_slots;
+            *reinterpret_cast<f32x4*>(part_acc + (row + dst) * kDim + d) = o;
+            if (d == 0) {
+                part_ml[2 * (row + dst)] = M;
+                part_ml[2 * (row + dst) + 1] = bad ? -1.f : lt;
+                for (int s = first_own; s < end_own; ++s) {
+                    if (s == dst) continue;
+                    part_ml[2 * (row + s)] = -INFINITY;
+                    part_ml[2 * (row + s) + 1] = 0.f;
+                }
+                if (owns_extra && dst != np_b) {
+                    part_ml[2 * (row + np_b)] = -INFINITY;
+                    part_ml[2 * (row + np_b) + 1] = 0.f;
                 }
             }
-        }
+        });
+        __syncthreads();            // the next piece rewrites the ids and the merge area
     }
 }
 
 // Combine the partitions of each (request, query head):
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p acc_p / sum_p w_p l_p
 // Requests that are aborted, empty, too long, or that a partition marked as
-// mapped to an invalid page (l_p < 0) get zeros. One 512-thread workgroup
-// per (b, h): 16 groups of 32 threads (4 dims each) sum interleaved
-// partitions. Each thread issues the loads of its first 16 partitions before
-// the weights are known, so they are in flight during the max / sum passes
-// (weights through LDS); the 16 group sums are added in LDS.
-constexpr int kReduceThreads = 512;
+// mapped to an invalid page (l_p < 0) get zeros. One wavefront per (b, h),
+// four per workgroup, no barriers: a first pass over the (max, sum) pairs
+// finds M and any invalid mark; the second takes 64 slots at a time (the
+// next 64 pairs loading meanwhile), and a ballot of the nonzero weights lists
+// the slots to read, whose outputs (two dims per lane, 512 B per slot) are
+// loaded up to 16 at a time before any is accumulated. Empty slots (weight 0)
+// are never read.
+constexpr int kReduceWaves = 4;
+constexpr int kReduceBatch = 16;            // slot outputs in flight per wavefront
 
-__device__ __forceinline__ float block_max(float v, float* red) {
+__device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    const int w = threadIdx.x / 64;
-    __syncthreads();
-    if (threadIdx.x % 64 == 0) red[w] = v;
-    __syncthreads();
-    float r = red[0];
-    for (int i = 1; i < kReduceThreads / 64; ++i) r = fmaxf(r, red[i]);
-    return r;
+    return v;
 }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
+__device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    const int w = threadIdx.x / 64;
-    __syncthreads();
-    if (threadIdx.x % 64 == 0) red[w] = v;
-    __syncthreads();
-    float r = 0.f;
-    for (int i = 0; i < kReduceThreads / 64; ++i) r += red[i];
-    return r;
+    return v;
 }
 
-__global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
+__global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_acc,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, int32_t bt_stride,
     const uint8_t* __restrict__ abort, const float* __restrict__ v_scale,
-    float* __restrict__ out, int32_t hq, int32_t hkv, int32_t part_tokens, int32_t n_parts) {
-    extern __shared__ float wts[];                  // [n_parts] weights
-    __shared__ float red[kReduceThreads / 64];
-    const int bh = blockIdx.x;
-    const int b = bh / hq;
-    const int h = bh % hq;
-    const int tid = threadIdx.x;
+    float* __restrict__ out, int32_t batch, int32_t hq, int32_t hkv, int32_t part_tokens,
+    int32_t n_parts, int32_t extra_slot) {
+    const int lane = threadIdx.x % 64;
+    const int64_t bh = static_cast<int64_t>(blockIdx.x) * kReduceWaves +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    if (bh >= static_cast<int64_t>(batch) * hq) return;       // wave-uniform
+    const int b = static_cast<int>(bh / hq);
+    const int h = static_cast<int>(bh % hq);
+    f32x2* o = reinterpret_cast<f32x2*>(out + bh * kDim) + lane;
     const int L = seq_lens[b];
     const bool aborted = abort != nullptr && abort[b] != 0;
-    const bool valid_req = !aborted && L >= 1 && L <= max_seq_len &&
-                           (static_cast<int64_t>(L) + kPage - 1) / kPage <= bt_stride;
-    float* o = out + static_cast<size_t>(bh) * kDim;
-    if (!valid_req) {                               // block-uniform
-        if (tid < kDim) o[tid] = 0.f;
+    if (aborted || L < 1 || L > max_seq_len ||
+        (static_cast<int64_t>(L) + kPage - 1) / kPage > bt_stride) {
+        *o = f32x2{0.f, 0.f};
         return;
     }
-    const int np = (L + part_tokens - 1) / part_tokens;
-    const int grp = tid / (kDim / 4);               // 16 groups of 32 threads x 4 dims
-    const int d4 = tid % (kDim / 4);
-    constexpr int kGroups = kReduceThreads / (kDim / 4);
-    constexpr int kBatch = 16;                      // partitions per group in flight
-    const float* acc = part_acc + static_cast<size_t>(bh) * n_parts * kDim + 4 * d4;
-    const auto load_batch = [&](f32x4 (&v)[kBatch], int base) __attribute__((always_inline)) {
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int i = base + grp + kGroups * k;
-            v[k] = i < np ? *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i) * kDim)
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    };
-    f32x4 v[kBatch];
-    load_batch(v, 0);
+    // the request's partitions, plus the slot after them when the persistent
+    // kernel may have written it
+    const int np = (L + part_tokens - 1) / part_tokens + extra_slot;
+    const size_t n_slots = partial_slots(n_parts);
+    const f32x2* ml = reinterpret_cast<const f32x2*>(part_ml) + bh * n_slots;
+    const float* acc = part_acc + bh * n_slots * kDim + 2 * lane;
 
-    const float* ml = part_ml + static_cast<size_t>(bh) * n_parts * 2;
+    constexpr f32x2 kEmpty = {-INFINITY, 0.f};
     float mx = -INFINITY;
-    int bad = 0;
-    for (int i = tid; i < np; i += kReduceThreads) {
-        const f32x2 e = *reinterpret_cast<const f32x2*>(ml + 2 * i);
-        bad |= e[1] < 0.f;
-        wts[i] = e[0];
-        mx = fmaxf(mx, e[0]);
+    bool bad = false;
+    for (int i0 = lane; i0 < np; i0 += 4 * 64) {              // four loads in flight
+        f32x2 e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) e[k] = i0 + 64 * k < np ? ml[i0 + 64 * k] : kEmpty;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bad |= e[k][1] < 0.f;
+            mx = fmaxf(mx, e[k][0]);
+        }
     }
-    bad = __syncthreads_or(bad);
-    if (bad) {
-        if (tid < kDim) o[tid] = 0.f;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+        *o = f32x2{0.f, 0.f};
         return;
     }
-    const float M = block_max(mx, red);
+    const float M = wave_max(mx);
+    const float M_use = M == -INFINITY ? 0.f : M;
     float lsum = 0.f;
-    for (int i = tid; i < np; i += kReduceThreads) {
-        const float w = exp2f(wts[i] - M);
-        lsum += w * ml[2 * i + 1];
-        wts[i] = w;
-    }
-    const float lt = block_sum(lsum, red);          // ends with a barrier: wts is complete
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int base = 0;;) {
+    f32x2 num = {0.f, 0.f};
+    f32x2 e_next = lane < np ? ml[lane] : kEmpty;
+    for (int c = 0; c < np; c += 64) {
+        const f32x2 e = e_next;                               // the next chunk's pairs load
+        e_next = c + 64 + lane < np ? ml[c + 64 + lane] : kEmpty;   // under this one's reads
+        const float w = exp2f(e[0] - M_use);                  // 0 for an empty slot
+        lsum += w * e[1];
+        uint64_t mask = __builtin_amdgcn_ballot_w64(w > 0.f);
+        while (mask != 0) {
+            int sl[kReduceBatch];
+            f32x2 v[kReduceBatch];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int i = base + grp + kGroups * k;
-            if (i < np && wts[i] > 0.f) num += wts[i] * v[k];   // slots of weight 0 may hold stale bytes
+            for (int k = 0; k < kReduceBatch; ++k) {
+                sl[k] = mask != 0 ? __builtin_ctzll(mask) : -1;    // wave-uniform
+                mask &= mask - 1;
+                if (sl[k] >= 0)
+                    v[k] = *reinterpret_cast<const f32x2*>(acc + static_cast<size_t>(c + sl[k]) * kDim);
+            }
+#pragma unroll
+            for (int k = 0; k < kReduceBatch; ++k) {
+                if (sl[k] >= 0)
+                    num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sl[k])) * v[k];
+            }
         }
-        base += kGroups * kBatch;
-        if (base >= np) break;
-        load_batch(v, base);
     }
-    __shared__ f32x4 part[kGroups][kDim / 4];
-    part[grp][d4] = num;
-    __syncthreads();
-    if (tid < kDim / 4) {
-        f32x4 t = part[0][tid];
-        for (int k = 1; k < kGroups; ++k) t += part[k][tid];
-        const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
-        const f32x4 r = lt > 0.f ? t * (vs / lt) : f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(o + 4 * tid) = r;
-    }
+    const float lt = wave_sum(lsum);
+    const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
+    *o = lt > 0.f ? num * (vs / lt) : f32x2{0.f, 0.f};
 }
 
 // gfx950 (MI355X) has 256 CUs; a grid of at most this many workgroups runs
 // one per CU.
 constexpr int64_t kNumCUs = 256;
+// LDS one workgroup may allocate without opting in to more.
+constexpr size_t kMaxLdsBytes = 64 * 1024;
 
 // Wave mode (one short partition per wavefront) only pays when there are
 // enough partitions for at least one 4-wave workgroup per CU; its LDS holds
@@ -935,7 +973,8 @@ constexpr int64_t kNumCUs = 256;
 bool use_wave_partitions(const AttnArgs& a) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads;
     return a.num_partitions > 1 && a.partition_tokens <= kWaveModeMaxTokens &&
-           a.batch <= kWaveModeMaxBatch && items * a.num_partitions >= kWaves * kNumCUs;
+           a.batch <= kWaveModeMaxBatch && items * a.num_partitions >= kWaves * kNumCUs &&
+           coop_lds_bytes(a.num_q_heads / a.num_kv_heads, a.batch) <= kMaxLdsBytes;
 }
 
 // Shared mode with 8 wavefronts when the grid has at most one workgroup per
@@ -958,10 +997,10 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
         a.seq_lens, a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2, a.batch,      \
         a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions
     if (use_wave_partitions(a)) {
-        // persistent: at most 2 workgroups per CU, each wavefront loops over items
+        // persistent: at most 2 workgroups per CU, each streams its range of pages
         const int64_t wgs = std::min<int64_t>(2 * kNumCUs,
                                               (items * a.num_partitions + kWaves - 1) / kWaves);
-        const size_t lds = sizeof(int32_t) * (2 * static_cast<size_t>(a.batch) + 1);
+        const size_t lds = coop_lds_bytes(group, a.batch);
 #define KVFP8_WAVE(F8, AP)                                                                       \
     hipLaunchKernelGGL((attn_wave_kernel<F8, AP>), dim3(static_cast<uint32_t>(wgs)),            \
                        dim3(kWaves * 64), lds, stream, KVFP8_ARGS)
@@ -973,7 +1012,7 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
 #undef KVFP8_WAVE
     } else {
         const int nw = use_wide_workgroups(a) ? kWavesWide : kWaves;
-        const size_t lds = sizeof(float) * (2 * nw * 16 + nw * group * kAccStride) +
+        const size_t lds = sizeof(float) * merge_floats(nw, group) +
                            sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage);
         const dim3 grid(static_cast<uint32_t>(a.num_partitions * items));
 #define KVFP8_SHARED(F8, NW, AP)                                                                 \
@@ -995,11 +1034,13 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
 #undef KVFP8_ARGS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_partitions == 1) return e;
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3(a.batch * a.num_q_heads), dim3(kReduceThreads),
-                       sizeof(float) * static_cast<size_t>(a.num_partitions), stream, a.part_ml,
-                       a.part_acc, a.seq_lens, a.max_seq_len, a.bt_stride, a.abort,
-                       fp8 ? a.v_scale : nullptr, a.out, a.num_q_heads, a.num_kv_heads,
-                       a.partition_tokens, a.num_partitions);
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
+    hipLaunchKernelGGL(reduce_partials_kernel,
+                       dim3(static_cast<uint32_t>((rows + kReduceWaves - 1) / kReduceWaves)),
+                       dim3(kReduceWaves * 64), 0, stream, a.part_ml, a.part_acc, a.seq_lens,
+                       a.max_seq_len, a.bt_stride, a.abort, fp8 ? a.v_scale : nullptr, a.out,
+                       a.batch, a.num_q_heads, a.num_kv_heads, a.partition_tokens,
+                       a.num_partitions, use_wave_partitions(a) ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -41,9 +41,16 @@ struct AttnArgs {
     int32_t num_pages;
     int32_t partition_tokens;   // resolved, > 0
     int32_t num_partitions;     // ceil(max_seq_len / partition_tokens), >= 1
-    float* part_ml;             // [batch][Hq][num_partitions][2], or null if 1 partition
-    float* part_acc;            // [batch][Hq][num_partitions][128]
+    float* part_ml;             // [batch][Hq][partial_slots(num_partitions)][2], or null if 1 partition
+    float* part_acc;            // [batch][Hq][partial_slots(num_partitions)][128]
 };
+
+// Split-K partial slots per (request, query head): one per partition, plus
+// one more that the wave-mode kernel uses when a wavefront's share starts
+// inside a request's last partition (the slot after that partition).
+__host__ __device__ constexpr int64_t partial_slots(int64_t num_partitions) {
+    return num_partitions + 1;
+}
 
 hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream);
 

@@ -88,7 +88,8 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
     const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
     if (parts64 > KV_MAX_PARTITIONS) return KV_ERR_UNSUPPORTED;
     // shared-mode grid: one workgroup of up to 8 wavefronts per (partition,
-    // request, KV head); the reduce: one of 512 threads per (request, query head)
+    // request, KV head); the reduce (one wavefront per (request, query head))
+    // is held to the same 512 work-items per row
     if (!grid_fits(parts64 * batch * num_kv_heads, 512)) return KV_ERR_SHAPE;
     if (parts64 > 1 && !grid_fits(static_cast<int64_t>(batch) * num_q_heads, 512))
         return KV_ERR_SHAPE;
@@ -131,7 +132,7 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
     a.partition_tokens = pt;
     a.num_partitions = parts;
     if (parts > 1) {
-        const size_t slots = static_cast<size_t>(batch) * num_q_heads * parts;
+        const size_t slots = static_cast<size_t>(batch) * num_q_heads * kvfp8::partial_slots(parts);
         const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
         a.part_ml = static_cast<float*>(workspace);
         a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
@@ -230,7 +231,7 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
     if (pt <= 0) return 0;
     const int64_t parts = (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
     if (parts <= 1) return 0;
-    const size_t slots = static_cast<size_t>(batch) * num_q_heads * parts;
+    const size_t slots = static_cast<size_t>(batch) * num_q_heads * kvfp8::partial_slots(parts);
     // [slots][2] (max, sum) then [slots][head_dim] outputs, 256-byte aligned
     const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
     return ml + slots * head_dim * sizeof(float);

@@ -187,9 +187,11 @@ int32_t paged_decode_attn_partition_tokens(int32_t batch, int32_t num_kv_heads,
 
 /*
  * Bytes of device workspace paged_decode_attn needs for these sizes (0 when a
- * single partition covers max_seq_len). The workspace holds per-partition
- * softmax partials (running max, normaliser, unnormalised output) that the
- * cross-partition reduction combines. Returns 0 for unsupported arguments.
+ * single partition covers max_seq_len). The workspace holds split-K softmax
+ * partials (running max, normaliser, unnormalised output), one slot per
+ * partition of each (request, query head) plus one more, that the
+ * cross-partition reduction combines. Its contents on entry do not matter.
+ * Returns 0 for unsupported arguments.
  */
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
@@ -240,10 +242,11 @@ int paged_decode_attn(const void* q, int32_t cache_dtype,
  * the same result as kv_append_quant (FP8) / kv_append_bf16 (BF16) with
  * tok_seq = 0..batch-1, tok_pos = seq_lens - 1, followed by paged_decode_attn,
  * for every request the attention accepts (abort[b] == 0, 1 <= L <= max_seq_len,
- * ceil(L/16) <= bt_stride). The new token is written exactly when its request
- * is accepted and every page of the split-K partition holding it is a valid
- * pool page (with the tag check run first, any request mapping an invalid
- * page is aborted, so it is neither written nor read). The wavefront that
+ * ceil(L/16) <= bt_stride). The new token is written when its request is
+ * accepted and maps only valid pool pages. A request that maps an invalid
+ * page gets zeros, and whether its new token is stored is left open (run
+ * the tag check first and such a request is aborted: neither written nor
+ * read). The wavefront that
  * processes the new token's page quantizes it, uses the codes from its
  * registers and stores them for later steps, so nothing in the launch reads
  * them back from memory. One launch per layer instead of two; the separate

@@ -242,8 +242,9 @@ def test_workspace_and_partition_sizing(lib):
     import fp8_e4m3_paged_amd as k
     # one partition covers everything: no workspace
     assert k.paged_decode_attn_workspace_bytes(64, 64, 8, 8000, 8192) == 0
-    # C5-like: 16 requests, 64 heads, 131073 tokens at 512 -> 257 partitions
-    n = 16 * 64 * 257
+    # C5-like: 16 requests, 64 heads, 131073 tokens at 512 -> 257 partitions, and
+    # one more partial slot per (request, query head) for the wave-mode kernel
+    n = 16 * 64 * (257 + 1)
     ml = -(-(n * 2 * 4) // 256) * 256
     assert k.paged_decode_attn_workspace_bytes(16, 64, 8, 131073, 512) == ml + n * 128 * 4
     for b, h, L in [(64, 8, 9193), (1, 1, 256), (16, 8, 131073), (8, 8, 8192)]:
@@ -285,7 +286,7 @@ def test_launch_size_limits_are_refused_before_anything_is_enqueued(lib):
     # attention: one workgroup (<= 512 threads) per (partition, request, KV head)
     assert attn(lib, batch=1_048_577) == SHAPE                 # one partition, 8 KV heads
     assert attn(lib, batch=1_048_575, q=None) == NULL
-    # ... and the reduce, one 512-thread workgroup per (request, query head)
+    # ... and the reduce, held to 512 work-items per (request, query head)
     assert attn(lib, batch=600_000, num_q_heads=16, num_kv_heads=1, max_seq_len=1024,
                 partition_tokens=512) == SHAPE
     assert attn(lib, batch=500_000, num_q_heads=16, num_kv_heads=1, max_seq_len=1024,

@@ -441,3 +441,98 @@ def test_verify_tags_cases(kv):
                           torch.from_numpy(ls).to(DEV), ab)
         torch.cuda.synchronize()
         assert np.array_equal(ab.cpu().numpy(), want), (ls, ab.cpu().numpy(), want)
+
+
+def test_verify_tags_long_rows(kv):
+    """Rows of up to 5,000 pages (80k tokens), more than one sweep of the
+    workgroup's 1,024 threads: a failing page anywhere (first, middle, last,
+    the one page of a last sweep) aborts exactly its request, pages past a
+    request's length are ignored, and flags that held 1 or junk before the
+    call are overwritten with the oracle's 0 / 1."""
+    rng = np.random.default_rng(23)
+    num_pages, batch, width = 50_000, 12, 5_000
+    tags = rng.integers(0, 2 ** 32, num_pages, dtype=np.uint64).astype(np.uint32)
+    bt = rng.integers(0, num_pages, (batch, width)).astype(np.int32)
+    exp = tags[bt].copy()
+    lens = np.array([16 * 5_000, 16 * 5_000, 16 * 5_000, 16 * 4_097, 16 * 1_024 + 1, 0, -1,
+                     16 * 5_000 + 1, 16 * 3_000, 16 * 2_048, 16 * 5_000, 16 * 1_500], np.int32)
+    exp[0, 0] ^= 1                     # the first page
+    exp[1, 2_500] ^= 1 << 7            # a middle one
+    exp[2, 4_999] ^= 1 << 31           # the last page of a full row
+    exp[3, 4_096] ^= 1                 # the one page of a 4,097-page request's last sweep
+    bt[4, 1_024] = num_pages           # a page id just outside the pool
+    bt[8, 3_000] = -1                  # past request 8's pages: ignored
+    exp[9, 2_048] ^= 1                 # likewise
+    bt[11, 1_499] = -7                 # last page of a 1500-page request
+    want = paged.verify_tags(tags, bt, exp, lens, 16)
+    assert want.tolist() == [1, 1, 1, 1, 1, 0, 1, 1, 0, 0, 0, 1]
+    for fill in (0, 1, 0xA5):
+        ab = torch.full((batch,), fill, dtype=torch.uint8, device=DEV)
+        kv.kv_verify_tags(torch.from_numpy(tags.view(np.int32)).to(DEV),
+                          torch.from_numpy(bt).to(DEV),
+                          torch.from_numpy(exp.view(np.int32)).to(DEV),
+                          torch.from_numpy(lens).to(DEV), ab)
+        torch.cuda.synchronize()
+        assert np.array_equal(ab.cpu().numpy(), want), (fill, ab.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_wave_mode_even_page_split_long_partitions(kv, cache):
+    """Partitions of 256 to 2048 tokens in the wave-mode kernel, which splits
+    the work evenly by pages: wavefronts start inside partitions, some inside a
+    request's last partition. Every output against the oracle, then the fused
+    append + attention against the separate calls, bit for bit, and again
+    against the oracle on the pools the fused launch wrote."""
+    hq, hkv = 64, 8
+    rng = np.random.default_rng(7)
+    lens = rng.integers(1, 3000, 72)
+    lens[[3, 40]] = 0
+    lens[[10, 11, 12, 13, 14]] = [2048, 2049, 4096, 1, 16]
+    lens = lens.tolist()
+    need = sum(max(1, -(-L // 16)) for L in lens)
+    e = _edge_state(kv, cache, hq, hkv, lens, pool_pages=need + 8)
+    zero = [b for b, L in enumerate(lens) if L == 0]
+    want = _edge_oracle(e, cache, lens)
+    for pt in (256, 1024, 2048):
+        assert _runs_one_partition_per_wave(len(lens), hkv, max(lens), pt)
+        got = _edge_run(kv, e, cache, partition_tokens=pt)
+        helpers.check_attention(got, want, zero_rows=zero, label=f"page split {cache} p{pt}")
+
+    # the fused path: a new row for position L - 1 of every non-empty request
+    batch = len(lens)
+    kn = synth._f32_to_bf16_bits(rng.normal(0, 1, (batch, hkv, 128)).astype(np.float32))
+    vn = synth._f32_to_bf16_bits(rng.normal(0, 0.5, (batch, hkv, 128)).astype(np.float32))
+    knt = torch.from_numpy(kn.view(np.int16)).to(DEV)
+    vnt = torch.from_numpy(vn.view(np.int16)).to(DEV)
+    live = np.array([b for b, L in enumerate(lens) if L > 0], np.int32)
+    pos = np.array([lens[b] - 1 for b in live], np.int32)
+    q = torch.from_numpy(e["q"].view(np.int16)).to(DEV)
+    seq = torch.from_numpy(np.array(lens, np.int32)).to(DEV)
+    msl = max(lens)
+    for pt in (1024, 2048):
+        n = kv.paged_decode_attn_workspace_bytes(batch, hq, hkv, msl, pt)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV)
+        kp_a, vp_a = e["kp"].clone(), e["vp"].clone()
+        kp_b, vp_b = e["kp"].clone(), e["vp"].clone()
+        li = torch.from_numpy(live).to(DEV)
+        args = (knt[li], vnt[li], li, torch.from_numpy(pos).to(DEV), e["btt"])
+        if cache == "fp8":
+            kv.kv_append_quant(*args, e["kst"], e["vst"], kp_a, vp_a)
+        else:
+            kv.kv_append_bf16(*args, kp_a, vp_a)
+        ks = e["kst"] if cache == "fp8" else None
+        vs = e["vst"] if cache == "fp8" else None
+        dt = 0 if cache == "fp8" else 1
+        out_a = torch.full((batch, hq, 128), float("nan"), device=DEV)
+        out_b = torch.full((batch, hq, 128), float("nan"), device=DEV)
+        kv.paged_decode_attn(q, kp_a, vp_a, ks, vs, e["btt"], seq, msl, out_a, 0.0883883,
+                             workspace=ws, partition_tokens=pt, cache_dtype=dt)
+        kv.paged_decode_attn_append(q, knt, vnt, kp_b, vp_b, ks, vs, e["btt"], seq, msl, out_b,
+                                    0.0883883, workspace=ws, partition_tokens=pt,
+                                    cache_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.equal(kp_a, kp_b) and torch.equal(vp_a, vp_b), f"fused pools p{pt}"
+        assert torch.equal(out_a, out_b), f"fused output p{pt}"
+    e2 = dict(e, kp=kp_b, vp=vp_b)
+    helpers.check_attention(out_b.cpu().numpy(), _edge_oracle(e2, cache, lens), zero_rows=zero,
+                            label=f"page split fused {cache}")
