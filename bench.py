@@ -59,9 +59,9 @@ INGEST_COUNTER_TRAFFIC = {
 }
 GEMV_COUNTER_TRAFFIC = {
     "sources": ("gemv.hip", "kv_device.h"),
-    "source_sha": "9bb40110c444bfcb",
-    "read_bytes": 1.24998e8,
-    "write_bytes": 2.294e6,
+    "source_sha": "c72e58afe66ac898",
+    "read_bytes": 1.24997e8,
+    "write_bytes": 5.734e5,
 }
 
 

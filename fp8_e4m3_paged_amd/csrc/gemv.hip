@@ -8,9 +8,13 @@
 //
 //  * packed layout (documented in kvfp8.h): block (nt, g) = rows 16 nt ..
 //    16 nt + 15, inputs 128 g .. 128 g + 127; lane l of a wavefront owns the
-//    16-byte chunk(s) at 16 l (+ 1 KiB) holding exactly its A operands of the
-//    four 16x16x32 bf16 MFMAs over the group (row l % 16, inputs
+//    16-byte chunk(s) at 16 l (+ 1 KiB) holding exactly its weight operands
+//    of the four 16x16x32 bf16 MFMAs over the group (row l % 16, inputs
 //    32 c + 8 (l / 16) + 0..7 of slice c), so each load is a coalesced 1 KiB;
+//  * the activations are the MFMA's A operand (tokens down the rows) and the
+//    weights its B operand, so a lane's four results are four tokens of one
+//    weight row and the 16 lanes of a token add to 16 consecutive outputs
+//    (one 64-byte line per atomic instruction and token group);
 //  * integer codes (sign-magnitude, |q| <= 7) become bf16 exactly through an
 //    e4m3 lookup and the hardware decode, e4m3 codes through the decode
 //    alone; the MFMA sums one group in fp32 and the group's row scale
@@ -142,7 +146,9 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo_w, uint32_t hi_w) {
 // Chunk and grid sizes (measured on the decode layer shapes): with one m-tile
 // (<= 16 tokens) short chunks and many workgroups keep the most weight bytes
 // in flight; with more tokens fewer splits of the inputs cut the re-staged
-// activations and the atomic adds.
+// activations and the atomic adds. Two groups per chunk with two m-tiles
+// (4 took 8% longer at 24-32 tokens); one with four m-tiles of INT4 weights
+// (6% faster than 2 at 64 tokens, while FP8 weights were 10% slower with it).
 #ifndef KVFP8_GEMV_CG1
 #define KVFP8_GEMV_CG1 2          // groups per chunk with one m-tile
 #endif
@@ -155,9 +161,9 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo_w, uint32_t hi_w) {
 #ifndef KVFP8_GEMV_TARGET_WGS3
 #define KVFP8_GEMV_TARGET_WGS3 512    // more than 16 tokens
 #endif
-template <int MT>
+template <bool INT4, int MT>
 struct GemvChunk {
-    static constexpr int CG = MT == 1 ? KVFP8_GEMV_CG1 : (MT == 2 ? 4 : 2);
+    static constexpr int CG = MT == 1 ? KVFP8_GEMV_CG1 : (MT == 4 && INT4 ? 1 : 2);
     static constexpr int ROW = CG * kWGroup + 8;      // halves per LDS row (16-byte pad)
     static constexpr int PIECES = MT * 16 * CG * 16;  // 16-byte pieces per chunk
     static_assert(PIECES % (kGemvWaves * 64) == 0, "pieces per thread");
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
     const uint16_t* __restrict__ x, int32_t m_rows, const uint8_t* __restrict__ packed,
     const float* __restrict__ scales, int32_t n, int32_t k, float* __restrict__ y,
     int32_t groups_per_wg) {
-    using C = GemvChunk<MT>;
+    using C = GemvChunk<INT4, MT>;
     constexpr int CG = C::CG;
     __shared__ uint16_t xs[2][MT * 16][C::ROW];
 
@@ -191,8 +197,8 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
     const int g0 = wg_k * groups_per_wg;
     const int g1 = min(groups, g0 + groups_per_wg);
     const int n_chunks = (g1 - g0 + CG - 1) / CG;
-    const int col = lane % 16;          // B: token m within the m-tile; C: column
-    const int jg = lane / 16;           // B: input sub-slice; C: row group of 4
+    const int col = lane % 16;          // A: token within the m-tile; B and result: weight row
+    const int jg = lane / 16;           // A, B: input sub-slice; result: token group of 4
 
     // activation chunk ci -> registers (zeros past the rows or groups), then LDS
     u32x4 xr[C::PER_THREAD];
@@ -218,8 +224,8 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
     };
     // codes and scales of chunk ci (groups past g1 are not loaded)
     GroupCodes<INT4> wc[CG];
-    f32x4 sc[CG];
-    const auto load_w = [&](int ci, GroupCodes<INT4> (&w)[CG], f32x4 (&s)[CG]) __attribute__((always_inline)) {
+    float sc[CG];
+    const auto load_w = [&](int ci, GroupCodes<INT4> (&w)[CG], float (&s)[CG]) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < CG; ++q) {
             const int g = g0 + ci * CG + q;
@@ -234,7 +240,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
                     w[q].w[1] = __builtin_nontemporal_load(
                         reinterpret_cast<const u32x4*>(packed + blk * 2048 + 1024 + 16 * lane));
                 }
-                s[q] = *reinterpret_cast<const f32x4*>(scales + blk * 16 + 4 * jg);
+                s[q] = scales[blk * 16 + col];
             }
         }
     };
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
         const int buf = ci & 1;
         const bool more = ci + 1 < n_chunks;                  // uniform over the workgroup
         GroupCodes<INT4> wn[CG];
-        f32x4 sn[CG];
+        float sn[CG];
         if (more) {                                           // next chunk in flight
             load_x(ci + 1);
             load_w(ci + 1, wn, sn);
@@ -280,9 +286,9 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
                         const u32x4 xb = *reinterpret_cast<const u32x4*>(
                             &xs[buf][16 * t + col][kWGroup * q + 32 * c + 8 * jg]);
                         part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            A[c], __builtin_bit_cast(bf16x8, xb), part, 0, 0, 0);
+                            __builtin_bit_cast(bf16x8, xb), A[c], part, 0, 0, 0);
                     }
-                    acc[t] += sc[q] * part;     // rows 4 jg + i of the tile carry scale sc[q][i]
+                    acc[t] += sc[q] * part;     // column col is weight row 16 nt + col
                 }
             }
         }
@@ -297,14 +303,15 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
         __syncthreads();
     }
     if (!active) return;
-    // C layout: lane holds rows 16 nt + 4 jg + i, column 16 t + col
+    // result layout: lane holds tokens 16 t + 4 jg + i of weight row 16 nt + col, so
+    // the 16 lanes of one jg add to 16 consecutive outputs (one 64-byte line)
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        const int m = 16 * t + col;
-        if (m >= m_rows) continue;
-        float* yr = y + static_cast<size_t>(m) * n + 16 * nt + 4 * jg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(yr + i, acc[t][i]);
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * t + 4 * jg + i;
+            if (m < m_rows) unsafeAtomicAdd(y + static_cast<size_t>(m) * n + 16 * nt + col, acc[t][i]);
+        }
     }
 }
 
@@ -312,11 +319,10 @@ __global__ __launch_bounds__(kGemvWaves * 64) void wq_gemv_kernel(
 // GEMV for 1 .. 4 tokens: no per-chunk barrier. The workgroup stages the
 // activations of its whole input range (real rows only; m_rows x ng x 256 B
 // of dynamic LDS) once, then every wavefront streams its tile's codes and
-// scales through a 3-deep register pipeline while it reads its B operands
-// from LDS (a separate counter from the code loads, so the waits for the
-// codes never wait on activations). Columns of the B operand past the real
-// tokens read row 0: their output columns are discarded, so no zero rows are
-// stored.
+// scales through a 3-deep register pipeline while it reads its activation
+// operands from LDS (a separate counter from the code loads, so the waits for
+// the codes never wait on activations). Operand rows past the real tokens
+// read token 0: their results are discarded, so no zero rows are stored.
 // ---------------------------------------------------------------------------
 // Up to 4 tokens (measured: from 5 tokens on the chunked kernel with 768
 // workgroups is faster, at 8 tokens 58 against 68 us per INT4 layer).
@@ -331,7 +337,7 @@ __host__ __device__ constexpr int small_max_groups(int m_rows) { return m_rows <
 template <bool INT4>
 struct GroupTile {
     u32x4 w[INT4 ? 1 : 2];
-    f32x4 s;
+    float s;                       // scale of weight row 16 nt + col
 };
 
 template <bool INT4>
@@ -363,18 +369,18 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
     __syncthreads();
     if (nt >= n_tiles) return;                             // no barrier below
 
-    const int col = lane % 16;                             // B: token; C: column
-    const int jg = lane / 16;                              // B: input sub-slice; C: row group of 4
+    const int col = lane % 16;                             // A: token; B and result: weight row
+    const int jg = lane / 16;                              // A, B: input sub-slice; result: token group
     const uint16_t* xb_base = xs_dyn + (col < m_rows ? col : 0) * row_h + 8 * jg;
     const size_t blk0 = static_cast<size_t>(nt) * groups + g0;
     const uint8_t* cbase = packed + blk0 * BLK + 16 * lane;
-    const float* sbase = scales + blk0 * 16 + 4 * jg;
+    const float* sbase = scales + blk0 * 16 + col;
 
     const auto issue = [&](GroupTile<INT4>& t, int i) __attribute__((always_inline)) {
         const uint8_t* cp = cbase + static_cast<size_t>(i) * BLK;
         t.w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp));
         if constexpr (!INT4) t.w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp + 1024));
-        t.s = *reinterpret_cast<const f32x4*>(sbase + static_cast<size_t>(i) * 16);
+        t.s = sbase[static_cast<size_t>(i) * 16];
     };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const auto proc = [&](const GroupTile<INT4>& t, int i) __attribute__((always_inline)) {
@@ -392,10 +398,10 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const u32x4 xb = *reinterpret_cast<const u32x4*>(xb_base + kWGroup * i + 32 * c);
-            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[c], __builtin_bit_cast(bf16x8, xb),
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xb), A[c],
                                                            part, 0, 0, 0);
         }
-        acc += t.s * part;                 // rows 4 jg + r of the tile carry scale s[r]
+        acc += t.s * part;                 // column col is weight row 16 nt + col
     };
     // 3-deep pipeline: the steady-state loop issues unconditionally (i + 5 < ng);
     // the last 1 .. 5 groups are handled with uniform conditions.
@@ -420,10 +426,11 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
     if (i + 3 < ng) proc(t0, i + 3);
     if (i + 4 < ng) proc(t1, i + 4);
 
-    if (col < m_rows) {
-        float* yr = y + static_cast<size_t>(col) * n + 16 * nt + 4 * jg;
+    // lane holds tokens 4 jg + r of weight row 16 nt + col
 #pragma unroll
-        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(yr + r, acc[r]);
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * jg + r;
+        if (m < m_rows) unsafeAtomicAdd(y + static_cast<size_t>(m) * n + 16 * nt + col, acc[r]);
     }
 }
 

@@ -443,6 +443,21 @@ def test_verify_tags_cases(kv):
         assert np.array_equal(ab.cpu().numpy(), want), (ls, ab.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_maximum_partition_count(kv, cache):
+    """131,072 tokens in 16-token partitions: 8,192 partitions, the most the
+    library accepts, in the persistent kernel. The reduce then combines 8,193
+    slots of the long request's rows, a few hundred of them non-empty, in
+    129 passes of 64; the short request and an empty one share the launch."""
+    lens = [131_072, 5_000, 0]
+    need = sum(max(1, -(-L // 16)) for L in lens)
+    e = _edge_state(kv, cache, 8, 1, lens, pool_pages=need + 4)
+    assert _runs_one_partition_per_wave(len(lens), 1, max(lens), 16)
+    got = _edge_run(kv, e, cache, partition_tokens=16)
+    want = _edge_oracle(e, cache, lens)
+    helpers.check_attention(got, want, zero_rows=[2], label=f"8192 partitions {cache}")
+
+
 def test_verify_tags_long_rows(kv):
     """Rows of up to 5,000 pages (80k tokens), more than one sweep of the
     workgroup's 1,024 threads: a failing page anywhere (first, middle, last,
