@@ -38,10 +38,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
 # reads for a plain 1 GiB device copy (fetch x2.000, write x1.000); valid only
 # for the kernel sources they were taken on (sha256 prefix of decode_attn.hip
-# + kv_device.h + kv_launch.h). See profiles/attn_partition_kernel_c4_hbm_counters.md.
+# + kv_device.h + kv_launch.h). See profiles/attn_partition_kernel_batch64_ctx8k_hbm_counters.md.
 COUNTER_TRAFFIC = {
-    "source_sha": "d152b534b6a88752",
-    "workload": "c4_headline",
+    "source_sha": "ba8664f65a5f1422",
+    "workload": "batch64_ctx8k",
     "read_bytes": 1.144e9,
     "write_bytes": 2.490e6,
     "algorithmic_bytes": 1143833636,
@@ -49,7 +49,7 @@ COUNTER_TRAFFIC = {
 
 
 # The same for the prefill page writer (ingest_kernel<FP8>, one layer of the
-# headline prompts; profiles/ingest_kernel_c4_prompts.md) and the INT4 GEMV
+# headline prompts; profiles/ingest_kernel_batch64_prompts.md) and the INT4 GEMV
 # roofline kernel (28672x8192, one token; profiles/wq_gemv_int4_1token.md).
 INGEST_COUNTER_TRAFFIC = {
     "sources": ("ingest.hip", "kv_device.h"),
@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c4", choices=["c3", "c4", "c5"])
+    ap.add_argument("--config", default="batch64", choices=["uniform32", "batch64", "skewed16"])
     ap.add_argument("--cache", default="fp8", choices=["fp8", "bf16"])
     ap.add_argument("--verify", default="on", choices=["on", "off"])
     ap.add_argument("--partition-tokens", type=int, default=-1,
@@ -327,7 +327,7 @@ def ingest_bench(args):
 
     kv.load()
     dev = "cuda"
-    make = {"c3": synth.c3_uniform, "c4": synth.c4_headline, "c5": synth.c5_skewed}[args.config]
+    make = {"uniform32": synth.uniform_32req, "batch64": synth.batch64_ctx8k, "skewed16": synth.skewed_16req}[args.config]
     wl = make(max_steps=1)
     fp8 = args.cache == "fp8"
     hkv, D, P = wl.num_kv_heads, wl.head_dim, wl.page_size
@@ -402,7 +402,7 @@ def ingest_bench(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ingest_bytes / t_ingest / 1e6 / HBM_PEAK_GBS, 4),
                      "traffic": (counter_traffic(INGEST_COUNTER_TRAFFIC)
-                                 if fp8 and wl.name == "c4_headline" else None),
+                                 if fp8 and wl.name == "batch64_ctx8k" else None),
                      "avg_launch_us": round(t_ingest * 1e3, 2),
                      "algorithmic_bytes_per_launch": ingest_bytes},
         "amax_kernel": {"GBps": round(2 * n_tok * row_bytes / 2 / t_amax / 1e6, 1),
@@ -422,7 +422,8 @@ def sweep_bench(args):
     the BF16 pools of 32 requests (room for the timed steps included), so
     BF16 runs out above 32 while FP8 reaches 64. Each point that fits runs the
     decode step (tag check, fused append + attention per layer) for --steps
-    steps after --warmup; a point that does not fit is reported as such."""
+    steps after --warmup, three times over, and reports the median window; a
+    point that does not fit is reported as such."""
     import numpy as np
     import torch
 
@@ -477,13 +478,19 @@ def sweep_bench(args):
             for i in range(args.warmup):
                 step(i)
             torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for i in range(args.steps):
-                step(args.warmup + i)
-            b.record()
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / args.steps
+            # the same K steps timed three times (a step rewrites its own new token,
+            # so repeating it is the same work); the median, since the windows of
+            # the small points are a few ms and the first can catch the clocks rising
+            windows = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for i in range(args.steps):
+                    step(args.warmup + i)
+                b.record()
+                torch.cuda.synchronize()
+                windows.append(a.elapsed_time(b) / args.steps)
+            ms = float(np.median(windows))
             byts = sum(step_bytes(wl, wl.seq_lens_at(args.warmup + i), cache, True)["total"]
                        for i in range(args.steps)) / args.steps
             pt.update(fits=True, ms_per_step=round(ms, 4),
@@ -624,7 +631,7 @@ def main():
     # which would add gaps), the attention calls bracketed by events, and
     # optionally the no-op tracker
     total_steps = args.warmup + args.steps * (3 if measure_noop else 2)
-    make = {"c3": synth.c3_uniform, "c4": synth.c4_headline, "c5": synth.c5_skewed}[args.config]
+    make = {"uniform32": synth.uniform_32req, "batch64": synth.batch64_ctx8k, "skewed16": synth.skewed_16req}[args.config]
     wl = make(max_steps=total_steps)
     pt = wl.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
     verify = args.verify == "on"
@@ -819,7 +826,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{wl.name}: batch {wl.batch}, ctx 8192+U[0,1000]"
-                         if wl.name == "c4_headline" else wl.name),
+                         if wl.name == "batch64_ctx8k" else wl.name),
             "batch": wl.batch, "layers": wl.num_layers, "num_q_heads": wl.num_q_heads,
             "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
             "page_size": wl.page_size, "mean_ctx": round(float(wl.seq_lens0.mean()) + 1, 1),

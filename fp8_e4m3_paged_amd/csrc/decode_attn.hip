@@ -38,7 +38,7 @@ constexpr int kWaves = 4;                      // wavefronts per workgroup (wave
 constexpr int kWavesWide = 8;                  // shared mode when the grid fills one per CU
 constexpr int kAccStride = kDim + 4;           // padded LDS row (floats)
 constexpr float kLog2e = 1.4426950408889634f;
-// Partitions up to this many tokens run one per wavefront (see the kernel).
+// Partitions up to this many tokens may run in the persistent kernel.
 constexpr int kWaveModeMaxTokens = 2048;
 
 // Raw registers of one page pair: K and V tiles of pages a and b.
@@ -869,10 +869,11 @@ void attn_wave_kernel(
 // finds M and any invalid mark; the second takes 64 slots at a time (the
 // next 64 pairs loading meanwhile), and a ballot of the nonzero weights lists
 // the slots to read, whose outputs (two dims per lane, 512 B per slot) are
-// loaded up to 16 at a time before any is accumulated. Empty slots (weight 0)
+// loaded up to 8 at a time before any is accumulated. Empty slots (weight 0)
 // are never read.
 constexpr int kReduceWaves = 4;
-constexpr int kReduceBatch = 16;            // slot outputs in flight per wavefront
+constexpr int kReduceBatch = 8;             // slot outputs in flight per wavefront (16 requests
+                                            // up to 131k tokens: 7.3 us; 4: 8.3, 16: 7.9, 32: 10.9)
 
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -967,9 +968,10 @@ constexpr int64_t kNumCUs = 256;
 // LDS one workgroup may allocate without opting in to more.
 constexpr size_t kMaxLdsBytes = 64 * 1024;
 
-// Wave mode (one short partition per wavefront) only pays when there are
-// enough partitions for at least one 4-wave workgroup per CU; its LDS holds
-// two ints per request.
+// The persistent kernel (even split of the pages over the workgroups) runs
+// when there is more than one partition and enough of them for at least one
+// 4-wave workgroup per CU, and its LDS (merge area, page ids, two ints per
+// request) fits a workgroup.
 bool use_wave_partitions(const AttnArgs& a) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads;
     return a.num_partitions > 1 && a.partition_tokens <= kWaveModeMaxTokens &&

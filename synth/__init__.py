@@ -291,24 +291,24 @@ def _rng(cfg_index: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(1000 + cfg_index))
 
 
-def c1_tiny(max_steps: int = 1) -> Workload:
+def tiny_1req(max_steps: int = 1) -> Workload:
     """1 sequence, ctx 256 (appended token included), 16 pages of a 64-page pool.
 
     8 query heads / 1 KV head, head_dim 128, page 16, one layer; q, K, V all
     N(0, 1); random uint32 tags, all matching.
     """
     rng = _rng(0)
-    return _build("c1_tiny", 0, batch=1, layers=1, hq=8, hkv=1, d=128, page=16,
+    return _build("tiny_1req", 0, batch=1, layers=1, hq=8, hkv=1, d=128, page=16,
                   seq_lens0=[255], max_steps=max_steps,
                   pool_pages=lambda total: max(64, total), k_sigma=1.0, v_sigma=1.0,
                   q_sigma=1.0, garbage_tail=False, rng=rng)
 
 
-def c2_mixed(max_steps: int = 1) -> Workload:
+def mixed_8req(max_steps: int = 1) -> Workload:
     """8 sequences, ctx uniform in [1024, 8192], GQA 64/8, pool 2x, one stale tag."""
     rng = _rng(1)
     L = rng.integers(1024, 8192, size=8, endpoint=True)
-    wl = _build("c2_mixed", 1, batch=8, layers=1, hq=64, hkv=8, d=128, page=16,
+    wl = _build("mixed_8req", 1, batch=8, layers=1, hq=64, hkv=8, d=128, page=16,
                 seq_lens0=L - 1, max_steps=max_steps,
                 pool_pages=lambda total: 2 * total, k_sigma=1.0, v_sigma=0.5,
                 q_sigma=1.0, garbage_tail=True, rng=rng)
@@ -321,20 +321,20 @@ def c2_mixed(max_steps: int = 1) -> Workload:
     return wl
 
 
-def c3_uniform(max_steps: int = 1) -> Workload:
+def uniform_32req(max_steps: int = 1) -> Workload:
     """32 sequences, every ctx 8192, GQA 64/8, 8 layers; FP8 and BF16 caches."""
     rng = _rng(2)
-    return _build("c3_uniform", 2, batch=32, layers=8, hq=64, hkv=8, d=128, page=16,
+    return _build("uniform_32req", 2, batch=32, layers=8, hq=64, hkv=8, d=128, page=16,
                   seq_lens0=np.full(32, 8191), max_steps=max_steps,
                   pool_pages=lambda total: total + 32, k_sigma=1.0, v_sigma=0.5,
                   q_sigma=1.0, garbage_tail=False, rng=rng)
 
 
-def c4_headline(max_steps: int = 1) -> Workload:
+def batch64_ctx8k(max_steps: int = 1) -> Workload:
     """64 sequences, ctx 8192 + uniform [0, 1000], GQA 64/8, 8 layers, FP8."""
     rng = _rng(3)
     L = 8192 + rng.integers(0, 1000, size=64, endpoint=True)
-    return _build("c4_headline", 3, batch=64, layers=8, hq=64, hkv=8, d=128, page=16,
+    return _build("batch64_ctx8k", 3, batch=64, layers=8, hq=64, hkv=8, d=128, page=16,
                   seq_lens0=L - 1, max_steps=max_steps,
                   pool_pages=lambda total: total + 64, k_sigma=1.0, v_sigma=0.5,
                   q_sigma=1.0, garbage_tail=False, rng=rng)
@@ -352,7 +352,7 @@ def concurrency_point(batch: int, max_steps: int = 1) -> Workload:
                   q_sigma=1.0, garbage_tail=False, rng=np.random.default_rng(1005 + batch))
 
 
-def c5_skewed(max_steps: int = 2) -> Workload:
+def skewed_16req(max_steps: int = 2) -> Workload:
     """16 sequences, ctx log-uniform in [512, 131072] (two at 131072), 1 layer.
 
     Split-K partitions of 512 tokens; pool 1.25x; between steps 10% of the
@@ -364,7 +364,7 @@ def c5_skewed(max_steps: int = 2) -> Workload:
     L = np.floor(np.exp(u)).astype(np.int64)
     L = np.clip(L, 512, 131072)
     L[0] = L[1] = 131072
-    wl = _build("c5_skewed", 4, batch=16, layers=1, hq=64, hkv=8, d=128, page=16,
+    wl = _build("skewed_16req", 4, batch=16, layers=1, hq=64, hkv=8, d=128, page=16,
                 seq_lens0=L - 1, max_steps=max_steps,
                 pool_pages=lambda total: (5 * total + 3) // 4, k_sigma=1.0,
                 v_sigma=0.5, q_sigma=1.0, garbage_tail=True, rng=rng,
@@ -375,9 +375,9 @@ def c5_skewed(max_steps: int = 2) -> Workload:
 
 
 CONFIGS = {
-    "c1": c1_tiny,
-    "c2": c2_mixed,
-    "c3": c3_uniform,
-    "c4": c4_headline,
-    "c5": c5_skewed,
+    "tiny": tiny_1req,
+    "mixed8": mixed_8req,
+    "uniform32": uniform_32req,
+    "batch64": batch64_ctx8k,
+    "skewed16": skewed_16req,
 }

@@ -242,7 +242,7 @@ def test_workspace_and_partition_sizing(lib):
     import fp8_e4m3_paged_amd as k
     # one partition covers everything: no workspace
     assert k.paged_decode_attn_workspace_bytes(64, 64, 8, 8000, 8192) == 0
-    # C5-like: 16 requests, 64 heads, 131073 tokens at 512 -> 257 partitions, and
+    # 16 requests, 64 heads, up to 131073 tokens at 512 -> 257 partitions, and
     # one more partial slot per (request, query head) for the wave-mode kernel
     n = 16 * 64 * (257 + 1)
     ml = -(-(n * 2 * 4) // 256) * 256
@@ -262,7 +262,7 @@ def test_tile_layouts_are_permutations(key):
 
 
 def test_device_hash_twin_matches_host_on_cpu_torch():
-    wl = synth.c2_mixed()
+    wl = synth.mixed_8req()
     seq = torch.tensor([0, 3, 3, 7], dtype=torch.int32)
     pos = torch.tensor([0, 5, 1500, int(wl.seq_lens0[7])], dtype=torch.int32)
     for kind in ("k", "v"):

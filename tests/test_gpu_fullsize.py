@@ -67,9 +67,9 @@ def _check_group(st, layer, b, g, step, q_bits, out, label):
     say(f"{label}: layer {layer} request {b} (L={L}) group {g}: rel_l2={rel:.2e} max_abs={mx:.2e}")
 
 
-def test_c4_headline_full_size(kv):
-    wl = synth.c4_headline(max_steps=2)
-    say("c4: building 8-layer FP8 pools (batch 64, ctx 8192+U[0,1000])")
+def test_batch64_ctx8k_full_size(kv):
+    wl = synth.batch64_ctx8k(max_steps=2)
+    say("batch64: building 8-layer FP8 pools (batch 64, ctx 8192+U[0,1000])")
     st = DeviceState(wl, kv, cache="fp8", device=DEV)
     # verify on, automatic partition, fused append + attention: as benchmarked
     ab, outs, inputs = gpu_step(st, 0, fused=True)
@@ -77,27 +77,27 @@ def test_c4_headline_full_size(kv):
     L = wl.seq_lens_at(0)
     samples = [(int(np.argmax(L)), 7, 5), (int(np.argmin(L)), 0, 0), (17, 3, 2), (40, 5, 7)]
     for b, layer, g in samples:
-        _check_group(st, layer, b, g, 0, inputs[layer][0], outs[layer], "c4")
+        _check_group(st, layer, b, g, 0, inputs[layer][0], outs[layer], "batch64")
     for layer in st.layers:
         assert np.all(np.isfinite(outs[layer]))
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
-def test_c3_uniform_full_size(kv, cache):
-    wl = synth.c3_uniform(max_steps=1)
-    say(f"c3/{cache}: building 8-layer pools (batch 32, ctx 8192)")
+def test_uniform_32req_full_size(kv, cache):
+    wl = synth.uniform_32req(max_steps=1)
+    say(f"uniform32/{cache}: building 8-layer pools (batch 32, ctx 8192)")
     st = DeviceState(wl, kv, cache=cache, device=DEV)
     ab, outs, inputs = gpu_step(st, 0)
     assert not ab.any()
     for b, layer, g in [(0, 0, 0), (31, 7, 7), (13, 4, 3)]:
-        _check_group(st, layer, b, g, 0, inputs[layer][0], outs[layer], f"c3/{cache}")
+        _check_group(st, layer, b, g, 0, inputs[layer][0], outs[layer], f"uniform32/{cache}")
 
 
-def test_c3_fp8_equals_quantized_bf16(kv):
+def test_uniform_32req_fp8_equals_quantized_bf16(kv):
     """Same seeded values in both caches: the FP8 output approximates the BF16
     one within the error FP8 storage itself introduces (loose), while each
     matches its own oracle tightly (above)."""
-    wl = synth.c3_uniform(max_steps=1)
+    wl = synth.uniform_32req(max_steps=1)
     st8 = DeviceState(wl, kv, cache="fp8", device=DEV, layers=[0])
     _, o8, _ = gpu_step(st8, 0)
     del st8
@@ -105,14 +105,14 @@ def test_c3_fp8_equals_quantized_bf16(kv):
     st16 = DeviceState(wl, kv, cache="bf16", device=DEV, layers=[0])
     _, o16, _ = gpu_step(st16, 0)
     err = np.linalg.norm(o8[0] - o16[0]) / np.linalg.norm(o16[0])
-    say(f"c3: FP8 vs BF16 cache output rel_l2 = {err:.3e}")
+    say(f"uniform32: FP8 vs BF16 cache output rel_l2 = {err:.3e}")
     assert 1e-4 < err < 0.2
 
 
-def test_c5_skewed_split_k_and_churn(kv):
-    wl = synth.c5_skewed(max_steps=2)
+def test_skewed_16req_split_k_and_churn(kv):
+    wl = synth.skewed_16req(max_steps=2)
     stale = wl.notes["churn_stale"]
-    say(f"c5: lengths {sorted(wl.seq_lens_at(0).tolist())}, stale after churn {stale}")
+    say(f"skewed16: lengths {sorted(wl.seq_lens_at(0).tolist())}, stale after churn {stale}")
     st = DeviceState(wl, kv, cache="fp8", device=DEV)
     pt = wl.partition_tokens
     ab0, outs0, inputs0 = gpu_step(st, 0, partition_tokens=pt)
@@ -121,7 +121,7 @@ def test_c5_skewed_split_k_and_churn(kv):
     longest = int(np.argmax(L0))
     shortest = int(np.argmin(L0))
     for b, g in [(longest, 1), (shortest, 6), (5, 3)]:
-        _check_group(st, 0, b, g, 0, inputs0[0][0], outs0[0], "c5 step 0")
+        _check_group(st, 0, b, g, 0, inputs0[0][0], outs0[0], "skewed16 step 0")
     # between steps: 10% of the pages are freed and reallocated with a tag
     # bump; the two stale requests keep their old expectations
     wl.notes["churn_step"] = 1
@@ -135,4 +135,4 @@ def test_c5_skewed_split_k_and_churn(kv):
         assert np.all(outs1[0][b] == 0.0)
     ok = [b for b in range(wl.batch) if b not in stale]
     for b, g in [(ok[0], 0), (ok[-1], 4)]:
-        _check_group(st, 0, b, g, 1, inputs1[0][0], outs1[0], "c5 step 1")
+        _check_group(st, 0, b, g, 1, inputs1[0][0], outs1[0], "skewed16 step 1")

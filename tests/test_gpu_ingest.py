@@ -203,7 +203,7 @@ def test_ingest_layer_then_decode_attention(kv, cache):
     """The whole handoff on a mixed-length batch (64 q / 8 KV heads): scales
     calibrated on the GPU equal the oracle's bit for bit, the ingested pool
     equals the oracle's, and decode attention over it is within tolerance."""
-    wl = synth.c2_mixed(max_steps=1)
+    wl = synth.mixed_8req(max_steps=1)
     st = DeviceState(wl, kv, cache=cache, device=DEV, layers=[0], fill=False,
                      scales={0: (np.ones(8, np.float32), np.ones(8, np.float32))})
     kr, start = prompt_rows(wl, 0, "k", DEV)
@@ -259,7 +259,7 @@ def test_ingest_full_size_headline_prompts(kv):
     sampled heads compared bit for bit with the oracle's codes of the same
     seeded values under the GPU's scales, which themselves must be the
     scales of some amax at least as large as every sampled value."""
-    wl = synth.c4_headline(max_steps=1)
+    wl = synth.batch64_ctx8k(max_steps=1)
     st = DeviceState(wl, kv, cache="fp8", device=DEV, layers=[0], fill=False,
                      scales={0: (np.ones(8, np.float32), np.ones(8, np.float32))})
     kr, start = prompt_rows(wl, 0, "k", DEV)

@@ -118,41 +118,41 @@ def _full_step_check(kv, wl, cache="fp8", partition_tokens=0, label="", fused=Fa
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
-def test_c1_tiny_step(kv, cache):
-    st, _, ab = _full_step_check(kv, synth.c1_tiny(), cache, label=f"c1/{cache}")
+def test_tiny_1req_step(kv, cache):
+    st, _, ab = _full_step_check(kv, synth.tiny_1req(), cache, label=f"tiny/{cache}")
     assert not ab.any()
 
 
 @pytest.mark.parametrize("partition_tokens", [0, 512])
-def test_c2_mixed_step_with_stale_tag(kv, partition_tokens):
-    wl = synth.c2_mixed()
-    _, _, ab = _full_step_check(kv, wl, "fp8", partition_tokens, label=f"c2/p{partition_tokens}")
+def test_mixed_8req_step_with_stale_tag(kv, partition_tokens):
+    wl = synth.mixed_8req()
+    _, _, ab = _full_step_check(kv, wl, "fp8", partition_tokens, label=f"mixed8/p{partition_tokens}")
     assert np.flatnonzero(ab).tolist() == list(wl.stale)
 
 
-def test_c2_bf16_step(kv):
-    wl = synth.c2_mixed()
-    _, _, ab = _full_step_check(kv, wl, "bf16", 1024, label="c2/bf16")
+def test_mixed_8req_bf16_step(kv):
+    wl = synth.mixed_8req()
+    _, _, ab = _full_step_check(kv, wl, "bf16", 1024, label="mixed8/bf16")
     assert np.flatnonzero(ab).tolist() == list(wl.stale)
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
-def test_c1_fused_append_attention_step(kv, cache):
-    st, _, ab = _full_step_check(kv, synth.c1_tiny(), cache, label=f"c1 fused/{cache}",
+def test_tiny_1req_fused_append_attention_step(kv, cache):
+    st, _, ab = _full_step_check(kv, synth.tiny_1req(), cache, label=f"tiny fused/{cache}",
                                  fused=True)
     assert not ab.any()
 
 
 @pytest.mark.parametrize("partition_tokens", [0, 512, 4096])
-def test_c2_fused_step_with_stale_tag(kv, partition_tokens):
-    wl = synth.c2_mixed()
+def test_mixed_8req_fused_step_with_stale_tag(kv, partition_tokens):
+    wl = synth.mixed_8req()
     _, _, ab = _full_step_check(kv, wl, "fp8", partition_tokens,
-                                label=f"c2 fused/p{partition_tokens}", fused=True)
+                                label=f"mixed8 fused/p{partition_tokens}", fused=True)
     assert np.flatnonzero(ab).tolist() == list(wl.stale)
 
 
 def test_fused_equals_separate_calls_bit_for_bit(kv):
-    wl = synth.c2_mixed(max_steps=3)
+    wl = synth.mixed_8req(max_steps=3)
     a = DeviceState(wl, kv, device=DEV)
     b = DeviceState(wl, kv, device=DEV)
     for step in range(3):
@@ -170,7 +170,7 @@ def test_step_captured_in_a_graph_replays_like_eager(kv, partition_tokens):
     replayed several times with eager work and synchronisations between
     replays: every replay equals the eager run bit for bit. (Replaying the
     same step rewrites the same codes into the same slot.)"""
-    wl = synth.c2_mixed(max_steps=1)
+    wl = synth.mixed_8req(max_steps=1)
     st = DeviceState(wl, kv, device=DEV, layers=[0])
     seq = st.seq_lens(0)
     q, kn, vn = st.step_layer_inputs(0, 0)
@@ -231,7 +231,7 @@ def _attn(kv, st, layer, step, partition_tokens=0, sm=None, block_table=None, k_
 
 
 def test_partition_size_independence_and_page_permutation(kv):
-    wl = synth.c2_mixed()
+    wl = synth.mixed_8req()
     st = DeviceState(wl, kv, device=DEV)
     base, _ = _attn(kv, st, 0, 0, partition_tokens=16384)
     for pt in (16, 32, 48, 512, 1024, 4096, 0):
@@ -253,7 +253,7 @@ def test_partition_size_independence_and_page_permutation(kv):
 
 
 def test_zero_temperature_is_mean_of_v(kv):
-    wl = synth.c2_mixed()
+    wl = synth.mixed_8req()
     st = DeviceState(wl, kv, device=DEV)
     out, _ = _attn(kv, st, 0, 0, sm=0.0, partition_tokens=1024)
     vlog = device_pool_logical(st, 0)[1]
@@ -381,8 +381,8 @@ def test_edge_abort_bad_ids_and_overlong(kv, cache):
     assert np.all(got[3] == 0)
 
 
-def _runs_one_partition_per_wave(batch, hkv, max_len, pt):
-    """Whether the library picks its persistent wave-per-partition kernel
+def _uses_persistent_kernel(batch, hkv, max_len, pt):
+    """Whether the library picks its persistent kernel
     (short partitions and enough of them to give every CU a 4-wave group)."""
     parts = -(-max_len // pt)
     return parts > 1 and pt <= 2048 and batch <= 4096 and batch * hkv * parts >= 1024
@@ -391,7 +391,7 @@ def _runs_one_partition_per_wave(batch, hkv, max_len, pt):
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
 @pytest.mark.parametrize("hq", [64, 128])
 def test_wave_mode_edges_aborts_and_bad_ids(kv, cache, hq):
-    """A batch large enough for the wave-per-partition kernel, with ragged
+    """A batch large enough for the persistent kernel, with ragged
     lengths (1 token, page and partition boundaries, empty requests) and
     aborted and badly mapped requests between valid ones, so the kernel's
     per-request numbering of its work items has to skip them."""
@@ -409,8 +409,8 @@ def test_wave_mode_edges_aborts_and_bad_ids(kv, cache, hq):
     zero = sorted({b for b, L in enumerate(lens) if L == 0} | {5, 60, 12} |
                   set(np.flatnonzero(abort).tolist()))
     want = _edge_oracle(e, cache, lens, abort=abort, bt=bt)
-    for pt in (16, 32, 64):
-        assert _runs_one_partition_per_wave(len(lens), hkv, max(lens), pt)
+    for pt in (16, 32, 48, 64, 80):            # 1 to 5 pages per partition, odd ones too
+        assert _uses_persistent_kernel(len(lens), hkv, max(lens), pt)
         got = _edge_run(kv, e, cache, abort=abort, partition_tokens=pt, bt=bt)
         helpers.check_attention(got, want, zero_rows=zero,
                                 label=f"wave mode {cache} G={hq // hkv} p{pt}")
@@ -452,7 +452,7 @@ def test_maximum_partition_count(kv, cache):
     lens = [131_072, 5_000, 0]
     need = sum(max(1, -(-L // 16)) for L in lens)
     e = _edge_state(kv, cache, 8, 1, lens, pool_pages=need + 4)
-    assert _runs_one_partition_per_wave(len(lens), 1, max(lens), 16)
+    assert _uses_persistent_kernel(len(lens), 1, max(lens), 16)
     got = _edge_run(kv, e, cache, partition_tokens=16)
     want = _edge_oracle(e, cache, lens)
     helpers.check_attention(got, want, zero_rows=[2], label=f"8192 partitions {cache}")
@@ -509,7 +509,7 @@ def test_wave_mode_even_page_split_long_partitions(kv, cache):
     zero = [b for b, L in enumerate(lens) if L == 0]
     want = _edge_oracle(e, cache, lens)
     for pt in (256, 1024, 2048):
-        assert _runs_one_partition_per_wave(len(lens), hkv, max(lens), pt)
+        assert _uses_persistent_kernel(len(lens), hkv, max(lens), pt)
         got = _edge_run(kv, e, cache, partition_tokens=pt)
         helpers.check_attention(got, want, zero_rows=zero, label=f"page split {cache} p{pt}")
 

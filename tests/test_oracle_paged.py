@@ -229,7 +229,7 @@ def test_aborted_empty_and_unmapped_requests_output_zero():
 # tag check
 # ---------------------------------------------------------------------------
 def test_verify_all_matching_is_all_zero():
-    for make in (synth.c1_tiny, synth.c3_uniform, synth.c4_headline):
+    for make in (synth.tiny_1req, synth.uniform_32req, synth.batch64_ctx8k):
         wl = make()
         ab = paged.verify_tags(wl.pool_tags, wl.block_table, wl.expected_tags,
                                wl.seq_lens_at(0), P)
@@ -237,7 +237,7 @@ def test_verify_all_matching_is_all_zero():
 
 
 def test_verify_flags_exactly_the_stale_request_and_ignores_the_tail():
-    wl = synth.c2_mixed()
+    wl = synth.mixed_8req()
     ab = paged.verify_tags(wl.pool_tags, wl.block_table, wl.expected_tags,
                            wl.seq_lens_at(0), P)
     assert np.flatnonzero(ab).tolist() == list(wl.stale)
@@ -267,7 +267,7 @@ def test_verify_page_boundaries_and_bad_ids():
 
 
 def test_churn_aborts_exactly_the_two_stale_requests():
-    wl = synth.c5_skewed()
+    wl = synth.skewed_16req()
     ab0 = paged.verify_tags(wl.pool_tags, wl.block_table, wl.expected_tags,
                             wl.seq_lens_at(0), P)
     assert not ab0.any()

@@ -30,8 +30,8 @@ def test_table_is_a_bf16_normal():
 
 
 def test_values_are_deterministic_and_regenerable_per_request():
-    a = synth.c2_mixed()
-    b = synth.c2_mixed()
+    a = synth.mixed_8req()
+    b = synth.mixed_8req()
     assert np.array_equal(a.block_table, b.block_table)
     assert np.array_equal(a.pool_tags, b.pool_tags)
     x = a.kv_bits(0, "k", 3, 0, 40)
@@ -44,7 +44,7 @@ def test_values_are_deterministic_and_regenerable_per_request():
 
 
 def test_value_statistics():
-    wl = synth.c2_mixed()
+    wl = synth.mixed_8req()
     k = (wl.kv_bits(0, "k", 0, 0, 512).astype(np.uint32) << 16).view(np.float32)
     v = (wl.kv_bits(0, "v", 0, 0, 512).astype(np.uint32) << 16).view(np.float32)
     assert abs(k.std() - 1.0) < 0.01 and abs(v.std() - 0.5) < 0.005
@@ -52,30 +52,30 @@ def test_value_statistics():
 
 
 def test_config_shapes():
-    c1 = synth.c1_tiny()
-    assert c1.num_pages == 64 and c1.block_table.shape == (1, 16)
-    assert int(c1.seq_lens_at(0)[0]) == 256
-    assert len(set(c1.block_table[0].tolist())) == 16
-    c2 = synth.c2_mixed()
-    L = c2.seq_lens_at(0)
+    tiny = synth.tiny_1req()
+    assert tiny.num_pages == 64 and tiny.block_table.shape == (1, 16)
+    assert int(tiny.seq_lens_at(0)[0]) == 256
+    assert len(set(tiny.block_table[0].tolist())) == 16
+    mixed = synth.mixed_8req()
+    L = mixed.seq_lens_at(0)
     assert L.min() >= 1024 and L.max() <= 8192
-    assert c2.num_pages == 2 * int(c2.pages_allocated.sum())
-    c4 = synth.c4_headline()
-    L = c4.seq_lens_at(0)
-    assert L.min() >= 8192 and L.max() <= 9192 and c4.batch == 64 and c4.num_layers == 8
-    c5 = synth.c5_skewed()
-    L = c5.seq_lens_at(0)
+    assert mixed.num_pages == 2 * int(mixed.pages_allocated.sum())
+    batch64 = synth.batch64_ctx8k()
+    L = batch64.seq_lens_at(0)
+    assert L.min() >= 8192 and L.max() <= 9192 and batch64.batch == 64 and batch64.num_layers == 8
+    skewed = synth.skewed_16req()
+    L = skewed.seq_lens_at(0)
     assert (L == 131072).sum() >= 2 and L.min() >= 512
-    assert c5.partition_tokens == 512
+    assert skewed.partition_tokens == 512
     # no physical page is owned twice
-    for wl in (c1, c2, c4, c5):
+    for wl in (tiny, mixed, batch64, skewed):
         ids = np.concatenate([wl.block_table[b, :wl.pages_allocated[b]] for b in range(wl.batch)])
         assert len(np.unique(ids)) == len(ids)
         assert ids.min() >= 0 and ids.max() < wl.num_pages
 
 
 def test_initial_scales_are_amax_over_448():
-    wl = synth.c1_tiny()
+    wl = synth.tiny_1req()
     ks, vs = wl.initial_scales(0)
     k = (wl.kv_bits(0, "k", 0, 0, 255).astype(np.uint32) << 16).view(np.float32)
     assert ks.dtype == np.float32
