@@ -13,8 +13,8 @@ own pool, FP8 e4m3 cache, tag check on every step.
 
 Prints ONE JSON line. ``value`` is the algorithmic HBM throughput of the
 whole step in GB/s; ``seq_steps_per_s`` is batch * steps / time. The
-``roofline`` object is the attention kernel measured alone with HIP events
-on its launch stream; ``cpu_baseline`` is the CPU oracle timed on a bounded
+``roofline`` object is the attention launches timed with HIP events on
+their launch stream in a pass of their own; ``cpu_baseline`` is the CPU oracle timed on a bounded
 sample of the same workload on this host.
 """
 
@@ -668,8 +668,11 @@ def main():
     sm = 1.0 / math.sqrt(wl.head_dim)
     stream = torch.cuda.current_stream()
 
+    # fused: one event pair around each step's back-to-back layer launches (the
+    # per-launch time is that span over the layer count, so the events' own
+    # cost is not counted once per launch); separate calls: a pair per attention call
     ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps * wl.num_layers)]
+               for _ in range(args.steps * (1 if fused else wl.num_layers))]
 
     def run_step(s, timed_slot=None, check=verify, stream=stream):
         abort = st.abort if check else None
@@ -679,15 +682,15 @@ def main():
         for layer in range(wl.num_layers):
             q, kn, vn = inputs[s][layer]
             if fused:
-                if timed_slot is not None:
-                    ev_attn[timed_slot + layer][0].record(stream)
+                if timed_slot is not None and layer == 0:
+                    ev_attn[timed_slot][0].record(stream)
                 kv.paged_decode_attn_append(q, kn, vn, st.k_pool[layer], st.v_pool[layer],
                                             st.k_scale[layer], st.v_scale[layer], st.block_table,
                                             seq_lens[s], max_len, outs[layer], sm, workspace=ws,
                                             abort=abort, partition_tokens=pt, cache_dtype=cd,
                                             stream=stream)
-                if timed_slot is not None:
-                    ev_attn[timed_slot + layer][1].record(stream)
+                if timed_slot is not None and layer == wl.num_layers - 1:
+                    ev_attn[timed_slot][1].record(stream)
                 continue
             if fp8:
                 kv.kv_append_quant(kn, vn, st.tok_seq, tok_pos[s], st.block_table,
@@ -738,14 +741,14 @@ def main():
     elapsed_ms = start.elapsed_time(end)
     ms_per_step = elapsed_ms / args.steps
 
-    # pass 2: the next steps again, each attention call bracketed by events on
-    # its launch stream (the event pair also spans the call's dispatch latency)
+    # pass 2: the next steps again with HIP events on the launch stream: around
+    # each step's layer launches (fused), or around each attention call
     base2 = args.warmup + args.steps
     torch.cuda.synchronize()
     for i in range(args.steps):
-        run_step(base2 + i, timed_slot=i * wl.num_layers)
+        run_step(base2 + i, timed_slot=i if fused else i * wl.num_layers)
     torch.cuda.synchronize()
-    attn_ms = [a.elapsed_time(b) for a, b in ev_attn]
+    attn_ms = [a.elapsed_time(b) / (wl.num_layers if fused else 1) for a, b in ev_attn]
     attn_avg_ms = float(np.mean(attn_ms))
 
     by = [step_bytes(wl, wl.seq_lens_at(args.warmup + i), cache, verify)
