@@ -670,10 +670,11 @@ void attn_partition_kernel(
 // Persistent kernel for short partitions (<= 2048 tokens), used when there
 // are enough of them to give every CU work. The (request, KV head, page)
 // units of the requests that have work are numbered request by request, then
-// KV head, then page; each workgroup first builds the per-request prefix of
-// page counts in LDS, then workgroup j of the G that share the work takes
-// the contiguous range of units [j U / G, (j + 1) U / G), so the split is even
-// to within a page. G is the grid size, lowered if needed so that every range
+// KV head, then page, each (request, KV head) led by kPiecePenalty units that
+// hold no page (the cost of one more piece); each workgroup first builds the
+// per-request prefix of unit counts in LDS, then workgroup j of the G that
+// share the work takes the contiguous range of units [j U / G, (j + 1) U / G),
+// so the split is even to within a unit. G is the grid size, lowered if needed so that every range
 // holds at least one partition's worth of pages. A range is streamed as runs,
 // one per (request, KV head) it touches, cut into pieces of at most
 // kCoopRunPages pages that end on partition boundaries. The four wavefronts
@@ -686,14 +687,23 @@ void attn_partition_kernel(
 // request is owned by exactly one piece. A piece writes its partial to the
 // first slot it owns and marks the others empty (max -inf, sum 0), which the
 // reduction weighs 0. Only a workgroup's first piece can start inside a
-// partition; since a range holds at least one partition's worth of pages and
-// a piece reaches at least the second partition boundary after its start,
-// such a piece streams the next partition's first page, or else ends the
+// partition. A range holds at least one partition's worth of units, and the
+// units after a page of a (request, KV head) up to its end are all pages, so
+// such a piece either reaches the next partition's first page (a piece runs
+// to at least the second partition boundary after its start) or ends the
 // (request, KV head) inside its last partition and takes the extra slot.
 // Aborted, empty or unmappable requests have no units (the reduction writes
 // their zeros).
 constexpr int kWaveModeMaxBatch = 4096;     // LDS: 2 * batch + 1 ints
 constexpr int kCoopRunPages = 512;          // pages of one piece (LDS page ids)
+#ifndef KVFP8_PIECE_PENALTY
+#define KVFP8_PIECE_PENALTY 8
+#endif
+// Units counted at the start of every (request, KV head) on top of its pages:
+// the cost of starting a piece (pipeline fill and drain, LDS merge, partial
+// store) in page-equivalents, so shares that cross many short requests get
+// fewer pages.
+constexpr int kPiecePenalty = KVFP8_PIECE_PENALTY;
 static_assert(kCoopRunPages >= 2 * (kWaveModeMaxTokens / kPage) - 1,
               "a piece starting inside a partition must reach the next partition's start");
 
@@ -741,7 +751,7 @@ void attn_wave_kernel(
             const int L = seq_lens[b];
             sm_len[b] = L;
             if (request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride))
-                local += (L + kPage - 1) / kPage;
+                local += (L + kPage - 1) / kPage + kPiecePenalty;
         }
         int incl = local;                                      // inclusive scan in the wave
 #pragma unroll
@@ -760,7 +770,7 @@ void attn_wave_kernel(
             sm_pre[b] = run;
             const int L = sm_len[b];
             if (request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride))
-                run += (L + kPage - 1) / kPage;
+                run += (L + kPage - 1) / kPage + kPiecePenalty;
         }
         if (tid == kThreads - 1) {
             int total = 0;
@@ -786,9 +796,15 @@ void attn_wave_kernel(
         const int b = __builtin_amdgcn_readfirstlane(lo);
         const int L = __builtin_amdgcn_readfirstlane(sm_len[b]);
         const int npg_b = (L + kPage - 1) / kPage;
+        const int ext_b = npg_b + kPiecePenalty;               // units of one (b, g)
         const int local = static_cast<int>(it - static_cast<int64_t>(sm_pre[b]) * hkv);
-        const int g = __builtin_amdgcn_readfirstlane(local / npg_b);
-        const int k0 = __builtin_amdgcn_readfirstlane(local % npg_b);
+        const int g = __builtin_amdgcn_readfirstlane(local / ext_b);
+        const int r = __builtin_amdgcn_readfirstlane(local % ext_b);
+        if (r < kPiecePenalty) {                               // the (b, g)'s leading units
+            it += min(static_cast<int64_t>(kPiecePenalty - r), u_end - it);
+            continue;                                          // uniform over the workgroup
+        }
+        const int k0 = r - kPiecePenalty;
         // the piece: pages k0 .. k_end - 1 of (b, g)
         const int cap = (k0 + kCoopRunPages) / ppp * ppp;
         const int k_end = static_cast<int>(
