@@ -252,10 +252,14 @@ def test_partition_size_independence_and_page_permutation(kv):
         assert np.array_equal(a, b)
 
 
-def test_zero_temperature_is_mean_of_v(kv):
+@pytest.mark.parametrize("partition_tokens", [1024, 64])
+def test_zero_temperature_is_mean_of_v(kv, partition_tokens):
+    """sm_scale = 0: every score is 0 and the output is the plain mean of V.
+    1,024-token partitions run the shared kernel, 64-token ones (8 requests x 8
+    KV heads x up to 128 partitions) the persistent one."""
     wl = synth.mixed_8req()
     st = DeviceState(wl, kv, device=DEV)
-    out, _ = _attn(kv, st, 0, 0, sm=0.0, partition_tokens=1024)
+    out, _ = _attn(kv, st, 0, 0, sm=0.0, partition_tokens=partition_tokens)
     vlog = device_pool_logical(st, 0)[1]
     for b in range(wl.batch):
         L = int(wl.seq_lens0[b])
