@@ -613,7 +613,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library runs on one GPU and has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

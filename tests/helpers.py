@@ -101,7 +101,7 @@ def gather_device_request(pool_host_tiles, block_table_row, L, kind, cache):
 
 
 def check_attention(got: np.ndarray, want: np.ndarray, zero_rows=(), label=""):
-    """Spec tolerance: rel-L2 <= 1e-3 and max |err| <= 5e-3 over the
+    """The attention tolerance: rel-L2 <= 1e-3 and max |err| <= 5e-3 over the
     non-aborted requests; requests listed in zero_rows must be exactly 0."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
