@@ -881,7 +881,8 @@ void attn_wave_kernel(
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p acc_p / sum_p w_p l_p
 // Requests that are aborted, empty, too long, or that a partition marked as
 // mapped to an invalid page (l_p < 0) get zeros. One wavefront per (b, h),
-// four per workgroup, no barriers: a first pass over the (max, sum) pairs
+// four per workgroup, no barriers (rows of more than 64 slots: see COOP
+// below): a first pass over the (max, sum) pairs
 // finds M and any invalid mark; the second takes 64 slots at a time (the
 // next 64 pairs loading meanwhile), and a ballot of the nonzero weights lists
 // the slots to read, whose outputs (two dims per lane, 512 B per slot) are
@@ -901,16 +902,26 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// COOP = false: one wavefront per (b, h), four rows per workgroup. COOP = true
+// (rows of more than 64 slots): one row per workgroup, its four wavefronts
+// taking every fourth 64-slot chunk; they agree on M (and any invalid mark)
+// through LDS, then wavefront 0 adds the four partial sums.
+template <bool COOP>
 __global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_acc,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, int32_t bt_stride,
     const uint8_t* __restrict__ abort, const float* __restrict__ v_scale,
     float* __restrict__ out, int32_t batch, int32_t hq, int32_t hkv, int32_t part_tokens,
     int32_t n_parts, int32_t extra_slot) {
+    __shared__ float sm_max[kReduceWaves];
+    __shared__ int sm_bad[kReduceWaves];
+    __shared__ float sm_sum[kReduceWaves];
+    __shared__ f32x2 sm_num[COOP ? kReduceWaves : 1][64];
     const int lane = threadIdx.x % 64;
-    const int64_t bh = static_cast<int64_t>(blockIdx.x) * kReduceWaves +
-                       __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    if (bh >= static_cast<int64_t>(batch) * hq) return;       // wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int64_t bh = COOP ? static_cast<int64_t>(blockIdx.x)
+                            : static_cast<int64_t>(blockIdx.x) * kReduceWaves + wave;
+    if (bh >= static_cast<int64_t>(batch) * hq) return;       // uniform per row
     const int b = static_cast<int>(bh / hq);
     const int h = static_cast<int>(bh % hq);
     f32x2* o = reinterpret_cast<f32x2*>(out + bh * kDim) + lane;
@@ -918,7 +929,7 @@ __global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
     const bool aborted = abort != nullptr && abort[b] != 0;
     if (aborted || L < 1 || L > max_seq_len ||
         (static_cast<int64_t>(L) + kPage - 1) / kPage > bt_stride) {
-        *o = f32x2{0.f, 0.f};
+        if (!COOP || wave == 0) *o = f32x2{0.f, 0.f};
         return;
     }
     // the request's partitions, plus the slot after them when the persistent
@@ -927,32 +938,47 @@ __global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
     const size_t n_slots = partial_slots(n_parts);
     const f32x2* ml = reinterpret_cast<const f32x2*>(part_ml) + bh * n_slots;
     const float* acc = part_acc + bh * n_slots * kDim + 2 * lane;
+    // this wavefront's 64-slot chunks: c0, c0 + cstep, ...
+    const int c0 = COOP ? 64 * wave : 0;
+    constexpr int cstep = COOP ? 64 * kReduceWaves : 64;
 
     constexpr f32x2 kEmpty = {-INFINITY, 0.f};
     float mx = -INFINITY;
     bool bad = false;
-    for (int i0 = lane; i0 < np; i0 += 4 * 64) {              // four loads in flight
+    for (int i0 = c0 + lane; i0 < np; i0 += 4 * cstep) {      // four loads in flight
         f32x2 e[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) e[k] = i0 + 64 * k < np ? ml[i0 + 64 * k] : kEmpty;
+        for (int k = 0; k < 4; ++k) e[k] = i0 + cstep * k < np ? ml[i0 + cstep * k] : kEmpty;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             bad |= e[k][1] < 0.f;
             mx = fmaxf(mx, e[k][0]);
         }
     }
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-        *o = f32x2{0.f, 0.f};
+    bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    float M = wave_max(mx);
+    if constexpr (COOP) {
+        if (lane == 0) {
+            sm_max[wave] = M;
+            sm_bad[wave] = any_bad;
+        }
+        __syncthreads();
+        for (int w = 0; w < kReduceWaves; ++w) {
+            M = fmaxf(M, sm_max[w]);
+            any_bad |= sm_bad[w] != 0;
+        }
+    }
+    if (any_bad) {                                            // uniform per row
+        if (!COOP || wave == 0) *o = f32x2{0.f, 0.f};
         return;
     }
-    const float M = wave_max(mx);
     const float M_use = M == -INFINITY ? 0.f : M;
     float lsum = 0.f;
     f32x2 num = {0.f, 0.f};
-    f32x2 e_next = lane < np ? ml[lane] : kEmpty;
-    for (int c = 0; c < np; c += 64) {
+    f32x2 e_next = c0 + lane < np ? ml[c0 + lane] : kEmpty;
+    for (int c = c0; c < np; c += cstep) {
         const f32x2 e = e_next;                               // the next chunk's pairs load
-        e_next = c + 64 + lane < np ? ml[c + 64 + lane] : kEmpty;   // under this one's reads
+        e_next = c + cstep + lane < np ? ml[c + cstep + lane] : kEmpty;   // under this one's reads
         const float w = exp2f(e[0] - M_use);                  // 0 for an empty slot
         lsum += w * e[1];
         uint64_t mask = __builtin_amdgcn_ballot_w64(w > 0.f);
@@ -973,7 +999,19 @@ __global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
             }
         }
     }
-    const float lt = wave_sum(lsum);
+    float lt = wave_sum(lsum);
+    if constexpr (COOP) {
+        sm_num[wave][lane] = num;
+        if (lane == 0) sm_sum[wave] = lt;
+        __syncthreads();
+        if (wave != 0) return;
+        lt = 0.f;
+        num = f32x2{0.f, 0.f};
+        for (int w = 0; w < kReduceWaves; ++w) {
+            lt += sm_sum[w];
+            num += sm_num[w][lane];
+        }
+    }
     const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
     *o = lt > 0.f ? num * (vs / lt) : f32x2{0.f, 0.f};
 }
@@ -1053,12 +1091,16 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_partitions == 1) return e;
     const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
-    hipLaunchKernelGGL(reduce_partials_kernel,
-                       dim3(static_cast<uint32_t>((rows + kReduceWaves - 1) / kReduceWaves)),
-                       dim3(kReduceWaves * 64), 0, stream, a.part_ml, a.part_acc, a.seq_lens,
-                       a.max_seq_len, a.bt_stride, a.abort, fp8 ? a.v_scale : nullptr, a.out,
-                       a.batch, a.num_q_heads, a.num_kv_heads, a.partition_tokens,
-                       a.num_partitions, use_wave_partitions(a) ? 1 : 0);
+    const int extra = use_wave_partitions(a) ? 1 : 0;
+#define KVFP8_REDUCE(CO, WGS)                                                                    \
+    hipLaunchKernelGGL(reduce_partials_kernel<CO>, dim3(static_cast<uint32_t>(WGS)),             \
+                       dim3(kReduceWaves * 64), 0, stream, a.part_ml, a.part_acc, a.seq_lens,    \
+                       a.max_seq_len, a.bt_stride, a.abort, fp8 ? a.v_scale : nullptr, a.out,    \
+                       a.batch, a.num_q_heads, a.num_kv_heads, a.partition_tokens,               \
+                       a.num_partitions, extra)
+    if (a.num_partitions + extra > 64) KVFP8_REDUCE(true, rows);
+    else KVFP8_REDUCE(false, (rows + kReduceWaves - 1) / kReduceWaves);
+#undef KVFP8_REDUCE
     return hipGetLastError();
 }
 

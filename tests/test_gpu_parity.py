@@ -451,8 +451,8 @@ def test_verify_tags_cases(kv):
 def test_maximum_partition_count(kv, cache):
     """131,072 tokens in 16-token partitions: 8,192 partitions, the most the
     library accepts, in the persistent kernel. The reduce then combines 8,193
-    slots of the long request's rows, a few hundred of them non-empty, in
-    129 passes of 64; the short request and an empty one share the launch."""
+    slots of the long request's rows, a few hundred of them non-empty, four
+    wavefronts per row; the short request and an empty one share the launch."""
     lens = [131_072, 5_000, 0]
     need = sum(max(1, -(-L // 16)) for L in lens)
     e = _edge_state(kv, cache, 8, 1, lens, pool_pages=need + 4)
@@ -460,6 +460,12 @@ def test_maximum_partition_count(kv, cache):
     got = _edge_run(kv, e, cache, partition_tokens=16)
     want = _edge_oracle(e, cache, lens)
     helpers.check_attention(got, want, zero_rows=[2], label=f"8192 partitions {cache}")
+    # an invalid page id deep inside the long request, and the short one aborted:
+    # both rows zero, seen by whichever wavefront of the reduction holds the slot
+    bt = e["bt"].copy()
+    bt[0, 6_000] = -1
+    got = _edge_run(kv, e, cache, partition_tokens=16, bt=bt, abort=[0, 1, 0])
+    assert np.all(got[0] == 0) and np.all(got[1] == 0) and np.all(got[2] == 0)
 
 
 def test_verify_tags_long_rows(kv):
