@@ -99,8 +99,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--graph", default="off", choices=["on", "off"],
-                    help="time the steps as captured HIP graphs (one per step, captured "
-                         "before timing) instead of eager launches (measured slower here)")
+                    help="step and sweep modes: time the steps as captured HIP graphs (one "
+                         "per step, captured before timing) instead of eager launches")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--mode", default="step", choices=["step", "copy", "ingest", "sweep", "gemv"],
                     help="copy: time a plain device copy of --copy-mib MiB (counter "
@@ -465,19 +465,34 @@ def sweep_bench(args):
             cd = kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16
             sm = 1.0 / math.sqrt(wl.head_dim)
 
-            def step(i):
-                kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens[i],
-                                  st.abort)
+            def step(i, prepare=False):
+                calls = [kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags,
+                                           seq_lens[i], st.abort, prepare=prepare)]
                 for l in range(wl.num_layers):
                     q, kn, vn = inputs[i][l]
-                    kv.paged_decode_attn_append(q, kn, vn, st.k_pool[l], st.v_pool[l],
-                                                st.k_scale[l], st.v_scale[l], st.block_table,
-                                                seq_lens[i], wl.max_seq_len, outs[l], sm,
-                                                workspace=ws, abort=st.abort, cache_dtype=cd)
+                    calls.append(kv.paged_decode_attn_append(
+                        q, kn, vn, st.k_pool[l], st.v_pool[l], st.k_scale[l], st.v_scale[l],
+                        st.block_table, seq_lens[i], wl.max_seq_len, outs[l], sm, workspace=ws,
+                        abort=st.abort, cache_dtype=cd, prepare=prepare))
+                return calls
 
             for i in range(args.warmup):
                 step(i)
             torch.cuda.synchronize()
+            # eager: each timed step's calls are checked once here and enqueued from
+            # their prepared form (the small points would otherwise time the host's
+            # per-call checks); with --graph on, each timed step is replayed from a
+            # HIP graph captured here
+            graphs = None
+            prepared = [step(args.warmup + i, prepare=True) for i in range(args.steps)]
+            if args.graph == "on":
+                graphs = []
+                for i in range(args.steps):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        step(args.warmup + i)
+                    graphs.append(g)
+                torch.cuda.synchronize()
             # the same K steps timed three times (a step rewrites its own new token,
             # so repeating it is the same work); the median, since the windows of
             # the small points are a few ms and the first can catch the clocks rising
@@ -486,7 +501,11 @@ def sweep_bench(args):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
                 for i in range(args.steps):
-                    step(args.warmup + i)
+                    if graphs is not None:
+                        graphs[i].replay()
+                    else:
+                        for call in prepared[i]:
+                            call()
                 b.record()
                 torch.cuda.synchronize()
                 windows.append(a.elapsed_time(b) / args.steps)
@@ -498,7 +517,7 @@ def sweep_bench(args):
             points.append(pt)
             log(args, f"{cache} B={B}: {ms:.3f} ms/step, {B / ms * 1e3:.0f} seq-steps/s, "
                       f"{byts / ms / 1e6:.0f} GB/s")
-            del st, inputs, outs, ws
+            del st, inputs, outs, ws, graphs, prepared
             torch.cuda.empty_cache()
     best = {c: max((p["seq_steps_per_s"] for p in points if p["cache"] == c and p["fits"]),
                    default=None) for c in ("bf16", "fp8")}
@@ -508,7 +527,9 @@ def sweep_bench(args):
         "steps": args.steps, "warmup": args.warmup, "dtype": "e4m3 / bf16", "data": "synthetic",
         "config": {"workload": "headline length draw (8192 + U[0,1000]), first B requests, "
                                "8 layers, 64 q / 8 KV heads, tag check on, fused append",
-                   "pool_budget_GB": round(budget / 1e9, 3)},
+                   "pool_budget_GB": round(budget / 1e9, 3),
+                   "launch": "HIP graph per step" if args.graph == "on"
+                             else "eager, calls prepared before timing"},
         "best": best,
         "fp8_over_best_bf16": round(best["fp8"] / best["bf16"], 3) if best["bf16"] else None,
         "points": points,

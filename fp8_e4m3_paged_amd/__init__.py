@@ -17,6 +17,9 @@ wq_gemv;
 plus ``decode_step``, which enqueues one decode step (tag check, then per
 layer append and attention) in the order the operations require, and
 ``ingest_layer``, which calibrates one layer's scales and writes its prompts.
+The decode entry points also take ``prepare=True``, which checks the call
+once and returns it as a ``Prepared`` to be enqueued again at the cost of the
+C call alone.
 ``PagePool`` wraps the host page pool and tag tracker of include/kvpool.h
 (kv_pool_create, kv_pool_alloc, kv_pool_free, kv_pool_tags,
 kv_pool_record_check, kv_pool_get_stats, kv_pool_destroy).
@@ -34,7 +37,7 @@ __all__ = [
     "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
     "kv_amax_accumulate", "kv_scales_from_amax", "kv_ingest_prefill", "ingest_layer",
     "PagePool", "KV_ERR_EXHAUSTED", "KV_ERR_STATE",
-    "WQ_INT4", "WQ_FP8_E4M3", "wq_packed_bytes", "wq_quantize_pack", "wq_gemv",
+    "WQ_INT4", "WQ_FP8_E4M3", "wq_packed_bytes", "wq_quantize_pack", "wq_gemv", "Prepared",
 ]
 
 WQ_INT4 = 0
@@ -153,6 +156,42 @@ def _check(fn, status):
         raise KvError(fn, status)
 
 
+class Prepared:
+    """One checked call of a C entry point, with its arguments fixed.
+
+    Calling the object enqueues the same call again, on the stream fixed when
+    it was prepared, without re-checking the tensors or rebuilding the
+    argument list: a decode loop whose buffers stay in place pays the host-side
+    checks once instead of on every layer of every step. The object holds
+    references to the tensors it was prepared with, so their memory stays
+    valid; their contents (lengths, flags, new tokens) may change between
+    calls. A call that the library refuses raises ``KvError``.
+    """
+
+    __slots__ = ("name", "_fn", "_args", "_keep")
+
+    def __init__(self, name, fn, args, keep):
+        self.name = name
+        self._fn = fn
+        # ctypes objects of the declared types: the per-call conversion is then a type check
+        self._args = tuple(a if a is None else t(a) for t, a in zip(fn.argtypes, args))
+        self._keep = keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise KvError(self.name, st)
+
+
+def _call(name, args, prepare, keep):
+    """Run entry point ``name`` now, or, with ``prepare``, return it as a Prepared."""
+    fn = getattr(load(), name)
+    if prepare:
+        return Prepared(name, fn, args, keep)
+    _check(name, fn(*args))
+    return None
+
+
 def _tile_bytes(fp8):
     """Bytes of one (page, KV head) tile: 16 tokens x 128 dims of e4m3 or bf16."""
     return PAGE_SIZE * HEAD_DIM * (1 if fp8 else 2)
@@ -188,38 +227,46 @@ def _check_scales(k_scale, v_scale, hkv, fp8):
             raise ValueError(f"{name} must hold {hkv} scales (one per KV head)")
 
 
+_DTYPES = None
+
+
 def _dt():
-    import torch
-    return dict(
-        i32=(torch.int32,), u32=(torch.int32, torch.uint32), u8=(torch.uint8,),
-        bf16=(torch.bfloat16, torch.int16, torch.uint16), f32=(torch.float32,),
-        pool=(torch.uint8, torch.int16, torch.bfloat16, torch.uint16),
-    )
+    """Accepted torch dtypes per argument kind (built once, on first use)."""
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
+        _DTYPES = dict(
+            i32=(torch.int32,), u32=(torch.int32, torch.uint32), u8=(torch.uint8,),
+            bf16=(torch.bfloat16, torch.int16, torch.uint16), f32=(torch.float32,),
+            pool=(torch.uint8, torch.int16, torch.bfloat16, torch.uint16),
+        )
+    return _DTYPES
 
 
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
 def kv_verify_tags(pool_tags, block_table, expected_tags, seq_lens, abort_out,
-                   page_size=PAGE_SIZE, stream=None):
-    """abort_out[b] = 1 iff request b's recorded (page, tag) pairs disagree with the pool."""
+                   page_size=PAGE_SIZE, stream=None, prepare=False):
+    """abort_out[b] = 1 iff request b's recorded (page, tag) pairs disagree with the pool.
+    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
     d = _dt()
     batch = seq_lens.numel()
     if block_table.dim() != 2 or expected_tags.shape != block_table.shape:
         raise ValueError("block_table / expected_tags must be [batch][bt_stride] alike")
     if block_table.shape[0] != batch or abort_out.numel() != batch:
         raise ValueError("batch mismatch")
-    st = load().kv_verify_tags(_ptr(pool_tags, "pool_tags", d["u32"]), pool_tags.numel(),
-                               _ptr(block_table, "block_table", d["i32"]),
-                               _ptr(expected_tags, "expected_tags", d["u32"]),
-                               block_table.shape[1], _ptr(seq_lens, "seq_lens", d["i32"]),
-                               batch, page_size, _ptr(abort_out, "abort_out", d["u8"]),
-                               _stream(stream))
-    _check("kv_verify_tags", st)
+    args = (_ptr(pool_tags, "pool_tags", d["u32"]), pool_tags.numel(),
+            _ptr(block_table, "block_table", d["i32"]),
+            _ptr(expected_tags, "expected_tags", d["u32"]),
+            block_table.shape[1], _ptr(seq_lens, "seq_lens", d["i32"]),
+            batch, page_size, _ptr(abort_out, "abort_out", d["u8"]), _stream(stream))
+    return _call("kv_verify_tags", args, prepare,
+                 (pool_tags, block_table, expected_tags, seq_lens, abort_out))
 
 
 def _append(fp8, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool, v_pool,
-            abort=None, batch=None, page_size=PAGE_SIZE, stream=None):
+            abort=None, batch=None, page_size=PAGE_SIZE, stream=None, prepare=False):
     d = _dt()
     n_tok = tok_seq.numel()
     if tok_pos.numel() != n_tok:
@@ -236,39 +283,40 @@ def _append(fp8, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, 
     if block_table.shape[0] != batch or (abort is not None and abort.numel() != batch):
         raise ValueError(f"block_table rows and abort must match batch {batch}")
     _check_scales(k_scale, v_scale, hkv, fp8)
-    lib = load()
+    keep = (k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool, v_pool, abort)
     if fp8:
-        st = lib.kv_append_quant(
+        args = (
             _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
             _ptr(tok_seq, "tok_seq", d["i32"]), _ptr(tok_pos, "tok_pos", d["i32"]), n_tok,
             _ptr(block_table, "block_table", d["i32"]), block_table.shape[1], batch,
             _ptr(k_scale, "k_scale", d["f32"]), _ptr(v_scale, "v_scale", d["f32"]),
             _ptr(k_pool, "k_pool", d["u8"]), _ptr(v_pool, "v_pool", d["u8"]), num_pages, hkv,
             hd, page_size, _ptr(abort, "abort", d["u8"], allow_none=True), _stream(stream))
-        _check("kv_append_quant", st)
-    else:
-        st = lib.kv_append_bf16(
-            _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
-            _ptr(tok_seq, "tok_seq", d["i32"]), _ptr(tok_pos, "tok_pos", d["i32"]), n_tok,
-            _ptr(block_table, "block_table", d["i32"]), block_table.shape[1], batch,
-            _ptr(k_pool, "k_pool", d["pool"]), _ptr(v_pool, "v_pool", d["pool"]), num_pages,
-            hkv, hd, page_size, _ptr(abort, "abort", d["u8"], allow_none=True),
-            _stream(stream))
-        _check("kv_append_bf16", st)
+        return _call("kv_append_quant", args, prepare, keep)
+    args = (
+        _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
+        _ptr(tok_seq, "tok_seq", d["i32"]), _ptr(tok_pos, "tok_pos", d["i32"]), n_tok,
+        _ptr(block_table, "block_table", d["i32"]), block_table.shape[1], batch,
+        _ptr(k_pool, "k_pool", d["pool"]), _ptr(v_pool, "v_pool", d["pool"]), num_pages,
+        hkv, hd, page_size, _ptr(abort, "abort", d["u8"], allow_none=True), _stream(stream))
+    return _call("kv_append_bf16", args, prepare, keep)
 
 
 def kv_append_quant(k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool,
-                    v_pool, abort=None, batch=None, page_size=PAGE_SIZE, stream=None):
-    """Quantize new K/V rows to E4M3 with per-KV-head scales and write them into pool pages."""
-    _append(True, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool,
-            v_pool, abort, batch, page_size, stream)
+                    v_pool, abort=None, batch=None, page_size=PAGE_SIZE, stream=None,
+                    prepare=False):
+    """Quantize new K/V rows to E4M3 with per-KV-head scales and write them into pool pages.
+    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
+    return _append(True, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool,
+                   v_pool, abort, batch, page_size, stream, prepare)
 
 
 def kv_append_bf16(k_new, v_new, tok_seq, tok_pos, block_table, k_pool, v_pool, abort=None,
-                   batch=None, page_size=PAGE_SIZE, stream=None):
-    """Write new bf16 K/V rows unchanged into BF16 pool pages."""
-    _append(False, k_new, v_new, tok_seq, tok_pos, block_table, None, None, k_pool, v_pool,
-            abort, batch, page_size, stream)
+                   batch=None, page_size=PAGE_SIZE, stream=None, prepare=False):
+    """Write new bf16 K/V rows unchanged into BF16 pool pages.
+    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
+    return _append(False, k_new, v_new, tok_seq, tok_pos, block_table, None, None, k_pool,
+                   v_pool, abort, batch, page_size, stream, prepare)
 
 
 def paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len, partition_tokens=0):
@@ -288,8 +336,10 @@ def paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_
 
 def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, max_seq_len,
                       out, sm_scale, workspace=None, abort=None, partition_tokens=0,
-                      cache_dtype=KV_CACHE_FP8_E4M3, page_size=PAGE_SIZE, stream=None):
-    """out[b][h] = softmax attention of q[b][h] over request b's cached tokens."""
+                      cache_dtype=KV_CACHE_FP8_E4M3, page_size=PAGE_SIZE, stream=None,
+                      prepare=False):
+    """out[b][h] = softmax attention of q[b][h] over request b's cached tokens.
+    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
     d = _dt()
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
@@ -303,7 +353,7 @@ def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens
     if workspace is not None:
         ws_ptr = _ptr(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = load().paged_decode_attn(
+    args = (
         _ptr(q, "q", d["bf16"]), int(cache_dtype),
         _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
         _ptr(v_pool, "v_pool", d["u8"] if fp8 else d["pool"]),
@@ -314,14 +364,17 @@ def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens
         _ptr(abort, "abort", d["u8"], allow_none=True), _ptr(out, "out", d["f32"]),
         float(sm_scale), batch, hq, hkv, hd, page_size, k_pool.shape[0], int(partition_tokens),
         ws_ptr, ws_bytes, _stream(stream))
-    _check("paged_decode_attn", st)
+    return _call("paged_decode_attn", args, prepare,
+                 (q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, abort, out,
+                  workspace))
 
 
 def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table,
                              seq_lens, max_seq_len, out, sm_scale, workspace=None, abort=None,
                              partition_tokens=0, cache_dtype=KV_CACHE_FP8_E4M3,
-                             page_size=PAGE_SIZE, stream=None):
-    """Append each request's new token (position seq_lens[b] - 1) and attend, in one launch."""
+                             page_size=PAGE_SIZE, stream=None, prepare=False):
+    """Append each request's new token (position seq_lens[b] - 1) and attend, in one launch.
+    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
     d = _dt()
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
@@ -337,7 +390,7 @@ def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, 
     if workspace is not None:
         ws_ptr = _ptr(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = load().paged_decode_attn_append(
+    args = (
         _ptr(q, "q", d["bf16"]), _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
         int(cache_dtype), _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
         _ptr(v_pool, "v_pool", d["u8"] if fp8 else d["pool"]),
@@ -348,7 +401,9 @@ def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, 
         _ptr(abort, "abort", d["u8"], allow_none=True), _ptr(out, "out", d["f32"]),
         float(sm_scale), batch, hq, hkv, hd, page_size, k_pool.shape[0], int(partition_tokens),
         ws_ptr, ws_bytes, _stream(stream))
-    _check("paged_decode_attn_append", st)
+    return _call("paged_decode_attn_append", args, prepare,
+                 (q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                  abort, out, workspace))
 
 
 def decode_step(layers, block_table, seq_lens, tok_pos, tok_seq, max_seq_len, sm_scale,

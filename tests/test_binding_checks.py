@@ -92,3 +92,26 @@ def test_ingest_and_gemv_sizes_are_checked():
     packed = torch.zeros(kv.wq_packed_bytes(64, 256, kv.WQ_INT4), dtype=torch.uint8)
     with pytest.raises(ValueError, match="scales"):
         kv.wq_gemv(x, packed, torch.zeros(64), y, 64, kv.WQ_INT4)
+
+
+def test_prepare_checks_sizes_like_a_direct_call():
+    """prepare=True runs the same checks before it builds anything."""
+    a = _attn_args(seq_lens=torch.ones(B - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="seq_lens"):
+        kv.paged_decode_attn(a["q"], a["k_pool"], a["v_pool"], a["k_scale"], a["v_scale"],
+                             a["block_table"], a["seq_lens"], a["max_seq_len"], a["out"],
+                             a["sm_scale"], prepare=True)
+
+
+def test_prepared_call_raises_what_the_library_refuses():
+    """A Prepared whose fixed arguments the C ABI refuses raises KvError with
+    that status on every call (a negative batch is refused before any HIP
+    call, so this runs without a GPU)."""
+    lib = kv.load()
+    args = (None, None, None, 0, None, None, None, None, None, 3, None, 48, None, None, 0.088,
+            -1, HQ, HKV, D, P, 10, 0, None, 0, None)
+    call = kv.Prepared("paged_decode_attn_append", lib.paged_decode_attn_append, args, ())
+    for _ in range(2):
+        with pytest.raises(kv.KvError) as e:
+            call()
+        assert e.value.status == -2            # KV_ERR_SHAPE
