@@ -359,20 +359,11 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
     const int ng = min(groups, g0 + groups_per_wg) - g0;  // 1 .. small_max_groups(m_rows)
     const int row_h = ng * kWGroup + 8;                    // halves per LDS row (16-byte pad)
 
-    // activations of rows 0 .. m_rows - 1, inputs 128 g0 .. 128 (g0 + ng): 16-byte pieces
-    const int per_row = ng * 16;
-    for (int p = threadIdx.x; p < m_rows * per_row; p += kGemvWaves * 64) {
-        const int row = p / per_row, c8 = p % per_row;
-        *reinterpret_cast<u32x4*>(xs_dyn + row * row_h + 8 * c8) = *reinterpret_cast<const u32x4*>(
-            x + static_cast<size_t>(row) * k + static_cast<size_t>(kWGroup) * g0 + 8 * c8);
-    }
-    __syncthreads();
-    if (nt >= n_tiles) return;                             // no barrier below
-
     const int col = lane % 16;                             // A: token; B and result: weight row
     const int jg = lane / 16;                              // A, B: input sub-slice; result: token group
-    const uint16_t* xb_base = xs_dyn + (col < m_rows ? col : 0) * row_h + 8 * jg;
-    const size_t blk0 = static_cast<size_t>(nt) * groups + g0;
+    const bool has_tile = nt < n_tiles;                    // uniform per wavefront
+    // a wavefront past the last row tile keeps its pointers at tile 0 and loads nothing
+    const size_t blk0 = static_cast<size_t>(has_tile ? nt : 0) * groups + g0;
     const uint8_t* cbase = packed + blk0 * BLK + 16 * lane;
     const float* sbase = scales + blk0 * 16 + col;
 
@@ -382,6 +373,31 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
         if constexpr (!INT4) t.w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp + 1024));
         t.s = sbase[static_cast<size_t>(i) * 16];
     };
+    GroupTile<INT4> t0, t1, t2;
+    const auto issue_first = [&]() __attribute__((always_inline)) {
+        issue(t0, 0);
+        if (ng > 1) issue(t1, 1);
+        if (ng > 2) issue(t2, 2);
+    };
+    // The first three groups' codes do not depend on the activations. FP8 codes
+    // are requested before the staging below, so their latency overlaps it
+    // (2-4% faster at 1-4 tokens); INT4 codes measured ~3% slower that way at
+    // one token, so they are requested after the barrier.
+    constexpr bool kIssueBeforeStaging = !INT4;
+    if (kIssueBeforeStaging && has_tile) issue_first();
+
+    // activations of rows 0 .. m_rows - 1, inputs 128 g0 .. 128 (g0 + ng): 16-byte pieces
+    const int per_row = ng * 16;
+    for (int p = threadIdx.x; p < m_rows * per_row; p += kGemvWaves * 64) {
+        const int row = p / per_row, c8 = p % per_row;
+        *reinterpret_cast<u32x4*>(xs_dyn + row * row_h + 8 * c8) = *reinterpret_cast<const u32x4*>(
+            x + static_cast<size_t>(row) * k + static_cast<size_t>(kWGroup) * g0 + 8 * c8);
+    }
+    __syncthreads();
+    if (!has_tile) return;                                 // no barrier below
+    if (!kIssueBeforeStaging) issue_first();
+
+    const uint16_t* xb_base = xs_dyn + (col < m_rows ? col : 0) * row_h + 8 * jg;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const auto proc = [&](const GroupTile<INT4>& t, int i) __attribute__((always_inline)) {
         bf16x8 A[4];
@@ -403,12 +419,9 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
         }
         acc += t.s * part;                 // column col is weight row 16 nt + col
     };
-    // 3-deep pipeline: the steady-state loop issues unconditionally (i + 5 < ng);
-    // the last 1 .. 5 groups are handled with uniform conditions.
-    GroupTile<INT4> t0, t1, t2;
-    issue(t0, 0);
-    if (ng > 1) issue(t1, 1);
-    if (ng > 2) issue(t2, 2);
+    // 3-deep pipeline (groups 0 .. 2 already requested): the steady-state loop
+    // issues unconditionally (i + 5 < ng); the last 1 .. 5 groups are handled
+    // with uniform conditions.
     int i = 0;
     for (; i + 5 < ng; i += 3) {
         proc(t0, i);
