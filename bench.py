@@ -59,7 +59,7 @@ INGEST_COUNTER_TRAFFIC = {
 }
 GEMV_COUNTER_TRAFFIC = {
     "sources": ("gemv.hip", "kv_device.h"),
-    "source_sha": "c72e58afe66ac898",
+    "source_sha": "fec999b66cdac863",
     "read_bytes": 1.24997e8,
     "write_bytes": 5.734e5,
 }
