@@ -53,7 +53,7 @@ COUNTER_TRAFFIC = {
 # roofline kernel (28672x8192, one token; profiles/wq_gemv_int4_1token.md).
 INGEST_COUNTER_TRAFFIC = {
     "sources": ("ingest.hip", "kv_device.h"),
-    "source_sha": "1ad0cc34a39d10cc",
+    "source_sha": "adf93a35b9782056",
     "read_bytes": 2.2816e9,
     "write_bytes": 1.1406e9,
 }

@@ -191,6 +191,12 @@ __device__ __forceinline__ bool wave_recip_range(const u32x4 (&w)[4]) {
     return __builtin_amdgcn_ballot_w64(!bf16x2_recip_range(m)) == 0;
 }
 
+// 16 bytes of a pool tile. The pages are written once and not read again by
+// this launch, so the store is non-temporal (streamed past the caches).
+__device__ __forceinline__ void store_stream(uint8_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // Page j of request b (one workgroup; each wavefront takes KV heads wave,
 // wave + 4, ... and uses only its own LDS block).
 template <bool FP8>
@@ -276,7 +282,7 @@ __device__ __forceinline__ void ingest_page(
                                               __uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u),
                                               ks, kinv);
                     }
-                    *reinterpret_cast<u32x4*>(kt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
+                    store_stream(kt + 1024 * h, u32x4{c[0], c[1], c[2], c[3]});
                 }
             };
             // one uniform branch per head: the scale is the wave's, the range is voted on
@@ -285,8 +291,7 @@ __device__ __forceinline__ void ingest_page(
         } else {
 #pragma unroll
             for (int h = 0; h < NCH; ++h)
-                *reinterpret_cast<u32x4*>(kt + 1024 * h) =
-                    *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 8 * h]);
+                store_stream(kt + 1024 * h, *reinterpret_cast<const u32x4*>(&sx[m][32 * jg + 8 * h]));
         }
         wave_lds_sync();                                 // K reads done before V overwrites
         // ---- V: lane holds dim m of each 16-dim chunk, tokens 4 jg .. 4 jg + 3
@@ -307,7 +312,7 @@ __device__ __forceinline__ void ingest_page(
                         for (int r = 0; r < 4; ++r) x[r] = bf16_bits_to_float(sx[4 * jg + r][d]);
                         c[e] = quant4_e4m3<R>(x[0], x[1], x[2], x[3], vs, vinv);
                     }
-                    *reinterpret_cast<u32x4*>(vt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
+                    store_stream(vt + 1024 * h, u32x4{c[0], c[1], c[2], c[3]});
                 }
             };
             if (recip_quotient_ok(vs) && wave_recip_range(vw)) encode_v(std::true_type{});
@@ -325,7 +330,7 @@ __device__ __forceinline__ void ingest_page(
                     c[2 * e] = hv[0] | (hv[1] << 16);
                     c[2 * e + 1] = hv[2] | (hv[3] << 16);
                 }
-                *reinterpret_cast<u32x4*>(vt + 1024 * h) = u32x4{c[0], c[1], c[2], c[3]};
+                store_stream(vt + 1024 * h, u32x4{c[0], c[1], c[2], c[3]});
             }
         }
         wave_lds_sync();                                 // V reads done before the next head
