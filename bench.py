@@ -461,7 +461,7 @@ def sweep_bench(args):
                     for _ in range(wl.num_layers)]
             n = kv.paged_decode_attn_workspace_bytes(B, wl.num_q_heads, wl.num_kv_heads,
                                                      wl.max_seq_len, 0)
-            ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=dev)
             cd = kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16
             sm = 1.0 / math.sqrt(wl.head_dim)
 

@@ -166,6 +166,13 @@ class Prepared:
     references to the tensors it was prepared with, so their memory stays
     valid; their contents (lengths, flags, new tokens) may change between
     calls. A call that the library refuses raises ``KvError``.
+
+    Sizes are fixed with the arguments, ``max_seq_len`` of the attention
+    calls included: every later value in ``seq_lens`` must stay at or below
+    the ``max_seq_len`` given when the call was prepared. A request whose
+    length exceeds it is refused by the kernels like any too-long request
+    (all-zero output, and in the fused call its new token is not stored), not
+    reported as an error. Prepare with the largest length the loop will reach.
     """
 
     __slots__ = ("name", "_fn", "_args", "_keep")
@@ -339,7 +346,9 @@ def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens
                       cache_dtype=KV_CACHE_FP8_E4M3, page_size=PAGE_SIZE, stream=None,
                       prepare=False):
     """out[b][h] = softmax attention of q[b][h] over request b's cached tokens.
-    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
+    A request longer than max_seq_len outputs zeros. With prepare=True nothing
+    is enqueued; the checked call is returned as a ``Prepared``, whose later
+    seq_lens must stay <= this max_seq_len."""
     d = _dt()
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
@@ -374,7 +383,9 @@ def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, 
                              partition_tokens=0, cache_dtype=KV_CACHE_FP8_E4M3,
                              page_size=PAGE_SIZE, stream=None, prepare=False):
     """Append each request's new token (position seq_lens[b] - 1) and attend, in one launch.
-    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
+    A request longer than max_seq_len is neither written nor read (zeros). With
+    prepare=True nothing is enqueued; the checked call is returned as a
+    ``Prepared``, whose later seq_lens must stay <= this max_seq_len."""
     d = _dt()
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
@@ -496,18 +507,27 @@ def ingest_layer(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, v_poo
                  cache_dtype=KV_CACHE_FP8_E4M3, stream=None):
     """Prefill handoff of one layer: for FP8, calibrate k_scale / v_scale
     (fp32 [num_kv_heads], written) from the rows' amax, then write the prompts.
-    ``amax`` is an optional fp32 [2][num_kv_heads] scratch tensor (zeroed here)."""
+    ``amax`` is an optional fp32 [2][num_kv_heads] scratch tensor (zeroed here).
+    Everything, the scratch's allocation and zeroing included, is enqueued on
+    ``stream`` (a torch stream, a raw HIP stream handle, or None for torch's
+    current stream), so the zeroing is ordered before the accumulation."""
     if cache_dtype == KV_CACHE_FP8_E4M3:
         import torch
         hkv = k_rows.shape[1]
-        if amax is None:
-            amax = torch.zeros((2, hkv), dtype=torch.float32, device=k_rows.device)
+        if stream is None or isinstance(stream, torch.cuda.Stream):
+            ts = stream if stream is not None else torch.cuda.current_stream(k_rows.device)
         else:
-            amax.zero_()
-        kv_amax_accumulate(k_rows, amax[0], stream=stream)
-        kv_amax_accumulate(v_rows, amax[1], stream=stream)
-        kv_scales_from_amax(amax[0], k_scale, stream=stream)
-        kv_scales_from_amax(amax[1], v_scale, stream=stream)
+            ts = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)),
+                                           device=k_rows.device)
+        with torch.cuda.stream(ts):
+            if amax is None:
+                amax = torch.zeros((2, hkv), dtype=torch.float32, device=k_rows.device)
+            else:
+                amax.zero_()
+            kv_amax_accumulate(k_rows, amax[0], stream=ts)
+            kv_amax_accumulate(v_rows, amax[1], stream=ts)
+            kv_scales_from_amax(amax[0], k_scale, stream=ts)
+            kv_scales_from_amax(amax[1], v_scale, stream=ts)
     kv_ingest_prefill(k_rows, v_rows, row_start, seq_lens, block_table, k_pool, v_pool,
                       max_seq_len, k_scale, v_scale, abort=abort, cache_dtype=cache_dtype,
                       stream=stream)

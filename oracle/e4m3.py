@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE (see the package docstring): never used by the product path.
 
-Which format: the pages say only that the cache is stored "in FP8 e4m3 instead
-of BF16" (remio.ai/it, "Il serving di modelli più piccoli di Cloudflare riduce
+Which format: the pages name only FP8 e4m3 as the cache's storage format, in
+place of BF16 (remio.ai/it, "Il serving di modelli più piccoli di Cloudflare riduce
 la memoria, ma la sicurezza diventa la prova decisiva", section "Cosa ha
 cambiato Cloudflare per Kimi e GLM"; the same on the iitog.ru and manulx.blog
 pages). The variant whose largest finite value is 448 is the OCP 8-bit

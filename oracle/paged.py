@@ -43,8 +43,6 @@ h // (Hq / Hkv).
 
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 from . import e4m3
@@ -160,8 +158,7 @@ def dequant_request(pool, block_table_row, L, page_size, scale, cache):
     """float64 [Hkv][L][D] values of one request as attention reads them."""
     raw = gather_request(pool, block_table_row, L, page_size)
     if cache == "fp8":
-        s = np.asarray(scale, dtype=np.float32).astype(np.float64)
-        return e4m3.decode(raw) * s[:, None, None]
+        return e4m3.dequantize(raw, np.asarray(scale, dtype=np.float32)[:, None, None])
     if cache == "bf16":
         return e4m3.bf16_bits_to_f64(raw)
     raise ValueError(cache)
@@ -224,11 +221,6 @@ def decode_attn(q_bits, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
                             block_table, seq_lens, sm_scale, cache, abort)
         for b in range(batch)
     ])
-
-
-def default_sm_scale(head_dim: int) -> float:
-    """1 / sqrt(head_dim), the usual attention temperature."""
-    return 1.0 / math.sqrt(head_dim)
 
 
 def decode_step(state, layers_q_bits, layers_k_new, layers_v_new, sm_scale,

@@ -29,7 +29,7 @@ def sm_scale_for(wl) -> float:
 def workspace(wl, partition_tokens: int, max_seq_len=None):
     n = kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads,
                                              max_seq_len or wl.max_seq_len, partition_tokens)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=DEV) if n else None
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV) if n else None
 
 
 def gpu_step(st: DeviceState, step: int, verify: bool = True, partition_tokens: int = 0,
@@ -107,25 +107,23 @@ class OracleRun:
                 wl, layer, st.k_scale_host[layer], st.v_scale_host[layer], st.cache)
 
     def step(self, step: int, inputs, verify=True, sm_scale=None):
+        """The oracle's decode step (paged.decode_step) over the layers in
+        ``inputs`` ({layer: (q, k_new, v_new)} bf16 bits), updating the host
+        pools in place. Returns (abort or None without the check, {layer: out})."""
         st, wl = self.st, self.st.wl
-        seq_lens = wl.seq_lens_at(step)
-        abort = (paged.verify_tags(wl.pool_tags, wl.block_table, wl.expected_tags, seq_lens,
-                                   wl.page_size) if verify else None)
+        layers = list(inputs)
+        state = dict(pool_tags=wl.pool_tags, block_table=wl.block_table,
+                     expected_tags=wl.expected_tags, seq_lens=wl.seq_lens_at(step),
+                     page_size=wl.page_size,
+                     k_pool=[self.kp[ly] for ly in layers], v_pool=[self.vp[ly] for ly in layers],
+                     k_scale=[st.k_scale_host[ly] for ly in layers],
+                     v_scale=[st.v_scale_host[ly] for ly in layers])
         sm = sm_scale_for(wl) if sm_scale is None else sm_scale
-        outs = {}
-        for layer, (q, kn, vn) in inputs.items():
-            pos = seq_lens - 1
-            if st.cache == "fp8":
-                paged.append_fp8(self.kp[layer], self.vp[layer], kn, vn, np.arange(wl.batch),
-                                 pos, wl.block_table, st.k_scale_host[layer],
-                                 st.v_scale_host[layer], abort)
-            else:
-                paged.append_bf16(self.kp[layer], self.vp[layer], kn, vn, np.arange(wl.batch),
-                                  pos, wl.block_table, abort)
-            outs[layer] = paged.decode_attn(q, self.kp[layer], self.vp[layer],
-                                            st.k_scale_host[layer], st.v_scale_host[layer],
-                                            wl.block_table, seq_lens, sm, st.cache, abort)
-        return abort, outs
+        abort, outs = paged.decode_step(state, [inputs[ly][0] for ly in layers],
+                                        [inputs[ly][1] for ly in layers],
+                                        [inputs[ly][2] for ly in layers], sm, cache=st.cache,
+                                        verify=verify)
+        return (abort if verify else None), dict(zip(layers, outs))
 
 
 def oracle_request(st: DeviceState, layer: int, b: int, step: int, q_bits, sm_scale=None):
@@ -141,8 +139,8 @@ def oracle_request(st: DeviceState, layer: int, b: int, step: int, q_bits, sm_sc
                                    st.v_scale_host[layer], st.cache)
     sm = sm_scale_for(wl) if sm_scale is None else sm_scale
     if st.cache == "fp8":
-        Kd = paged.e4m3.decode(kc) * st.k_scale_host[layer].astype(np.float64)[:, None, None]
-        Vd = paged.e4m3.decode(vc) * st.v_scale_host[layer].astype(np.float64)[:, None, None]
+        Kd = paged.e4m3.dequantize(kc, st.k_scale_host[layer][:, None, None])
+        Vd = paged.e4m3.dequantize(vc, st.v_scale_host[layer][:, None, None])
     else:
         Kd = paged.e4m3.bf16_bits_to_f64(kc)
         Vd = paged.e4m3.bf16_bits_to_f64(vc)

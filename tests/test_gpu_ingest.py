@@ -241,7 +241,7 @@ def test_ingest_layer_then_decode_attention(kv, cache):
     out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=DEV)
     n = kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads,
                                              wl.max_seq_len, 0)
-    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
     kv.paged_decode_attn(q, st.k_pool[0], st.v_pool[0], ks if cache == "fp8" else None,
                          vs if cache == "fp8" else None, st.block_table, lens0, wl.max_seq_len,
                          out, 1.0 / np.sqrt(wl.head_dim), workspace=ws,

@@ -327,7 +327,7 @@ def _edge_run(kv, e, cache, lens=None, abort=None, max_seq_len=None, partition_t
     msl = int(lens.max()) if max_seq_len is None else max_seq_len
     out = torch.full((batch, hq, 128), float("nan"), device=DEV)
     n = kv.paged_decode_attn_workspace_bytes(batch, hq, e["kp"].shape[1], msl, partition_tokens)
-    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
     btt = e["btt"] if bt is None else torch.from_numpy(bt).to(DEV)
     kv.paged_decode_attn(torch.from_numpy(e["q"].view(np.int16)).to(DEV), e["kp"], e["vp"],
                          e["kst"] if cache == "fp8" else None,
@@ -354,7 +354,8 @@ def _edge_oracle(e, cache, lens, abort=None, bt=None):
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
-@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2), (4, 4), (32, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2), (4, 4), (32, 2), (4, 2), (6, 2), (12, 3),
+                                     (24, 4), (24, 2), (10, 2), (14, 1)])
 def test_edge_lengths_groups_and_garbage_slots(kv, cache, hq, hkv):
     lens = [1, 2, 15, 16, 17, 31, 33, 100, 0, 47]
     e = _edge_state(kv, cache, hq, hkv, lens)
@@ -393,7 +394,7 @@ def _uses_persistent_kernel(batch, hkv, max_len, pt):
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
-@pytest.mark.parametrize("hq", [64, 128])
+@pytest.mark.parametrize("hq", [16, 24, 32, 48, 64, 96, 128])
 def test_wave_mode_edges_aborts_and_bad_ids(kv, cache, hq):
     """A batch large enough for the persistent kernel, with ragged
     lengths (1 token, page and partition boundaries, empty requests) and
@@ -536,7 +537,7 @@ def test_wave_mode_even_page_split_long_partitions(kv, cache):
     msl = max(lens)
     for pt in (1024, 2048):
         n = kv.paged_decode_attn_workspace_bytes(batch, hq, hkv, msl, pt)
-        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
         kp_a, vp_a = e["kp"].clone(), e["vp"].clone()
         kp_b, vp_b = e["kp"].clone(), e["vp"].clone()
         li = torch.from_numpy(live).to(DEV)
