@@ -108,6 +108,9 @@ def parse():
                          "sweep: BF16 vs FP8 decode at 1..64 requests under one pool budget; "
                          "gemv: INT4 vs FP8 weight-only decode GEMV at 1..64 tokens")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--sweep-batches", default=",".join(str(b) for b in SWEEP_BATCHES),
+                    help="sweep mode: the request counts to run")
+    ap.add_argument("--sweep-caches", default="bf16,fp8", help="sweep mode: the caches to run")
     ap.add_argument("--gemv-tokens", default="1,8,16,32,64",
                     help="--mode gemv: comma-separated token counts (the roofline needs 1)")
     return ap.parse_args()
@@ -442,8 +445,8 @@ def sweep_bench(args):
     ref = synth.concurrency_point(32, max_steps=total_steps)
     budget = int(1.01 * pool_bytes(ref, "bf16"))
     points = []
-    for cache in ("bf16", "fp8"):
-        for B in SWEEP_BATCHES:
+    for cache in args.sweep_caches.split(","):
+        for B in [int(x) for x in args.sweep_batches.split(",")]:
             wl = synth.concurrency_point(B, max_steps=total_steps)
             need = pool_bytes(wl, cache)
             pt = {"cache": cache, "batch": B, "pool_GB": round(need / 1e9, 3)}
@@ -684,7 +687,7 @@ def main():
     pt_eff = kv.paged_decode_attn_partition_tokens(wl.batch, wl.num_kv_heads, max_len, pt)
     ws_n = kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads,
                                                 max_len, pt)
-    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_n, 256), dtype=torch.uint8, device=dev)
     cd = kv.KV_CACHE_FP8_E4M3 if fp8 else kv.KV_CACHE_BF16
     sm = 1.0 / math.sqrt(wl.head_dim)
     stream = torch.cuda.current_stream()

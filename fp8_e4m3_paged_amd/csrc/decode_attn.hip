@@ -40,6 +40,12 @@ constexpr int kAccStride = kDim + 4;           // padded LDS row (floats)
 constexpr float kLog2e = 1.4426950408889634f;
 // Partitions up to this many tokens may run in the persistent kernel.
 constexpr int kWaveModeMaxTokens = 2048;
+// FP8 register pipeline depth of the shared kernel (page pairs in flight + 1);
+// the persistent kernel keeps 3 (its fused form has no registers for a 4th).
+#ifndef KVFP8_SHARED_DEPTH
+#define KVFP8_SHARED_DEPTH 3
+#endif
+constexpr int kSharedDepth = KVFP8_SHARED_DEPTH;
 
 // Raw registers of one page pair: K and V tiles of pages a and b.
 template <bool FP8>
@@ -368,19 +374,49 @@ __device__ __forceinline__ void apply_new_token(u32x4 (&K)[PairTiles<FP8>::N],
 }
 
 // Software pipeline over a wavefront's n page pairs: register buffers rotate
-// so that while one pair is processed the next ones are in flight (two for
-// FP8, one for BF16, whose tiles take twice the registers). Every load in the
-// steady-state loop is unconditional (the index is clamped to the last pair),
-// so each wait is a static partial vmcnt; the FP8 epilogue issues only the
-// loads that are still needed.
+// so that while one pair is processed the next ones are in flight (DEPTH - 1
+// of them for FP8: two or three; one for BF16, whose tiles take twice the
+// registers). Every load in the steady-state loop is unconditional (the index
+// is clamped to the last pair), so each wait is a static partial vmcnt; the
+// FP8 epilogue issues only the loads that are still needed.
 // `proc_end` processes the pairs of the FP8 epilogue, which always include
 // the wave's last pair (the only one the fused append ever patches), so the
 // steady-state loop carries no patch logic.
-template <bool FP8, typename Issue, typename Proc, typename ProcEnd, typename Hook>
+template <bool FP8, int DEPTH, typename Issue, typename Proc, typename ProcEnd, typename Hook>
 __device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc, ProcEnd&& proc_end,
                                                Hook&& after_issue) {
     if (n <= 0) return;
-    if constexpr (FP8) {
+    if constexpr (FP8 && DEPTH == 4) {
+        PairTiles<FP8> t0, t1, t2, t3;
+        issue(t0, 0);
+        issue(t1, 1);
+        issue(t2, 2);
+        issue(t3, 3);
+        after_issue();     // runs while the first tiles are in flight
+        int i = 0;
+        for (; i + 7 < n; i += 4) {
+            proc(t0, i);
+            issue(t0, i + 4);
+            proc(t1, i + 1);
+            issue(t1, i + 5);
+            proc(t2, i + 2);
+            issue(t2, i + 6);
+            proc(t3, i + 3);
+            issue(t3, i + 7);
+        }
+        // 1..7 pairs left: t0..t3 hold pairs i .. i+3 (when they exist)
+        proc_end(t0, i);
+        if (i + 4 < n) issue(t0, i + 4);
+        if (i + 1 < n) proc_end(t1, i + 1);
+        if (i + 5 < n) issue(t1, i + 5);
+        if (i + 2 < n) proc_end(t2, i + 2);
+        if (i + 6 < n) issue(t2, i + 6);
+        if (i + 3 < n) proc_end(t3, i + 3);
+        if (i + 4 < n) proc_end(t0, i + 4);
+        if (i + 5 < n) proc_end(t1, i + 5);
+        if (i + 6 < n) proc_end(t2, i + 6);
+    } else if constexpr (FP8) {
+        static_assert(DEPTH == 3, "FP8 pipelines are 3 or 4 deep");
         PairTiles<FP8> t0, t1, t2;
         issue(t0, 0);
         issue(t1, 1);
@@ -446,7 +482,7 @@ __device__ __forceinline__ void load_q_operand(bf16x8 (&qop)[4], const uint16_t*
 // slot in the pair's registers when it gets there, and stores the codes to
 // the pool after its last load. Nothing in the launch reads those codes back
 // from memory, so no fence or barrier is involved.
-template <bool FP8, bool APPEND, typename TileOf>
+template <bool FP8, bool APPEND, int DEPTH, typename TileOf>
 __device__ __forceinline__ void stream_share(
     TileOf&& tile_of, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int npg,
     int pg0, int first, int stride, int t_begin, int t_end, int L, int lane, int jgrp,
@@ -490,7 +526,7 @@ __device__ __forceinline__ void stream_share(
         process_pair<FP8>(t, (pg0 + 2 * pr) * kPage, t_end, jgrp, s_scale, qop, m_run, l_run,
                           acc_o);
     };
-    pipeline_pairs<FP8>(n_w, issue, proc, proc_end, prepare);
+    pipeline_pairs<FP8, DEPTH>(n_w, issue, proc, proc_end, prepare);
     if constexpr (APPEND) {
         if (owns_new) {
             const size_t tile = tile_of(t_new / kPage - pg0);
@@ -559,11 +595,149 @@ __device__ __forceinline__ void merge_waves(float* sm, int wave, int lane, int g
     }
 }
 
+// Combine the partitions of each (request, query head):
+//   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p acc_p / sum_p w_p l_p
+// Requests that are aborted, empty, too long, or that a partition marked as
+// mapped to an invalid page (l_p < 0) get zeros. A wavefront reduces a row in
+// two passes: the first over the (max, sum) pairs finds M and any invalid
+// mark; the second takes 64 slots at a time (the next 64 pairs loading
+// meanwhile), and a ballot of the nonzero weights lists the slots to read,
+// whose outputs (two dims per lane, 512 B per slot) are loaded up to 8 at a
+// time before any is accumulated. Empty slots (weight 0) are never read.
+// The shared attention kernel runs this itself in the workgroup that
+// completes a (request, KV head); reduce_partials_kernel runs it for the
+// persistent kernel's partials.
+constexpr int kReduceWaves = 4;
+constexpr int kReduceBatch = 8;             // slot outputs in flight per wavefront (16 requests
+                                            // up to 131k tokens: 7.3 us; 4: 8.3, 16: 7.9, 32: 10.9)
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+constexpr f32x2 kEmptySlot = {-INFINITY, 0.f};
+
+// Partials exchanged between the workgroups of one launch are written and
+// read with agent-scope atomic accesses: the stores write through to the
+// point where every XCD's L2 sees them and the loads fetch from there, so
+// no cache-wide writeback or invalidate (what a device-scope fence costs on
+// this chip) is needed around the counter that publishes them.
+__device__ __forceinline__ void store_shared_f32x2(float* p, f32x2 v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared_f32x4(float* p, const f32x4& v) {
+    store_shared_f32x2(p, f32x2{v[0], v[1]});
+    store_shared_f32x2(p + 2, f32x2{v[2], v[3]});
+}
+template <bool SHARED>
+__device__ __forceinline__ f32x2 load_f32x2(const f32x2* p) {
+    if constexpr (SHARED) {
+        return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
+                                                           __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT));
+    } else {
+        return *p;
+    }
+}
+
+// First pass over this wavefront's slots c0 + lane, c0 + lane + cstep, ...
+// (< np) of one row's (max, sum) pairs: the lane's maximum and whether any
+// slot carries the invalid-page mark. Four loads in flight per lane.
+template <bool SHARED>
+__device__ __forceinline__ void row_slot_max(const f32x2* __restrict__ ml, int np, int c0, int cstep,
+                                             int lane, float& mx, bool& bad) {
+    mx = -INFINITY;
+    bad = false;
+    for (int i0 = c0 + lane; i0 < np; i0 += 4 * cstep) {
+        f32x2 e[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            e[k] = i0 + cstep * k < np ? load_f32x2<SHARED>(ml + i0 + cstep * k) : kEmptySlot;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bad |= e[k][1] < 0.f;
+            mx = fmaxf(mx, e[k][0]);
+        }
+    }
+}
+
+// Second pass over the 64-slot chunks c0, c0 + cstep, ... (< np): the lane's
+// share of sum_p w_p l_p and its two dims of sum_p w_p acc_p, with
+// w_p = 2^(m_p - M_use). acc points at the row's outputs plus 2 * lane.
+template <bool SHARED>
+__device__ __forceinline__ void row_slot_accumulate(const f32x2* __restrict__ ml,
+                                                    const float* __restrict__ acc, int np, int c0,
+                                                    int cstep, int lane, float M_use, float& lsum,
+                                                    f32x2& num) {
+    lsum = 0.f;
+    num = f32x2{0.f, 0.f};
+    f32x2 e_next = c0 + lane < np ? load_f32x2<SHARED>(ml + c0 + lane) : kEmptySlot;
+    for (int c = c0; c < np; c += cstep) {
+        const f32x2 e = e_next;                               // the next chunk's pairs load
+        e_next = c + cstep + lane < np ? load_f32x2<SHARED>(ml + c + cstep + lane)
+                                       : kEmptySlot;          // under this one's reads
+        const float w = exp2f(e[0] - M_use);                  // 0 for an empty slot
+        lsum += w * e[1];
+        uint64_t mask = __builtin_amdgcn_ballot_w64(w > 0.f);
+        while (mask != 0) {
+            int sl[kReduceBatch];
+            f32x2 v[kReduceBatch];
+#pragma unroll
+            for (int k = 0; k < kReduceBatch; ++k) {
+                sl[k] = mask != 0 ? __builtin_ctzll(mask) : -1;    // wave-uniform
+                mask &= mask - 1;
+                if (sl[k] >= 0)
+                    v[k] = load_f32x2<SHARED>(reinterpret_cast<const f32x2*>(
+                        acc + static_cast<size_t>(c + sl[k]) * kDim));
+            }
+#pragma unroll
+            for (int k = 0; k < kReduceBatch; ++k) {
+                if (sl[k] >= 0)
+                    num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sl[k])) * v[k];
+            }
+        }
+    }
+}
+
+// One wavefront reduces one whole row (slots [0, np)) and writes its two
+// dims per lane of the output o (already offset by the lane). SHARED: the
+// partials were written by other workgroups of the same launch.
+template <bool SHARED>
+__device__ __forceinline__ void reduce_row_wave(const f32x2* __restrict__ ml,
+                                                const float* __restrict__ acc, int np, float vs,
+                                                f32x2* o, int lane) {
+    float mx;
+    bool bad;
+    row_slot_max<SHARED>(ml, np, 0, 64, lane, mx, bad);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {              // uniform per row
+        *o = f32x2{0.f, 0.f};
+        return;
+    }
+    const float M = wave_max(mx);
+    float lsum;
+    f32x2 num;
+    row_slot_accumulate<SHARED>(ml, acc, np, 0, 64, lane, M == -INFINITY ? 0.f : M, lsum, num);
+    const float lt = wave_sum(lsum);
+    *o = lt > 0.f ? num * (vs / lt) : f32x2{0.f, 0.f};
+}
+
 // Shared-mode partition kernel. Grid: blockIdx.x = (p * batch + b) * hkv + g;
 // the NW wavefronts of the workgroup share partition p of (b, g) (pairs w,
 // w + NW, ...) and merge in LDS. NW = 4, or 8 when the grid has at most one
 // workgroup per CU (e.g. 32 requests x 8 KV heads), so each CU still streams
 // with 8 wavefronts and no split-K reduction is needed.
+// With several partitions each workgroup writes its partial, then counts it
+// on the (b, g)'s counter; the workgroup whose increment completes the count
+// combines the (b, g)'s partials itself, one wavefront per query head, and
+// sets the counter back to zero, so no second launch is needed. The counters
+// start at zero (a zero-filled workspace) and every call leaves them at zero.
 // Occupancy is pinned at 2 waves per SIMD: the register pipeline needs ~200
 // VGPRs, and without the cap the scheduler may trade the in-flight loads for a
 // third wave (sinking the prefetches next to their uses), which halves the
@@ -577,9 +751,10 @@ void attn_partition_kernel(
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const uint8_t* __restrict__ abort,
     float* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_acc,
-    float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv, int32_t num_pages,
-    int32_t part_tokens, int32_t n_parts) {
+    uint32_t* __restrict__ counters, float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv,
+    int32_t num_pages, int32_t part_tokens, int32_t n_parts) {
     extern __shared__ float smem[];
+    __shared__ int sm_last;
     constexpr int kThreads = NW * 64;
     const int group = hq / hkv;
     // LDS: the merge area, then the page ids of the partition
@@ -596,11 +771,11 @@ void attn_partition_kernel(
     const int jgrp = lane / 16;      // k-group of the operands / row group of the result
 
     const int L = seq_lens[b];
-    if (!request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride) ||
-        static_cast<int64_t>(p) * part_tokens >= L) {
-        // Only the single-partition case owns the final output here; with
-        // several partitions the reduction writes zeros for such requests.
-        if (n_parts == 1) {
+    const bool ok = request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride);
+    if (!ok || static_cast<int64_t>(p) * part_tokens >= L) {
+        // A refused request's zeros come from its first partition's
+        // workgroup; partitions past a valid request's end have nothing to do.
+        if (!ok && p == 0) {
             for (int i = tid; i < group * kDim; i += kThreads)
                 out[(static_cast<size_t>(b) * hq + g * group) * kDim + i] = 0.f;
         }
@@ -640,9 +815,9 @@ void attn_partition_kernel(
             return static_cast<size_t>(id) * hkv + g;
         };
         const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
-        stream_share<FP8, APPEND>(tile_of, k_pool, v_pool, npg, pg0, wave, NW, t_begin, t_end, L,
-                                  lane, jgrp, s_scale, qop, k_new + new_row, v_new + new_row,
-                                  k_scale + g, v_scale + g, m_run, l_run, acc_o);
+        stream_share<FP8, APPEND, kSharedDepth>(
+            tile_of, k_pool, v_pool, npg, pg0, wave, NW, t_begin, t_end, L, lane, jgrp, s_scale,
+            qop, k_new + new_row, v_new + new_row, k_scale + g, v_scale + g, m_run, l_run, acc_o);
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -658,13 +833,33 @@ void attn_partition_kernel(
             *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
         } else {
             const size_t pslot = (q_row + qh) * partial_slots(n_parts) + p;
-            *reinterpret_cast<f32x4*>(part_acc + pslot * kDim + d) = o;
-            if (d == 0) {
-                part_ml[2 * pslot] = M;
-                part_ml[2 * pslot + 1] = bad ? -1.f : lt;
-            }
+            store_shared_f32x4(part_acc + pslot * kDim + d, o);
+            if (d == 0) store_shared_f32x2(part_ml + 2 * pslot, f32x2{M, bad ? -1.f : lt});
         }
     });
+    if (n_parts == 1) return;
+
+    // ---- count this partition; the last one of (b, g) combines them ------
+    __builtin_amdgcn_s_waitcnt(0);    // this workgroup's partial stores have completed
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t np_b = static_cast<uint32_t>((L + part_tokens - 1) / part_tokens);
+        sm_last = __hip_atomic_fetch_add(counters + static_cast<size_t>(b) * hkv + g, 1u,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np_b - 1;
+    }
+    __syncthreads();
+    if (!sm_last) return;
+    if (tid == 0)                     // ready for the next call
+        __hip_atomic_store(counters + static_cast<size_t>(b) * hkv + g, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    const int np_b = (L + part_tokens - 1) / part_tokens;
+    const int64_t n_slots = partial_slots(n_parts);
+    for (int qh = wave; qh < group; qh += NW) {
+        const size_t row = q_row + qh;
+        reduce_row_wave<true>(reinterpret_cast<const f32x2*>(part_ml) + row * n_slots,
+                        part_acc + row * n_slots * kDim + 2 * lane, np_b, vs,
+                        reinterpret_cast<f32x2*>(out + row * kDim) + lane, lane);
+    }
 }
 
 // Persistent kernel for short partitions (<= 2048 tokens), used when there
@@ -723,8 +918,8 @@ void attn_wave_kernel(
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const uint8_t* __restrict__ abort,
     float* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_acc,
-    float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv, int32_t num_pages,
-    int32_t part_tokens, int32_t n_parts) {
+    uint32_t* __restrict__ /*counters*/, float sm_scale_log2, int32_t batch, int32_t hq,
+    int32_t hkv, int32_t num_pages, int32_t part_tokens, int32_t n_parts) {
     constexpr int kThreads = kWaves * 64;
     extern __shared__ float smem[];
     const int group = hq / hkv;
@@ -841,7 +1036,7 @@ void attn_wave_kernel(
                 return static_cast<size_t>(id) * hkv + g;
             };
             const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
-            stream_share<FP8, APPEND>(tile_of, k_pool, v_pool, npg, k0, wave, kWaves, t_begin,
+            stream_share<FP8, APPEND, 3>(tile_of, k_pool, v_pool, npg, k0, wave, kWaves, t_begin,
                                       t_end, L, lane, jgrp, s_scale, qop, k_new + new_row,
                                       v_new + new_row, k_scale + g, v_scale + g, m_run, l_run,
                                       acc_o);
@@ -875,31 +1070,6 @@ void attn_wave_kernel(
         });
         __syncthreads();            // the next piece rewrites the ids and the merge area
     }
-}
-
-// Combine the partitions of each (request, query head):
-//   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p acc_p / sum_p w_p l_p
-// Requests that are aborted, empty, too long, or that a partition marked as
-// mapped to an invalid page (l_p < 0) get zeros. One wavefront per (b, h),
-// four per workgroup, no barriers (rows of more than 64 slots: see COOP
-// below): a first pass over the (max, sum) pairs
-// finds M and any invalid mark; the second takes 64 slots at a time (the
-// next 64 pairs loading meanwhile), and a ballot of the nonzero weights lists
-// the slots to read, whose outputs (two dims per lane, 512 B per slot) are
-// loaded up to 8 at a time before any is accumulated. Empty slots (weight 0)
-// are never read.
-constexpr int kReduceWaves = 4;
-constexpr int kReduceBatch = 8;             // slot outputs in flight per wavefront (16 requests
-                                            // up to 131k tokens: 7.3 us; 4: 8.3, 16: 7.9, 32: 10.9)
-
-__device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
 }
 
 // COOP = false: one wavefront per (b, h), four rows per workgroup. COOP = true
@@ -938,82 +1108,48 @@ __global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
     const size_t n_slots = partial_slots(n_parts);
     const f32x2* ml = reinterpret_cast<const f32x2*>(part_ml) + bh * n_slots;
     const float* acc = part_acc + bh * n_slots * kDim + 2 * lane;
-    // this wavefront's 64-slot chunks: c0, c0 + cstep, ...
-    const int c0 = COOP ? 64 * wave : 0;
-    constexpr int cstep = COOP ? 64 * kReduceWaves : 64;
-
-    constexpr f32x2 kEmpty = {-INFINITY, 0.f};
-    float mx = -INFINITY;
-    bool bad = false;
-    for (int i0 = c0 + lane; i0 < np; i0 += 4 * cstep) {      // four loads in flight
-        f32x2 e[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) e[k] = i0 + cstep * k < np ? ml[i0 + cstep * k] : kEmpty;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            bad |= e[k][1] < 0.f;
-            mx = fmaxf(mx, e[k][0]);
-        }
-    }
-    bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-    float M = wave_max(mx);
-    if constexpr (COOP) {
+    const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
+    if constexpr (!COOP) {
+        reduce_row_wave<false>(ml, acc, np, vs, o, lane);
+    } else {
+        // this wavefront's 64-slot chunks: 64 wave, 64 wave + 256, ...
+        constexpr int cstep = 64 * kReduceWaves;
+        float mx;
+        bool bad;
+        row_slot_max<false>(ml, np, 64 * wave, cstep, lane, mx, bad);
+        const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+        float M = wave_max(mx);
         if (lane == 0) {
             sm_max[wave] = M;
-            sm_bad[wave] = any_bad;
+            sm_bad[wave] = wave_bad;
         }
         __syncthreads();
+        bool any_bad = false;
         for (int w = 0; w < kReduceWaves; ++w) {
             M = fmaxf(M, sm_max[w]);
             any_bad |= sm_bad[w] != 0;
         }
-    }
-    if (any_bad) {                                            // uniform per row
-        if (!COOP || wave == 0) *o = f32x2{0.f, 0.f};
-        return;
-    }
-    const float M_use = M == -INFINITY ? 0.f : M;
-    float lsum = 0.f;
-    f32x2 num = {0.f, 0.f};
-    f32x2 e_next = c0 + lane < np ? ml[c0 + lane] : kEmpty;
-    for (int c = c0; c < np; c += cstep) {
-        const f32x2 e = e_next;                               // the next chunk's pairs load
-        e_next = c + cstep + lane < np ? ml[c + cstep + lane] : kEmpty;   // under this one's reads
-        const float w = exp2f(e[0] - M_use);                  // 0 for an empty slot
-        lsum += w * e[1];
-        uint64_t mask = __builtin_amdgcn_ballot_w64(w > 0.f);
-        while (mask != 0) {
-            int sl[kReduceBatch];
-            f32x2 v[kReduceBatch];
-#pragma unroll
-            for (int k = 0; k < kReduceBatch; ++k) {
-                sl[k] = mask != 0 ? __builtin_ctzll(mask) : -1;    // wave-uniform
-                mask &= mask - 1;
-                if (sl[k] >= 0)
-                    v[k] = *reinterpret_cast<const f32x2*>(acc + static_cast<size_t>(c + sl[k]) * kDim);
-            }
-#pragma unroll
-            for (int k = 0; k < kReduceBatch; ++k) {
-                if (sl[k] >= 0)
-                    num += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sl[k])) * v[k];
-            }
+        if (any_bad) {                                        // uniform per row
+            if (wave == 0) *o = f32x2{0.f, 0.f};
+            return;
         }
-    }
-    float lt = wave_sum(lsum);
-    if constexpr (COOP) {
+        float lsum;
+        f32x2 num;
+        row_slot_accumulate<false>(ml, acc, np, 64 * wave, cstep, lane,
+                                   M == -INFINITY ? 0.f : M, lsum, num);
         sm_num[wave][lane] = num;
-        if (lane == 0) sm_sum[wave] = lt;
+        const float ls = wave_sum(lsum);
+        if (lane == 0) sm_sum[wave] = ls;
         __syncthreads();
         if (wave != 0) return;
-        lt = 0.f;
+        float lt = 0.f;
         num = f32x2{0.f, 0.f};
         for (int w = 0; w < kReduceWaves; ++w) {
             lt += sm_sum[w];
             num += sm_num[w][lane];
         }
+        *o = lt > 0.f ? num * (vs / lt) : f32x2{0.f, 0.f};
     }
-    const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
-    *o = lt > 0.f ? num * (vs / lt) : f32x2{0.f, 0.f};
 }
 
 // gfx950 (MI355X) has 256 CUs; a grid of at most this many workgroups runs
@@ -1050,8 +1186,8 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
 #define KVFP8_ARGS                                                                               \
     a.q, a.k_new, a.v_new, static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool),    \
         fp8 ? a.k_scale : nullptr, fp8 ? a.v_scale : nullptr, a.block_table, a.bt_stride,        \
-        a.seq_lens, a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2, a.batch,      \
-        a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions
+        a.seq_lens, a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, a.counters, sm_log2,   \
+        a.batch, a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions
     if (use_wave_partitions(a)) {
         // persistent: at most 2 workgroups per CU, each streams its range of pages
         const int64_t wgs = std::min<int64_t>(2 * kNumCUs,
@@ -1089,9 +1225,11 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
     }
 #undef KVFP8_ARGS
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.num_partitions == 1) return e;
+    // the shared kernel combines its own partitions; the persistent one leaves
+    // them to the reduction kernel
+    if (e != hipSuccess || a.num_partitions == 1 || !use_wave_partitions(a)) return e;
     const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
-    const int extra = use_wave_partitions(a) ? 1 : 0;
+    const int extra = 1;            // the persistent kernel's slot after the last partition
 #define KVFP8_REDUCE(CO, WGS)                                                                    \
     hipLaunchKernelGGL(reduce_partials_kernel<CO>, dim3(static_cast<uint32_t>(WGS)),             \
                        dim3(kReduceWaves * 64), 0, stream, a.part_ml, a.part_acc, a.seq_lens,    \

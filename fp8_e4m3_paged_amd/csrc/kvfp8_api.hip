@@ -132,10 +132,12 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
     a.partition_tokens = pt;
     a.num_partitions = parts;
     if (parts > 1) {
-        const size_t slots = static_cast<size_t>(batch) * num_q_heads * kvfp8::partial_slots(parts);
-        const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
-        a.part_ml = static_cast<float*>(workspace);
-        a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+        const kvfp8::WorkspaceLayout w = kvfp8::workspace_layout(batch, num_q_heads, num_kv_heads,
+                                                                 parts);
+        char* base = static_cast<char*>(workspace);
+        a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+        a.part_ml = reinterpret_cast<float*>(base + w.ml);
+        a.part_acc = reinterpret_cast<float*>(base + w.acc);
     }
     return launch_status(kvfp8::launch_decode_attn(fp8, a, static_cast<hipStream_t>(stream)));
 }
@@ -231,10 +233,8 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
     if (pt <= 0) return 0;
     const int64_t parts = (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
     if (parts <= 1) return 0;
-    const size_t slots = static_cast<size_t>(batch) * num_q_heads * kvfp8::partial_slots(parts);
-    // [slots][2] (max, sum) then [slots][head_dim] outputs, 256-byte aligned
-    const size_t ml = ((slots * 2 * sizeof(float)) + 255) / 256 * 256;
-    return ml + slots * head_dim * sizeof(float);
+    // [batch][Hkv] counters, [slots][2] (max, sum), then [slots][head_dim] outputs
+    return kvfp8::workspace_layout(batch, num_q_heads, num_kv_heads, parts).total;
 }
 
 int paged_decode_attn(const void* q, int32_t cache_dtype, const void* k_pool, const void* v_pool,

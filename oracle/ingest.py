@@ -58,8 +58,9 @@ def scales_from_amax(amax) -> np.ndarray:
     rounded to fp32; with 53 >= 2 * 24 + 2 bits that double rounding equals
     rounding the exact quotient once (the tests also check it against exact
     rationals)."""
-    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
-    s = (a / 448.0).astype(np.float32)
+    with np.errstate(invalid="ignore"):           # signalling-NaN patterns stay NaN
+        a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+        s = (a / 448.0).astype(np.float32)
     ok = np.isfinite(a) & (a > 0)
     return np.where(ok, np.maximum(s, FLT_MIN), np.float32(1.0)).astype(np.float32)
 

@@ -254,10 +254,15 @@ def test_workspace_and_partition_sizing(real_lib):
     # one partition covers everything: no workspace
     assert k.paged_decode_attn_workspace_bytes(64, 64, 8, 8000, 8192) == 0
     # 16 requests, 64 heads, up to 131073 tokens at 512 -> 257 partitions, and
-    # one more partial slot per (request, query head) for the wave-mode kernel
+    # one more partial slot per (request, query head) for the wave-mode kernel;
+    # after 16 x 8 counters (512 bytes)
     n = 16 * 64 * (257 + 1)
     ml = -(-(n * 2 * 4) // 256) * 256
-    assert k.paged_decode_attn_workspace_bytes(16, 64, 8, 131073, 512) == ml + n * 128 * 4
+    assert k.paged_decode_attn_workspace_bytes(16, 64, 8, 131073, 512) == 512 + ml + n * 128 * 4
+    # counters rounded up to 256 bytes: 3 requests x 2 KV heads
+    n = 3 * 4 * (3 + 1)
+    assert k.paged_decode_attn_workspace_bytes(3, 4, 2, 3 * 1024, 1024) == \
+        256 + -(-(n * 2 * 4) // 256) * 256 + n * 128 * 4
     for b, h, L in [(64, 8, 9193), (1, 1, 256), (16, 8, 131073), (8, 8, 8192)]:
         pt = k.paged_decode_attn_partition_tokens(b, h, L, 0)
         assert pt % 16 == 0 and 16 <= pt <= 16384

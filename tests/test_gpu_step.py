@@ -121,8 +121,11 @@ def test_fused_append_every_bf16_value(kv, partition_tokens):
     t = lens - 1
     pages = bt[np.arange(batch), t // P]
     scales = _encode_scales()
-    say(f"fused encode p{partition_tokens}: {len(scales) // hkv} launches x 65536 patterns")
-    for i in range(0, len(scales), hkv):
+    starts = list(range(0, len(scales) - hkv + 1, hkv))
+    if starts[-1] + hkv < len(scales):
+        starts.append(len(scales) - hkv)             # the last few scales, in a full launch
+    say(f"fused encode p{partition_tokens}: {len(starts)} launches x 65536 patterns")
+    for i in starts:
         ks = scales[i:i + hkv].copy()
         vs = scales[::-1][i:i + hkv].copy()
         kp = torch.from_numpy(junk).to(DEV)
