@@ -462,8 +462,9 @@ def sweep_bench(args):
                        for l in range(wl.num_layers)] for i in range(total_steps)]
             outs = [torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
                     for _ in range(wl.num_layers)]
+            spt = max(args.partition_tokens, 0)          # -1 (default): automatic
             n = kv.paged_decode_attn_workspace_bytes(B, wl.num_q_heads, wl.num_kv_heads,
-                                                     wl.max_seq_len, 0)
+                                                     wl.max_seq_len, spt)
             ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=dev)
             cd = kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16
             sm = 1.0 / math.sqrt(wl.head_dim)
@@ -476,7 +477,7 @@ def sweep_bench(args):
                     calls.append(kv.paged_decode_attn_append(
                         q, kn, vn, st.k_pool[l], st.v_pool[l], st.k_scale[l], st.v_scale[l],
                         st.block_table, seq_lens[i], wl.max_seq_len, outs[l], sm, workspace=ws,
-                        abort=st.abort, cache_dtype=cd, prepare=prepare))
+                        abort=st.abort, cache_dtype=cd, partition_tokens=spt, prepare=prepare))
                 return calls
 
             for i in range(args.warmup):

@@ -622,6 +622,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 constexpr f32x2 kEmptySlot = {-INFINITY, 0.f};
+// Rows of at most this many slots are combined in one round trip.
+constexpr int kShortRow = 16;
 
 // Partials exchanged between the workgroups of one launch are written and
 // read with agent-scope atomic accesses: the stores write through to the
@@ -713,6 +715,31 @@ template <bool SHARED>
 __device__ __forceinline__ void reduce_row_wave(const f32x2* __restrict__ ml,
                                                 const float* __restrict__ acc, int np, float vs,
                                                 f32x2* o, int lane) {
+    if (np <= kShortRow) {
+        // one round trip: every (max, sum) pair and every slot's two dims
+        // are requested before any is used
+        const f32x2 e = lane < np ? load_f32x2<SHARED>(ml + lane) : kEmptySlot;
+        f32x2 v[kShortRow];
+#pragma unroll
+        for (int k = 0; k < kShortRow; ++k)              // slots past np re-read the last one
+            v[k] = load_f32x2<SHARED>(reinterpret_cast<const f32x2*>(
+                acc + static_cast<size_t>(min(k, np - 1)) * kDim));
+        if (__builtin_amdgcn_ballot_w64(e[1] < 0.f) != 0) {  // an invalid-page mark
+            *o = f32x2{0.f, 0.f};
+            return;
+        }
+        const float M = wave_max(e[0]);
+        const float w = exp2f(e[0] - (M == -INFINITY ? 0.f : M));   // 0 for empty slots
+        const float lt = wave_sum(w * e[1]);
+        f32x2 num = {0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < kShortRow; ++k) {
+            const f32x2 t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k)) * v[k];
+            num += k < np ? t : f32x2{0.f, 0.f};
+        }
+        *o = lt > 0.f ? num * (vs / lt) : f32x2{0.f, 0.f};
+        return;
+    }
     float mx;
     bool bad;
     row_slot_max<SHARED>(ml, np, 0, 64, lane, mx, bad);
@@ -770,7 +797,19 @@ void attn_partition_kernel(
     const int col = lane % 16;       // query column of the MFMA tiles
     const int jgrp = lane / 16;      // k-group of the operands / row group of the result
 
+    // The loads that do not depend on each other go out together: the
+    // request's length, this thread's first page id of the partition (within
+    // the table row whatever the length) and the query operand. A short
+    // request then waits one memory round trip before its tiles, not three.
+    const int t_begin = p * part_tokens;
+    const int pg0 = t_begin / kPage;
+    const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
+    const size_t q_row = static_cast<size_t>(b) * hq + g * group;
     const int L = seq_lens[b];
+    int32_t id0 = -1;
+    if (tid < part_tokens / kPage && pg0 + tid < bt_stride) id0 = bt_row[tid];
+    bf16x8 qop[4];
+    load_q_operand(qop, q, q_row, group, col, jgrp);
     const bool ok = request_ok(seq_lens, abort, b, L, max_seq_len, bt_stride);
     if (!ok || static_cast<int64_t>(p) * part_tokens >= L) {
         // A refused request's zeros come from its first partition's
@@ -781,25 +820,23 @@ void attn_partition_kernel(
         }
         return;
     }
-    const int t_begin = p * part_tokens;
     const int t_end = min(L, t_begin + part_tokens);
-    const int pg0 = t_begin / kPage;
     const int npg = (t_end + kPage - 1) / kPage - pg0;
 
     // Page ids -> LDS; any id outside the pool poisons the partition (its
     // output, and the request's, becomes zero and none of its pages is read).
     int bad = 0;
-    {
-        const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride + pg0;
-        for (int k = tid; k < npg; k += kThreads) {
-            const int32_t id = bt_row[k];
-            bad |= (id < 0 || id >= num_pages);
-            sm_ids[k] = id;
-        }
+    if (tid < npg) {
+        bad |= (id0 < 0 || id0 >= num_pages);
+        sm_ids[tid] = id0;
+    }
+    for (int k = tid + kThreads; k < npg; k += kThreads) {
+        const int32_t id = bt_row[k];
+        bad |= (id < 0 || id >= num_pages);
+        sm_ids[k] = id;
     }
     bad = __syncthreads_or(bad);
 
-    const size_t q_row = static_cast<size_t>(b) * hq + g * group;
     float m_run = -INFINITY;
     float l_run = 0.f;
     f32x4 acc_o[8];
@@ -807,8 +844,6 @@ void attn_partition_kernel(
     for (int c = 0; c < 8; ++c) acc_o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (!bad) {
-        bf16x8 qop[4];
-        load_q_operand(qop, q, q_row, group, col, jgrp);
         const float s_scale = FP8 ? sm_scale_log2 * k_scale[g] : sm_scale_log2;
         const auto tile_of = [&](int page_idx) __attribute__((always_inline)) -> size_t {
             const int id = __builtin_amdgcn_readfirstlane(sm_ids[page_idx]);

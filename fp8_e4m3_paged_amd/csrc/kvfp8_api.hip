@@ -43,9 +43,12 @@ int check_append_common(const void* k_new, const void* v_new, const int32_t* tok
 // Automatic split-K size. Long partitions stream best (the per-workgroup
 // set-up and the partial traffic are amortised, and no reduction pass is
 // needed with one partition), so split only as far as needed to keep 8
-// wavefronts streaming on every compute unit. Partitions are equal shares of
-// max_seq_len rounded up to 256 tokens, at least 512 and at most the LDS page
-// list's capacity.
+// wavefronts streaming on every compute unit, and into at most 16 partitions
+// (the combine then takes one round trip: at one request of 9,193 tokens the
+// step went from 0.129 ms with 18 partitions to 0.107 ms with 12). Partitions
+// are equal shares of max_seq_len rounded up to 256 tokens (whole page pairs
+// for each of 8 wavefronts), at least 512 and at most the LDS page list's
+// capacity.
 int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
     // 512 four-wave workgroups for the 256 CUs, or, when the (request, KV
     // head) items divide 256, 256 eight-wave ones (half the partitions to
@@ -55,6 +58,7 @@ int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len)
     if (items >= 512) parts = 1;
     else if (items <= 256 && 256 % items == 0) parts = 256 / items;
     else parts = (512 + items - 1) / items;
+    if (parts > 16) parts = 16;
     int64_t tokens = (static_cast<int64_t>(max_seq_len) + parts - 1) / parts;
     tokens = ((tokens + 255) / 256) * 256;
     if (tokens < 512) tokens = 512;
