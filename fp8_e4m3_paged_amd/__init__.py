@@ -9,8 +9,8 @@ works but the first call raises ``KvLibraryMissing``.
 
 Entry points (same names as the C ABI):
     kv_verify_tags, kv_append_quant, kv_append_bf16, paged_decode_attn,
-    paged_decode_attn_append, paged_decode_attn_workspace_bytes,
-    paged_decode_attn_partition_tokens, kv_amax_accumulate,
+    paged_decode_attn_append, paged_decode_attn_append_noalloc,
+    paged_decode_attn_workspace_bytes, paged_decode_attn_partition_tokens, kv_amax_accumulate,
     kv_scales_from_amax, kv_ingest_prefill, kv_status_str
 and the weight-only quantized decode GEMV: wq_packed_bytes, wq_quantize_pack,
 wq_gemv;
@@ -34,6 +34,7 @@ __all__ = [
     "KV_CACHE_FP8_E4M3", "KV_CACHE_BF16", "KvError", "KvLibraryMissing", "lib_path",
     "load", "kv_status_str", "kv_verify_tags", "kv_append_quant", "kv_append_bf16",
     "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_workspace_bytes",
+    "paged_decode_attn_append_noalloc", "KV_NOALLOC_SCRATCH_BYTES",
     "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
     "kv_amax_accumulate", "kv_scales_from_amax", "kv_ingest_prefill", "ingest_layer",
     "PagePool", "KV_ERR_EXHAUSTED", "KV_ERR_STATE",
@@ -50,6 +51,7 @@ KV_CACHE_FP8_E4M3 = 0
 KV_CACHE_BF16 = 1
 PAGE_SIZE = 16
 HEAD_DIM = 128
+KV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -89,6 +91,9 @@ _SIGS = {
     "paged_decode_attn_append": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _I,
                                                 _P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _I,
                                                 _I, _P, ctypes.c_size_t, _P]),
+    "paged_decode_attn_append_noalloc": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I,
+                                                        _P, _I, _P, _P, ctypes.c_float, _I, _I,
+                                                        _I, _I, _I, _I, _I, _P]),
     "kv_amax_accumulate": (ctypes.c_int, [_P, _L, _I, _I, _P, _P]),
     "wq_packed_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "wq_quantize_pack": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
@@ -415,6 +420,41 @@ def paged_decode_attn_append(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, 
     return _call("paged_decode_attn_append", args, prepare,
                  (q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
                   abort, out, workspace))
+
+
+def paged_decode_attn_append_noalloc(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                                     block_table, seq_lens, max_seq_len, out, sm_scale,
+                                     abort=None, partition_tokens=0,
+                                     cache_dtype=KV_CACHE_FP8_E4M3, page_size=PAGE_SIZE,
+                                     stream=None, prepare=False):
+    """paged_decode_attn_append with the library's own static split-K scratch
+    (KV_NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace argument: the C
+    call allocates nothing. Calls that overlap on one GPU race on the scratch."""
+    d = _dt()
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q / out must both be [batch][num_q_heads][head_dim]")
+    batch, hq, hd = q.shape
+    hkv = k_pool.shape[1]
+    if k_new.shape != (batch, hkv, hd) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [batch][num_kv_heads][head_dim]")
+    fp8 = cache_dtype == KV_CACHE_FP8_E4M3
+    _check_pools(k_pool, v_pool, hkv, fp8)
+    _check_requests(batch, seq_lens, block_table, abort)
+    _check_scales(k_scale, v_scale, hkv, fp8)
+    args = (
+        _ptr(q, "q", d["bf16"]), _ptr(k_new, "k_new", d["bf16"]), _ptr(v_new, "v_new", d["bf16"]),
+        int(cache_dtype), _ptr(k_pool, "k_pool", d["u8"] if fp8 else d["pool"]),
+        _ptr(v_pool, "v_pool", d["u8"] if fp8 else d["pool"]),
+        _ptr(k_scale, "k_scale", d["f32"], allow_none=not fp8),
+        _ptr(v_scale, "v_scale", d["f32"], allow_none=not fp8),
+        _ptr(block_table, "block_table", d["i32"]), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", d["i32"]), int(max_seq_len),
+        _ptr(abort, "abort", d["u8"], allow_none=True), _ptr(out, "out", d["f32"]),
+        float(sm_scale), batch, hq, hkv, hd, page_size, k_pool.shape[0], int(partition_tokens),
+        _stream(stream))
+    return _call("paged_decode_attn_append_noalloc", args, prepare,
+                 (q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                  abort, out))
 
 
 def decode_step(layers, block_table, seq_lens, tok_pos, tok_seq, max_seq_len, sm_scale,

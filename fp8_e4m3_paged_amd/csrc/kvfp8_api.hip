@@ -5,6 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kv_launch.h"
 
 namespace {
@@ -68,6 +71,49 @@ int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len)
 
 }  // namespace
 
+// ---- the no-alloc entry point's scratch ------------------------------------
+// The split-K workspace of paged_decode_attn_append_noalloc: a static device
+// array that every GPU the library runs on holds (zero-filled when the code
+// object is loaded) until the process ends. Host code never uses the array's
+// name as an address: the first call on a device asks the runtime for that
+// device's copy (hipGetSymbolAddress, with that device current) and keeps the
+// pointer; kernels receive that pointer. The counters at its start are zero
+// on load and every call leaves them at zero; the rest is overwritten before
+// it is read. Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[KV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch's device address on the device `stream` belongs to (the
+// current device for the null stream).
+int scratch_for_stream(hipStream_t stream, void** out) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return KV_ERR_LAUNCH;
+    int dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return KV_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return KV_ERR_LAUNCH;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (dev != cur && hipSetDevice(dev) != hipSuccess) return KV_ERR_LAUNCH;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (dev != cur && hipSetDevice(cur) != hipSuccess) return KV_ERR_LAUNCH;
+            if (e != hipSuccess || p == nullptr) return KV_ERR_LAUNCH;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return KV_OK;
+}
+
+}  // namespace
+
 // Shared body of paged_decode_attn (k_new = v_new = NULL: read only) and
 // paged_decode_attn_append (the new token is written by the kernel first).
 static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_t cache_dtype,
@@ -76,7 +122,8 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
                      int32_t max_seq_len, const uint8_t* abort, float* out, float sm_scale,
                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t page_size, int32_t num_pages, int32_t partition_tokens,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream,
+                     bool static_workspace = false) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || bt_stride < 0 || num_pages < 0 ||
         max_seq_len < 0)
         return KV_ERR_SHAPE;
@@ -110,6 +157,13 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
     const int32_t parts = static_cast<int32_t>(parts64);
     const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
                                                           head_dim, max_seq_len, pt);
+    if (parts > 1 && static_workspace) {
+        // the library's own scratch, resolved only after every check passed
+        if (need > KV_NOALLOC_SCRATCH_BYTES) return KV_ERR_WORKSPACE;
+        const int r = scratch_for_stream(static_cast<hipStream_t>(stream), &workspace);
+        if (r != KV_OK) return r;
+        workspace_bytes = KV_NOALLOC_SCRATCH_BYTES;
+    }
     if (parts > 1) {
         if (!workspace || workspace_bytes < need) return KV_ERR_WORKSPACE;
         if (misaligned(workspace, 16)) return KV_ERR_ALIGN;
@@ -270,6 +324,22 @@ int paged_decode_attn_append(const void* q, const void* k_new, const void* v_new
                      block_table, bt_stride, seq_lens, max_seq_len, abort, out, sm_scale, batch,
                      num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                      partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int paged_decode_attn_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                     int32_t cache_dtype, void* k_pool, void* v_pool,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_table, int32_t bt_stride,
+                                     const int32_t* seq_lens, int32_t max_seq_len,
+                                     const uint8_t* abort, float* out, float sm_scale,
+                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                     int32_t partition_tokens, void* stream) {
+    if (batch > 0 && (!k_new || !v_new)) return KV_ERR_NULL;
+    return attn_impl(q, k_new, v_new, cache_dtype, k_pool, v_pool, k_scale, v_scale,
+                     block_table, bt_stride, seq_lens, max_seq_len, abort, out, sm_scale, batch,
+                     num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                     partition_tokens, nullptr, 0, stream, /*static_workspace=*/true);
 }
 
 int kv_amax_accumulate(const void* x, int64_t n_rows, int32_t num_kv_heads, int32_t head_dim,

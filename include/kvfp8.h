@@ -276,6 +276,31 @@ int paged_decode_attn_append(const void* q, const void* k_new, const void* v_new
                              size_t workspace_bytes, void* stream);
 
 /*
+ * paged_decode_attn_append without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). The split-K workspace is a static
+ * device array of KV_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the call allocates nothing. Same
+ * arguments and result as paged_decode_attn_append otherwise. Sizes whose
+ * workspace (paged_decode_attn_workspace_bytes) exceeds the array are refused
+ * with KV_ERR_WORKSPACE before anything is enqueued. All calls on one GPU
+ * share that GPU's array: calls that may overlap in time on one GPU (other
+ * streams, other host threads) race and must not be issued; calls in order on
+ * one stream are fine. KV_ERR_LAUNCH also if the array's device address
+ * cannot be obtained.
+ */
+#define KV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_decode_attn_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                     int32_t cache_dtype, void* k_pool, void* v_pool,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_table, int32_t bt_stride,
+                                     const int32_t* seq_lens, int32_t max_seq_len,
+                                     const uint8_t* abort, float* out, float sm_scale,
+                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                     int32_t partition_tokens, void* stream);
+
+/*
  * Prefill ingest: the handoff of a prompt's BF16 keys and values into the
  * decode cache. The pages run prefill and decode in separate pools; prefill
  * builds a prompt's initial cache state in BF16, decode reads the smaller

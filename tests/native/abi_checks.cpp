@@ -96,6 +96,20 @@ int main() {
                                                   nullptr, 0, nullptr),
            KV_ERR_NULL);
 
+    // the no-alloc entry point: refused before its scratch is looked up
+    expect("noalloc scratch", paged_decode_attn_append_noalloc(
+               A, A, A, 0, A, A, P<float>(), P<float>(), P<int32_t>(), 8193, P<int32_t>(), 131073,
+               nullptr, P<float>(), 0.1f, 16, 64, 8, 128, 16, 10, 512, nullptr),
+           KV_ERR_WORKSPACE);
+    expect("noalloc null", paged_decode_attn_append_noalloc(
+               A, nullptr, A, 0, A, A, P<float>(), P<float>(), P<int32_t>(), 8, P<int32_t>(), 100,
+               nullptr, P<float>(), 0.1f, 4, 64, 8, 128, 16, 10, 0, nullptr),
+           KV_ERR_NULL);
+    expect("noalloc group", paged_decode_attn_append_noalloc(
+               A, A, A, 0, A, A, P<float>(), P<float>(), P<int32_t>(), 8, P<int32_t>(), 100,
+               nullptr, P<float>(), 0.1f, 4, 64, 2, 128, 16, 10, 0, nullptr),
+           KV_ERR_UNSUPPORTED);
+
     // prefill ingest, weight GEMV
     expect("ingest dtype", kv_ingest_prefill(A, A, 10, P<int32_t>(), P<int32_t>(), 2, 10, P<int32_t>(),
                                              4, 5, P<float>(), P<float>(), A, A, 10, 8, 128, 16,

@@ -80,7 +80,8 @@ def test_header_declares_the_entry_points():
               "paged_decode_attn_append", "kv_amax_accumulate", "kv_scales_from_amax",
               "kv_ingest_prefill", "kv_status_str", "kv_pool_create", "kv_pool_destroy",
               "kv_pool_alloc", "kv_pool_free", "kv_pool_tags", "kv_pool_record_check",
-              "kv_pool_get_stats", "wq_packed_bytes", "wq_quantize_pack", "wq_gemv"]:
+              "kv_pool_get_stats", "wq_packed_bytes", "wq_quantize_pack", "wq_gemv",
+              "paged_decode_attn_append_noalloc"]:
         assert n in names
 
 
