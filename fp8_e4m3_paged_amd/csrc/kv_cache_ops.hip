@@ -17,11 +17,13 @@ namespace kvfp8 {
 
 // ---------------------------------------------------------------------------
 // kv_verify_tags: one 1024-thread workgroup per request. Each thread checks up
-// to 8 logical pages per sweep; loads of a sweep are independent so their
-// latencies overlap, and one sweep covers 8192 pages (131,072 tokens), so
-// even a very long request costs two dependent round trips (table entries,
-// then the gathered pool tags). The workgroup ORs the per-thread verdicts and
-// one thread writes the request's flag.
+// to 8 logical pages per sweep and one sweep covers 8192 pages (131,072
+// tokens). A sweep is branch-free: the table entries and expected tags are
+// loaded with indices clamped into the request's row, then every pool tag is
+// gathered (an out-of-range id reads tag 0 instead, and is flagged anyway),
+// so all loads of a step are in flight together and a sweep costs two memory
+// round trips, not one per page. The workgroup ORs the per-thread verdicts
+// and one thread writes the request's flag.
 // ---------------------------------------------------------------------------
 constexpr int kVerifyThreads = 1024;
 constexpr int kVerifyUnroll = 8;
@@ -39,30 +41,32 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_tags_kernel(
     } else {
         npages = (static_cast<int64_t>(L) + kPage - 1) / kPage;
         if (npages > bt_stride) bad = 1;
+        if (npages > 0 && num_pages <= 0) bad = 1;       // no page can be valid (no tags to read)
     }
-    if (!bad) {
+    if (!bad && npages > 0) {
         const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride;
         const uint32_t* ex_row = expected_tags + static_cast<size_t>(b) * bt_stride;
         for (int64_t base = 0; base < npages; base += kVerifyThreads * kVerifyUnroll) {
             int32_t page[kVerifyUnroll];
             uint32_t want[kVerifyUnroll];
+            uint32_t have[kVerifyUnroll];
 #pragma unroll
             for (int u = 0; u < kVerifyUnroll; ++u) {
-                const int64_t j = base + u * kVerifyThreads + threadIdx.x;
-                page[u] = 0;
-                want[u] = 0;
-                if (j < npages) {
-                    page[u] = bt_row[j];
-                    want[u] = ex_row[j];
-                }
+                const int64_t j = min(base + u * kVerifyThreads + threadIdx.x, npages - 1);
+                page[u] = bt_row[j];
+                want[u] = ex_row[j];
+            }
+#pragma unroll
+            for (int u = 0; u < kVerifyUnroll; ++u) {
+                const int32_t p = page[u];
+                have[u] = pool_tags[(p >= 0 && p < num_pages) ? p : 0];
             }
 #pragma unroll
             for (int u = 0; u < kVerifyUnroll; ++u) {
                 const int64_t j = base + u * kVerifyThreads + threadIdx.x;
-                if (j < npages) {
-                    const int32_t p = page[u];
-                    if (p < 0 || p >= num_pages || pool_tags[p] != want[u]) bad = 1;
-                }
+                const int32_t p = page[u];
+                const bool wrong = p < 0 || p >= num_pages || have[u] != want[u];
+                bad |= (j < npages && wrong) ? 1 : 0;
             }
         }
     }
