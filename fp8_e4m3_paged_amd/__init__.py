@@ -83,8 +83,8 @@ _SIGS = {
                                        _I, _I, _I, _P, _P]),
     "kv_append_bf16": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I,
                                       _I, _P, _P]),
-    "paged_decode_attn_partition_tokens": (ctypes.c_int32, [_I, _I, _I, _I]),
-    "paged_decode_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "paged_decode_attn_partition_tokens": (ctypes.c_int32, [_I, _I, _I, _I, _I]),
+    "paged_decode_attn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
     "paged_decode_attn": (ctypes.c_int, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P,
                                          ctypes.c_float, _I, _I, _I, _I, _I, _I, _I, _P,
                                          ctypes.c_size_t, _P]),
@@ -331,19 +331,21 @@ def kv_append_bf16(k_new, v_new, tok_seq, tok_pos, block_table, k_pool, v_pool, 
                    v_pool, abort, batch, page_size, stream, prepare)
 
 
-def paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len, partition_tokens=0):
+def paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len, partition_tokens=0,
+                                       cache_dtype=KV_CACHE_FP8_E4M3):
     v = load().paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
-                                                  partition_tokens)
+                                                  partition_tokens, int(cache_dtype))
     if v < 0:
         raise KvError("paged_decode_attn_partition_tokens", v)
     return v
 
 
 def paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len,
-                                      partition_tokens=0, head_dim=HEAD_DIM):
+                                      partition_tokens=0, head_dim=HEAD_DIM,
+                                      cache_dtype=KV_CACHE_FP8_E4M3):
     return int(load().paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
                                                         head_dim, max_seq_len,
-                                                        partition_tokens))
+                                                        partition_tokens, int(cache_dtype)))
 
 
 def paged_decode_attn(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, max_seq_len,

@@ -48,14 +48,14 @@ int check_append_common(const void* k_new, const void* v_new, const int32_t* tok
 // needed with one partition), so split only as far as needed to keep 8
 // wavefronts streaming on every compute unit, and into at most 16 partitions
 // (the combine then takes one round trip: at one request of 9,193 tokens the
-// step went from 0.129 ms with 18 partitions to 0.107 ms with 12). Partitions
-// are equal shares of max_seq_len rounded up to 256 tokens (whole page pairs
-// for each of 8 wavefronts), at least 512 and at most the LDS page list's
-// capacity.
-int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
-    // 512 four-wave workgroups for the 256 CUs, or, when the (request, KV
-    // head) items divide 256, 256 eight-wave ones (half the partitions to
-    // reduce). One partition when the items alone fill the chip.
+// FP8 step went from 0.129 ms with 18 partitions to 0.107 ms with 12).
+// Partitions are equal shares of max_seq_len rounded up to whole page pairs
+// (32 tokens), at most the LDS page list's capacity, and hold at least
+// 192 KiB of K and V per KV head (768 FP8 or 384 BF16 tokens): below that
+// the wavefronts' pipeline start-up dominates. At that one request the FP8
+// step takes 0.107 ms with 12 partitions of 768 tokens and 0.125 ms with 16
+// of 576, while the BF16 step takes 0.143 ms with 16 and 0.168 ms with 12.
+int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, bool fp8) {
     const int64_t items = static_cast<int64_t>(batch) * num_kv_heads;
     int64_t parts;
     if (items >= 512) parts = 1;
@@ -63,8 +63,9 @@ int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len)
     else parts = (512 + items - 1) / items;
     if (parts > 16) parts = 16;
     int64_t tokens = (static_cast<int64_t>(max_seq_len) + parts - 1) / parts;
-    tokens = ((tokens + 255) / 256) * 256;
-    if (tokens < 512) tokens = 512;
+    tokens = ((tokens + 31) / 32) * 32;
+    const int64_t min_tokens = (192 * 1024) / (2 * KV_HEAD_DIM * (fp8 ? 1 : 2));
+    if (tokens < min_tokens) tokens = min_tokens;
     if (tokens > KV_MAX_PARTITION_TOKENS) tokens = KV_MAX_PARTITION_TOKENS;
     return static_cast<int32_t>(tokens);
 }
@@ -134,7 +135,7 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
         return KV_ERR_UNSUPPORTED;
     if (!(sm_scale >= 0.0f) || !(sm_scale < INFINITY)) return KV_ERR_UNSUPPORTED;
     const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
-                                                          partition_tokens);
+                                                          partition_tokens, cache_dtype);
     if (pt <= 0) return KV_ERR_UNSUPPORTED;
     const int64_t parts64 = max_seq_len == 0 ? 1 : (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
     if (parts64 > KV_MAX_PARTITIONS) return KV_ERR_UNSUPPORTED;
@@ -156,7 +157,7 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
         return KV_ERR_ALIGN;
     const int32_t parts = static_cast<int32_t>(parts64);
     const size_t need = paged_decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads,
-                                                          head_dim, max_seq_len, pt);
+                                                          head_dim, max_seq_len, pt, cache_dtype);
     if (parts > 1 && static_workspace) {
         // the library's own scratch, resolved only after every check passed
         if (need > KV_NOALLOC_SCRATCH_BYTES) return KV_ERR_WORKSPACE;
@@ -269,25 +270,29 @@ int kv_append_bf16(const void* k_new, const void* v_new, const int32_t* tok_seq,
 }
 
 int32_t paged_decode_attn_partition_tokens(int32_t batch, int32_t num_kv_heads,
-                                           int32_t max_seq_len, int32_t partition_tokens) {
+                                           int32_t max_seq_len, int32_t partition_tokens,
+                                           int32_t cache_dtype) {
     if (partition_tokens < 0) return KV_ERR_UNSUPPORTED;
+    if (cache_dtype != KV_CACHE_FP8_E4M3 && cache_dtype != KV_CACHE_BF16)
+        return KV_ERR_UNSUPPORTED;
     if (partition_tokens > 0) {
         if (partition_tokens % KV_PAGE_SIZE != 0 || partition_tokens > KV_MAX_PARTITION_TOKENS)
             return KV_ERR_UNSUPPORTED;
         return partition_tokens;
     }
     if (batch <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return 1024;
-    return auto_partition(batch, num_kv_heads, max_seq_len);
+    return auto_partition(batch, num_kv_heads, max_seq_len, cache_dtype == KV_CACHE_FP8_E4M3);
 }
 
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t max_seq_len, int32_t partition_tokens) {
+                                         int32_t max_seq_len, int32_t partition_tokens,
+                                         int32_t cache_dtype) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
         head_dim != KV_HEAD_DIM)
         return 0;
     const int32_t pt = paged_decode_attn_partition_tokens(batch, num_kv_heads, max_seq_len,
-                                                          partition_tokens);
+                                                          partition_tokens, cache_dtype);
     if (pt <= 0) return 0;
     const int64_t parts = (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
     if (parts <= 1) return 0;

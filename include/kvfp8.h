@@ -178,12 +178,15 @@ int kv_append_bf16(const void* k_new, const void* v_new,
 
 /*
  * Split-K partition size (tokens) that paged_decode_attn will use for these
- * sizes. partition_tokens > 0 is returned unchanged if it is a multiple of
- * 16 and at most KV_MAX_PARTITION_TOKENS, else KV_ERR_UNSUPPORTED;
- * partition_tokens == 0 picks one (a pure function of the arguments).
+ * sizes and cache_dtype (KV_CACHE_*; anything else: KV_ERR_UNSUPPORTED).
+ * partition_tokens > 0 is returned unchanged if it is a multiple of 16 and
+ * at most KV_MAX_PARTITION_TOKENS, else KV_ERR_UNSUPPORTED;
+ * partition_tokens == 0 picks one (a pure function of the arguments; the
+ * BF16 cache, with twice the bytes per token, may get shorter partitions).
  */
 int32_t paged_decode_attn_partition_tokens(int32_t batch, int32_t num_kv_heads,
-                                           int32_t max_seq_len, int32_t partition_tokens);
+                                           int32_t max_seq_len, int32_t partition_tokens,
+                                           int32_t cache_dtype);
 
 /*
  * Bytes of device workspace paged_decode_attn needs for these sizes (0 when a
@@ -194,11 +197,13 @@ int32_t paged_decode_attn_partition_tokens(int32_t batch, int32_t num_kv_heads,
  * Zero-fill it once before its first use: the counters must start at zero,
  * and every call leaves them at zero again (the rest is overwritten before
  * it is read), so one buffer serves any later calls and sizes that fit it.
- * Returns 0 for unsupported arguments.
+ * The partition count, and so the size, depends on cache_dtype when
+ * partition_tokens is 0. Returns 0 for unsupported arguments.
  */
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t max_seq_len, int32_t partition_tokens);
+                                         int32_t max_seq_len, int32_t partition_tokens,
+                                         int32_t cache_dtype);
 
 /*
  * Decode-step attention over the paged cache, dequantizing on read.

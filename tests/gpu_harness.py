@@ -27,8 +27,11 @@ def sm_scale_for(wl) -> float:
 
 
 def workspace(wl, partition_tokens: int, max_seq_len=None):
-    n = kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads,
-                                             max_seq_len or wl.max_seq_len, partition_tokens)
+    """A zero-filled workspace that fits either cache's partitioning."""
+    n = max(kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads,
+                                                 max_seq_len or wl.max_seq_len, partition_tokens,
+                                                 cache_dtype=cd)
+            for cd in (kv.KV_CACHE_FP8_E4M3, kv.KV_CACHE_BF16))
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV) if n else None
 
 

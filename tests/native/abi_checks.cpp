@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 
 #include "kvfp8.h"
 
@@ -61,15 +62,21 @@ int main() {
            KV_ERR_ALIGN);
 
     // attention: sizing at the extremes, then refusals
-    for (int32_t b : big)
-        for (int32_t L : big) {
-            const int32_t pt = paged_decode_attn_partition_tokens(b, 8, L, 0);
-            if (pt != KV_ERR_UNSUPPORTED && (pt < 16 || pt > KV_MAX_PARTITION_TOKENS || pt % 16))
-                expect("partition tokens range", pt, 512);
-            (void)paged_decode_attn_workspace_bytes(b, 64, 8, 128, L, 0);
-            (void)paged_decode_attn_workspace_bytes(b, INT32_MAX, 1, 128, L, 16);
-            (void)paged_decode_attn_workspace_bytes(b, 64, INT32_MAX, 128, L, 16384);
-        }
+    for (int32_t cd : {KV_CACHE_FP8_E4M3, KV_CACHE_BF16})
+        for (int32_t b : big)
+            for (int32_t L : big) {
+                const int32_t pt = paged_decode_attn_partition_tokens(b, 8, L, 0, cd);
+                if (pt != KV_ERR_UNSUPPORTED &&
+                    (pt < 16 || pt > KV_MAX_PARTITION_TOKENS || pt % 16))
+                    expect("partition tokens range", pt, 512);
+                (void)paged_decode_attn_workspace_bytes(b, 64, 8, 128, L, 0, cd);
+                (void)paged_decode_attn_workspace_bytes(b, INT32_MAX, 1, 128, L, 16, cd);
+                (void)paged_decode_attn_workspace_bytes(b, 64, INT32_MAX, 128, L, 16384, cd);
+            }
+    expect("partition tokens dtype", paged_decode_attn_partition_tokens(4, 8, 1000, 0, 7),
+           KV_ERR_UNSUPPORTED);
+    if (paged_decode_attn_workspace_bytes(4, 64, 8, 128, 100000, 0, 7) != 0)
+        expect("workspace dtype", 1, 0);
     expect("attn partitions", paged_decode_attn(A, 0, A, A, P<float>(), P<float>(), P<int32_t>(), 8,
                                                  P<int32_t>(), INT32_MAX, nullptr, P<float>(), 0.1f,
                                                  4, 64, 8, 128, 16, 10, 16, A, 1 << 20, nullptr),

@@ -239,8 +239,9 @@ def test_ingest_layer_then_decode_attention(kv, cache):
     # attention over the ingested tokens (no append: L = the prompt length)
     q = torch.from_numpy(wl.q_bits(0, 0).view(np.int16)).to(DEV)
     out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=DEV)
-    n = kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads,
-                                             wl.max_seq_len, 0)
+    n = kv.paged_decode_attn_workspace_bytes(
+        wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.max_seq_len, 0,
+        cache_dtype=kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16)
     ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
     kv.paged_decode_attn(q, st.k_pool[0], st.v_pool[0], ks if cache == "fp8" else None,
                          vs if cache == "fp8" else None, st.block_table, lens0, wl.max_seq_len,

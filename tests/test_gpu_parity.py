@@ -326,7 +326,9 @@ def _edge_run(kv, e, cache, lens=None, abort=None, max_seq_len=None, partition_t
     batch, hq, _ = e["q"].shape
     msl = int(lens.max()) if max_seq_len is None else max_seq_len
     out = torch.full((batch, hq, 128), float("nan"), device=DEV)
-    n = kv.paged_decode_attn_workspace_bytes(batch, hq, e["kp"].shape[1], msl, partition_tokens)
+    n = kv.paged_decode_attn_workspace_bytes(
+        batch, hq, e["kp"].shape[1], msl, partition_tokens,
+        cache_dtype=kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16)
     ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
     btt = e["btt"] if bt is None else torch.from_numpy(bt).to(DEV)
     kv.paged_decode_attn(torch.from_numpy(e["q"].view(np.int16)).to(DEV), e["kp"], e["vp"],
