@@ -462,11 +462,14 @@ def sweep_bench(args):
             n = kv.paged_decode_attn_workspace_bytes(B, wl.num_q_heads, wl.num_kv_heads,
                                                      wl.max_seq_len, spt, cache_dtype=cd)
             ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=dev)
+            vws_n = kv.kv_verify_tags_workspace_bytes(B, st.block_table.shape[1])
+            vws = torch.zeros(vws_n, dtype=torch.uint8, device=dev) if vws_n else None
             sm = 1.0 / math.sqrt(wl.head_dim)
 
             def step(i, prepare=False):
                 calls = [kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags,
-                                           seq_lens[i], st.abort, prepare=prepare)]
+                                           seq_lens[i], st.abort, prepare=prepare,
+                                           workspace=vws)]
                 for l in range(wl.num_layers):
                     q, kn, vn = inputs[i][l]
                     calls.append(kv.paged_decode_attn_append(
@@ -694,11 +697,15 @@ def main():
     ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps * (1 if fused else wl.num_layers))]
 
+    # counters of the split tag check (rows longer than one 2,048-page chunk)
+    vws_n = kv.kv_verify_tags_workspace_bytes(wl.batch, st.block_table.shape[1])
+    vws = torch.zeros(vws_n, dtype=torch.uint8, device=dev) if vws_n else None
+
     def run_step(s, timed_slot=None, check=verify, stream=stream):
         abort = st.abort if check else None
         if check:
             kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens[s],
-                              st.abort, stream=stream)
+                              st.abort, stream=stream, workspace=vws)
         for layer in range(wl.num_layers):
             q, kn, vn = inputs[s][layer]
             if fused:

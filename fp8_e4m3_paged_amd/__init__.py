@@ -8,7 +8,8 @@ fallback: if the shared library is not built, importing this package still
 works but the first call raises ``KvLibraryMissing``.
 
 Entry points (same names as the C ABI):
-    kv_verify_tags, kv_append_quant, kv_append_bf16, paged_decode_attn,
+    kv_verify_tags, kv_verify_tags_workspace_bytes, kv_append_quant, kv_append_bf16,
+    paged_decode_attn,
     paged_decode_attn_append, paged_decode_attn_append_noalloc,
     paged_decode_attn_workspace_bytes, paged_decode_attn_partition_tokens, kv_amax_accumulate,
     kv_scales_from_amax, kv_ingest_prefill, kv_status_str
@@ -32,7 +33,8 @@ import os
 
 __all__ = [
     "KV_CACHE_FP8_E4M3", "KV_CACHE_BF16", "KvError", "KvLibraryMissing", "lib_path",
-    "load", "kv_status_str", "kv_verify_tags", "kv_append_quant", "kv_append_bf16",
+    "load", "kv_status_str", "kv_verify_tags", "kv_verify_tags_workspace_bytes",
+    "kv_append_quant", "kv_append_bf16",
     "paged_decode_attn", "paged_decode_attn_append", "paged_decode_attn_workspace_bytes",
     "paged_decode_attn_append_noalloc", "KV_NOALLOC_SCRATCH_BYTES",
     "paged_decode_attn_partition_tokens", "decode_step", "PAGE_SIZE", "HEAD_DIM",
@@ -78,7 +80,9 @@ _I = ctypes.c_int32
 _L = ctypes.c_int64
 _SIGS = {
     "kv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
-    "kv_verify_tags": (ctypes.c_int, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P]),
+    "kv_verify_tags": (ctypes.c_int, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P, ctypes.c_size_t,
+                                      _P]),
+    "kv_verify_tags_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "kv_append_quant": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _I,
                                        _I, _I, _I, _P, _P]),
     "kv_append_bf16": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I,
@@ -258,10 +262,16 @@ def _dt():
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
+def kv_verify_tags_workspace_bytes(batch, bt_stride):
+    return int(load().kv_verify_tags_workspace_bytes(batch, bt_stride))
+
+
 def kv_verify_tags(pool_tags, block_table, expected_tags, seq_lens, abort_out,
-                   page_size=PAGE_SIZE, stream=None, prepare=False):
+                   page_size=PAGE_SIZE, stream=None, prepare=False, workspace=None):
     """abort_out[b] = 1 iff request b's recorded (page, tag) pairs disagree with the pool.
-    With prepare=True nothing is enqueued; the checked call is returned as a ``Prepared``."""
+    ``workspace`` (optional, zero-filled once, kv_verify_tags_workspace_bytes long)
+    lets several workgroups share a long row. With prepare=True nothing is
+    enqueued; the checked call is returned as a ``Prepared``."""
     d = _dt()
     batch = seq_lens.numel()
     if block_table.dim() != 2 or expected_tags.shape != block_table.shape:
@@ -272,9 +282,12 @@ def kv_verify_tags(pool_tags, block_table, expected_tags, seq_lens, abort_out,
             _ptr(block_table, "block_table", d["i32"]),
             _ptr(expected_tags, "expected_tags", d["u32"]),
             block_table.shape[1], _ptr(seq_lens, "seq_lens", d["i32"]),
-            batch, page_size, _ptr(abort_out, "abort_out", d["u8"]), _stream(stream))
+            batch, page_size, _ptr(abort_out, "abort_out", d["u8"]),
+            _ptr(workspace, "workspace", allow_none=True),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream))
     return _call("kv_verify_tags", args, prepare,
-                 (pool_tags, block_table, expected_tags, seq_lens, abort_out))
+                 (pool_tags, block_table, expected_tags, seq_lens, abort_out, workspace))
 
 
 def _append(fp8, k_new, v_new, tok_seq, tok_pos, block_table, k_scale, v_scale, k_pool, v_pool,
@@ -461,17 +474,19 @@ def paged_decode_attn_append_noalloc(q, k_new, v_new, k_pool, v_pool, k_scale, v
 
 def decode_step(layers, block_table, seq_lens, tok_pos, tok_seq, max_seq_len, sm_scale,
                 pool_tags=None, expected_tags=None, abort=None, cache_dtype=KV_CACHE_FP8_E4M3,
-                workspace=None, partition_tokens=0, fused=True, stream=None):
+                workspace=None, partition_tokens=0, fused=True, stream=None,
+                verify_workspace=None):
     """Enqueue one decode step: tag check (if pool_tags is given), then for
     each layer the append of the new token and attention over the pages
     (one fused launch per layer, or the two separate calls with fused=False).
 
     ``layers`` is a sequence of dicts with keys q, k_new, v_new, k_pool, v_pool,
     k_scale, v_scale, out. With pool_tags=None no check runs and abort=None is
-    passed on (the no-op tracker).
+    passed on (the no-op tracker). ``verify_workspace`` goes to the tag check.
     """
     if pool_tags is not None:
-        kv_verify_tags(pool_tags, block_table, expected_tags, seq_lens, abort, stream=stream)
+        kv_verify_tags(pool_tags, block_table, expected_tags, seq_lens, abort, stream=stream,
+                       workspace=verify_workspace)
     else:
         abort = None
     for ly in layers:

@@ -21,9 +21,11 @@ namespace kvfp8 {
 // tokens). A sweep is branch-free: the table entries and expected tags are
 // loaded with indices clamped into the request's row, then every pool tag is
 // gathered (an out-of-range id reads tag 0 instead, and is flagged anyway),
-// so all loads of a step are in flight together and a sweep costs two memory
-// round trips, not one per page. The workgroup ORs the per-thread verdicts
-// and one thread writes the request's flag.
+// so all loads of a step are in flight together. The first sweep's table
+// loads are clamped into the table row (bt_stride entries) rather than the
+// request's pages, so they go out together with the length load and the
+// check costs two memory round trips, not three. The workgroup ORs the
+// per-thread verdicts and one thread writes the request's flag.
 // ---------------------------------------------------------------------------
 constexpr int kVerifyThreads = 1024;
 constexpr int kVerifyUnroll = 8;
@@ -33,6 +35,18 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_tags_kernel(
     const int32_t* __restrict__ block_table, const uint32_t* __restrict__ expected_tags,
     int32_t bt_stride, const int32_t* __restrict__ seq_lens, uint8_t* __restrict__ abort_out) {
     const int b = blockIdx.x;
+    const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride;
+    const uint32_t* ex_row = expected_tags + static_cast<size_t>(b) * bt_stride;
+    int32_t page[kVerifyUnroll];
+    uint32_t want[kVerifyUnroll];
+    if (bt_stride > 0) {
+#pragma unroll
+        for (int u = 0; u < kVerifyUnroll; ++u) {
+            const int j = min(u * kVerifyThreads + static_cast<int>(threadIdx.x), bt_stride - 1);
+            page[u] = bt_row[j];
+            want[u] = ex_row[j];
+        }
+    }
     const int L = seq_lens[b];
     int bad = 0;
     int64_t npages = 0;
@@ -44,22 +58,21 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_tags_kernel(
         if (npages > 0 && num_pages <= 0) bad = 1;       // no page can be valid (no tags to read)
     }
     if (!bad && npages > 0) {
-        const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride;
-        const uint32_t* ex_row = expected_tags + static_cast<size_t>(b) * bt_stride;
         for (int64_t base = 0; base < npages; base += kVerifyThreads * kVerifyUnroll) {
-            int32_t page[kVerifyUnroll];
-            uint32_t want[kVerifyUnroll];
+            if (base > 0) {
+#pragma unroll
+                for (int u = 0; u < kVerifyUnroll; ++u) {
+                    const int64_t j = min(base + u * kVerifyThreads + threadIdx.x, npages - 1);
+                    page[u] = bt_row[j];
+                    want[u] = ex_row[j];
+                }
+            }
             uint32_t have[kVerifyUnroll];
 #pragma unroll
             for (int u = 0; u < kVerifyUnroll; ++u) {
-                const int64_t j = min(base + u * kVerifyThreads + threadIdx.x, npages - 1);
-                page[u] = bt_row[j];
-                want[u] = ex_row[j];
-            }
-#pragma unroll
-            for (int u = 0; u < kVerifyUnroll; ++u) {
+                const int64_t j = base + u * kVerifyThreads + threadIdx.x;
                 const int32_t p = page[u];
-                have[u] = pool_tags[(p >= 0 && p < num_pages) ? p : 0];
+                have[u] = pool_tags[(j < npages && p >= 0 && p < num_pages) ? p : 0];
             }
 #pragma unroll
             for (int u = 0; u < kVerifyUnroll; ++u) {
@@ -74,13 +87,105 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_tags_kernel(
     if (threadIdx.x == 0) abort_out[b] = bad ? 1 : 0;
 }
 
+// ---------------------------------------------------------------------------
+// Split tag check: workgroup (b, c) of 256 threads checks pages
+// [c * 2048, (c + 1) * 2048) of request b's row, 8 per thread, all loads of a
+// thread in flight together as above. A row of n chunks (n = 1 for a refused
+// request; workgroups past a row's n exit at once) with n == 1 writes its
+// flag directly. Otherwise each of the n workgroups adds 1 to the request's
+// 64-bit counter, plus 2^32 if it found a mismatch, with one relaxed device-
+// scope atomic; the workgroup that brings the count to n writes the flag from
+// the sum it read and stores 0 back, so the counters start every call at zero
+// and the flag is still overwritten, never accumulated. The verdict travels
+// inside the atomic, so no other memory has to become visible.
+// ---------------------------------------------------------------------------
+constexpr int kVerifySplitThreads = 256;
+constexpr int kVerifySplitUnroll = kVerifyChunkPages / kVerifySplitThreads;
+static_assert(kVerifySplitUnroll * kVerifySplitThreads == kVerifyChunkPages, "chunk shape");
+
+__global__ __launch_bounds__(kVerifySplitThreads) void verify_tags_split_kernel(
+    const uint32_t* __restrict__ pool_tags, int32_t num_pages,
+    const int32_t* __restrict__ block_table, const uint32_t* __restrict__ expected_tags,
+    int32_t bt_stride, const int32_t* __restrict__ seq_lens, uint8_t* __restrict__ abort_out,
+    uint64_t* __restrict__ counters, int32_t chunks_per_row) {
+    const int b = static_cast<int>(blockIdx.x / static_cast<uint32_t>(chunks_per_row));
+    const int c = static_cast<int>(blockIdx.x % static_cast<uint32_t>(chunks_per_row));
+    const int64_t j0 = static_cast<int64_t>(c) * kVerifyChunkPages + threadIdx.x;
+    const int32_t* bt_row = block_table + static_cast<size_t>(b) * bt_stride;
+    const uint32_t* ex_row = expected_tags + static_cast<size_t>(b) * bt_stride;
+    // this chunk's table entries, clamped into the row, go out with the length
+    int32_t page[kVerifySplitUnroll];
+    uint32_t want[kVerifySplitUnroll];
+    if (bt_stride > 0) {
+#pragma unroll
+        for (int u = 0; u < kVerifySplitUnroll; ++u) {
+            const int64_t j = min(j0 + u * kVerifySplitThreads, static_cast<int64_t>(bt_stride) - 1);
+            page[u] = bt_row[j];
+            want[u] = ex_row[j];
+        }
+    }
+    const int L = seq_lens[b];
+    int bad = 0;
+    int64_t npages = 0;
+    if (L < 0) {
+        bad = 1;
+    } else {
+        npages = (static_cast<int64_t>(L) + kPage - 1) / kPage;
+        if (npages > bt_stride) bad = 1;
+        if (npages > 0 && num_pages <= 0) bad = 1;
+    }
+    const int64_t n_chunks =
+        bad ? 1 : max(int64_t{1}, (npages + kVerifyChunkPages - 1) / kVerifyChunkPages);
+    if (c >= n_chunks) return;                                // uniform per workgroup
+    if (!bad) {
+        uint32_t have[kVerifySplitUnroll];
+#pragma unroll
+        for (int u = 0; u < kVerifySplitUnroll; ++u) {
+            const int64_t j = j0 + u * kVerifySplitThreads;
+            const int32_t p = page[u];
+            have[u] = pool_tags[(j < npages && p >= 0 && p < num_pages) ? p : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kVerifySplitUnroll; ++u) {
+            const int64_t j = j0 + u * kVerifySplitThreads;
+            const int32_t p = page[u];
+            const bool wrong = p < 0 || p >= num_pages || have[u] != want[u];
+            bad |= (j < npages && wrong) ? 1 : 0;
+        }
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x != 0) return;
+    if (n_chunks == 1) {
+        abort_out[b] = bad ? 1 : 0;
+        return;
+    }
+    const uint64_t add = 1u + (bad ? (uint64_t{1} << 32) : 0u);
+    const uint64_t old = __hip_atomic_fetch_add(counters + b, add, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (static_cast<int64_t>(old & 0xFFFFFFFFu) + 1 == n_chunks) {
+        abort_out[b] = ((old >> 32) != 0 || bad) ? 1 : 0;
+        __hip_atomic_store(counters + b, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 hipError_t launch_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
                               const int32_t* block_table, const uint32_t* expected_tags,
                               int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
-                              uint8_t* abort_out, hipStream_t stream) {
-    hipLaunchKernelGGL(verify_tags_kernel, dim3(batch), dim3(kVerifyThreads), 0, stream,
-                       pool_tags, num_pages, block_table, expected_tags, bt_stride, seq_lens,
-                       abort_out);
+                              uint8_t* abort_out, uint64_t* counters, hipStream_t stream) {
+    const int64_t chunks = bt_stride <= kVerifyChunkPages
+                               ? 1
+                               : (static_cast<int64_t>(bt_stride) + kVerifyChunkPages - 1) /
+                                     kVerifyChunkPages;
+    if (chunks == 1 || counters != nullptr) {
+        hipLaunchKernelGGL(verify_tags_split_kernel,
+                           dim3(static_cast<uint32_t>(batch * chunks)), dim3(kVerifySplitThreads),
+                           0, stream, pool_tags, num_pages, block_table, expected_tags, bt_stride,
+                           seq_lens, abort_out, counters, static_cast<int32_t>(chunks));
+    } else {
+        hipLaunchKernelGGL(verify_tags_kernel, dim3(batch), dim3(kVerifyThreads), 0, stream,
+                           pool_tags, num_pages, block_table, expected_tags, bt_stride, seq_lens,
+                           abort_out);
+    }
     return hipGetLastError();
 }
 

@@ -8,10 +8,15 @@
 
 namespace kvfp8 {
 
+// Pages of a request's row that one workgroup of the split tag check covers.
+constexpr int kVerifyChunkPages = 2048;
+
+// counters: nullptr (one workgroup per whole row), or batch zero-filled 64-bit
+// words (rows split into chunks of kVerifyChunkPages pages, one workgroup each).
 hipError_t launch_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
                               const int32_t* block_table, const uint32_t* expected_tags,
                               int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
-                              uint8_t* abort_out, hipStream_t stream);
+                              uint8_t* abort_out, uint64_t* counters, hipStream_t stream);
 
 hipError_t launch_append(bool fp8, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok,

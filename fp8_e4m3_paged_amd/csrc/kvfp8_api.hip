@@ -220,21 +220,37 @@ const char* kv_status_str(int status) {
     }
 }
 
+static_assert(kvfp8::kVerifyChunkPages == KV_VERIFY_CHUNK_PAGES, "tag-check chunk");
+
+size_t kv_verify_tags_workspace_bytes(int32_t batch, int32_t bt_stride) {
+    if (batch <= 0 || bt_stride <= KV_VERIFY_CHUNK_PAGES) return 0;
+    return static_cast<size_t>(batch) * sizeof(uint64_t);     // one counter per request
+}
+
 int kv_verify_tags(const uint32_t* pool_tags, int32_t num_pages, const int32_t* block_table,
                    const uint32_t* expected_tags, int32_t bt_stride, const int32_t* seq_lens,
-                   int32_t batch, int32_t page_size, uint8_t* abort_out, void* stream) {
+                   int32_t batch, int32_t page_size, uint8_t* abort_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
     if (batch < 0 || num_pages < 0 || bt_stride < 0) return KV_ERR_SHAPE;
     if (page_size != KV_PAGE_SIZE) return KV_ERR_UNSUPPORTED;
     if (!grid_fits(batch, 1024)) return KV_ERR_SHAPE;     // one 1024-thread workgroup per request
+    const int64_t chunks =
+        bt_stride <= KV_VERIFY_CHUNK_PAGES
+            ? 1
+            : (static_cast<int64_t>(bt_stride) + KV_VERIFY_CHUNK_PAGES - 1) / KV_VERIFY_CHUNK_PAGES;
+    const bool split = chunks > 1 && workspace != nullptr;
+    if (split && !grid_fits(static_cast<int64_t>(batch) * chunks, 256)) return KV_ERR_SHAPE;
     if (batch == 0) return KV_OK;
     if (!block_table || !expected_tags || !seq_lens || !abort_out) return KV_ERR_NULL;
     if (!pool_tags && num_pages > 0) return KV_ERR_NULL;
+    if (split && workspace_bytes < kv_verify_tags_workspace_bytes(batch, bt_stride))
+        return KV_ERR_WORKSPACE;
     if (misaligned(pool_tags, 4) || misaligned(block_table, 4) || misaligned(expected_tags, 4) ||
-        misaligned(seq_lens, 4))
+        misaligned(seq_lens, 4) || (split && misaligned(workspace, 8)))
         return KV_ERR_ALIGN;
-    return launch_status(kvfp8::launch_verify_tags(pool_tags, num_pages, block_table,
-                                                   expected_tags, bt_stride, seq_lens, batch,
-                                                   abort_out, static_cast<hipStream_t>(stream)));
+    return launch_status(kvfp8::launch_verify_tags(
+        pool_tags, num_pages, block_table, expected_tags, bt_stride, seq_lens, batch, abort_out,
+        split ? static_cast<uint64_t*>(workspace) : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int kv_append_quant(const void* k_new, const void* v_new, const int32_t* tok_seq,

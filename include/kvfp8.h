@@ -113,7 +113,11 @@ typedef enum { KV_CACHE_FP8_E4M3 = 0, KV_CACHE_BF16 = 1 } kv_cache_dtype;
 #define KV_MAX_PARTITIONS 8192        /* ceil(max_seq_len / partition_tokens) */
 
 /*
- * Batched page-tag check (the separate batch operation the pages describe).
+ * Batched page-tag check: the separate batch operation that compares each
+ * request's recorded (page, tag) pairs with the pool before supported decode
+ * operations read, and aborts only the mismatching request (remio.ai/it,
+ * sections "Cosa ha cambiato Cloudflare per Kimi e GLM" and "La sicurezza
+ * della cache KV condivisa diventa una questione di produzione").
  *
  * For every request b < batch writes abort_out[b] = 1 if
  *   seq_lens[b] < 0, or ceil(seq_lens[b]/page_size) > bt_stride, or
@@ -126,18 +130,30 @@ typedef enum { KV_CACHE_FP8_E4M3 = 0, KV_CACHE_BF16 = 1 } kv_cache_dtype;
  *
  * pool_tags [num_pages], block_table/expected_tags [batch][bt_stride],
  * seq_lens [batch]: read. abort_out uint8 [batch]: written.
+ * workspace: optional device memory of kv_verify_tags_workspace_bytes(batch,
+ * bt_stride) bytes, zero-filled before its first use; every call leaves it
+ * zeroed again. With it, rows of more than KV_VERIFY_CHUNK_PAGES pages are
+ * checked by several workgroups whose verdicts the last one combines; with
+ * NULL (or when that size is 0) one workgroup checks each whole row. Calls
+ * that overlap in time must not share a workspace.
  * Errors: KV_ERR_NULL (any pointer NULL while batch > 0), KV_ERR_SHAPE
- * (batch, num_pages or bt_stride negative, or batch > 4,194,303: one
- * 1024-thread workgroup per request), KV_ERR_UNSUPPORTED (page_size != 16),
- * KV_ERR_ALIGN. batch == 0 enqueues nothing.
+ * (batch, num_pages or bt_stride negative, or batch > 4,194,303; with a
+ * workspace, batch x ceil(bt_stride / KV_VERIFY_CHUNK_PAGES) > 16,777,215),
+ * KV_ERR_UNSUPPORTED (page_size != 16), KV_ERR_WORKSPACE (workspace_bytes
+ * below the size above), KV_ERR_ALIGN. batch == 0 enqueues nothing.
  */
+#define KV_VERIFY_CHUNK_PAGES 2048
+size_t kv_verify_tags_workspace_bytes(int32_t batch, int32_t bt_stride);
 int kv_verify_tags(const uint32_t* pool_tags, int32_t num_pages,
                    const int32_t* block_table, const uint32_t* expected_tags,
                    int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
-                   int32_t page_size, uint8_t* abort_out, void* stream);
+                   int32_t page_size, uint8_t* abort_out, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
- * Quantize-on-append into an FP8 e4m3 pool (the FP8 cache write).
+ * Quantize-on-append into an FP8 e4m3 pool: the cache holds e4m3 codes
+ * instead of BF16 values (remio.ai/it, section "Cosa ha cambiato Cloudflare
+ * per Kimi e GLM"), written through one fp32 scale per (layer, KV head).
  *
  * For each new token n < n_tok, request b = tok_seq[n], position t =
  * tok_pos[n]: if 0 <= b < batch, abort (if non-NULL) has abort[b] == 0,
@@ -206,7 +222,9 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                          int32_t cache_dtype);
 
 /*
- * Decode-step attention over the paged cache, dequantizing on read.
+ * Decode-step attention over the paged cache, dequantizing on read: the
+ * kernel converts the cached codes as it reads them (remio.ai/it, section
+ * "Perché le cache più piccole di Cloudflare battono la velocità pura").
  *
  * For each request b with abort[b] == 0 (or abort == NULL) and
  * 1 <= L = seq_lens[b] <= max_seq_len whose pages j < ceil(L/16) are all

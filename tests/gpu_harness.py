@@ -35,6 +35,12 @@ def workspace(wl, partition_tokens: int, max_seq_len=None):
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV) if n else None
 
 
+def verify_workspace(st: DeviceState):
+    """Zeroed counters for the split tag check, or None when every row fits one chunk."""
+    n = kv.kv_verify_tags_workspace_bytes(st.wl.batch, st.block_table.shape[1])
+    return torch.zeros(n, dtype=torch.uint8, device=DEV) if n else None
+
+
 def gpu_step(st: DeviceState, step: int, verify: bool = True, partition_tokens: int = 0,
              sm_scale=None, layers=None, max_seq_len=None, fused: bool = False):
     """One decode step on the GPU (separate append + attention calls, or the
@@ -49,7 +55,8 @@ def gpu_step(st: DeviceState, step: int, verify: bool = True, partition_tokens: 
     ws = workspace(wl, partition_tokens, msl)
     abort = None
     if verify:
-        kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens, st.abort)
+        kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens, st.abort,
+                          workspace=verify_workspace(st))
         abort = st.abort
     outs, inputs = {}, {}
     for layer in layers:

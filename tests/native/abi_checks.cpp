@@ -35,16 +35,31 @@ int main() {
 
     // tag check
     expect("verify page_size", kv_verify_tags(P<uint32_t>(), 10, P<int32_t>(), P<uint32_t>(), 4,
-                                              P<int32_t>(), 2, 8, P<uint8_t>(), nullptr),
+                                              P<int32_t>(), 2, 8, P<uint8_t>(), nullptr, 0,
+                                              nullptr),
            KV_ERR_UNSUPPORTED);
     for (int32_t b : big)
         if (b > 4194303 || b < 0)
             expect("verify batch", kv_verify_tags(P<uint32_t>(), 10, P<int32_t>(), P<uint32_t>(), 4,
-                                                  P<int32_t>(), b, 16, P<uint8_t>(), nullptr),
+                                                  P<int32_t>(), b, 16, P<uint8_t>(), nullptr, 0,
+                                                  nullptr),
                    KV_ERR_SHAPE);
     expect("verify null", kv_verify_tags(P<uint32_t>(), 10, nullptr, P<uint32_t>(), 4,
-                                         P<int32_t>(), 2, 16, P<uint8_t>(), nullptr),
+                                         P<int32_t>(), 2, 16, P<uint8_t>(), nullptr, 0, nullptr),
            KV_ERR_NULL);
+    // the split check: its workgroup count at the extremes, and a short workspace
+    for (int32_t b : {1, 2, 4096, 4194303})
+        for (int32_t w : big)
+            if (w > 0) {    // every such row is split, so the empty workspace is refused
+                const int st = kv_verify_tags(P<uint32_t>(), 10, P<int32_t>(), P<uint32_t>(), w,
+                                              P<int32_t>(), b, 16, P<uint8_t>(), A, 0, nullptr);
+                if (st != KV_ERR_SHAPE && st != KV_ERR_WORKSPACE)
+                    expect("verify split sizes", st, KV_ERR_SHAPE);
+                (void)kv_verify_tags_workspace_bytes(b, w);
+            }
+    expect("verify workspace", kv_verify_tags(P<uint32_t>(), 10, P<int32_t>(), P<uint32_t>(), 5000,
+                                              P<int32_t>(), 4, 16, P<uint8_t>(), A, 24, nullptr),
+           KV_ERR_WORKSPACE);
 
     // append
     for (int32_t n : big)

@@ -103,7 +103,8 @@ A = 1 << 20        # a fake, 16-byte aligned "device" address (never dereference
 
 def verify(lib, **kw):
     args = dict(pool_tags=A, num_pages=10, block_table=A, expected_tags=A, bt_stride=4,
-                seq_lens=A, batch=2, page_size=16, abort_out=A, stream=None)
+                seq_lens=A, batch=2, page_size=16, abort_out=A, workspace=None,
+                workspace_bytes=0, stream=None)
     args.update(kw)
     return lib.kv_verify_tags(*args.values())
 
@@ -116,6 +117,15 @@ def test_verify_rejects_bad_arguments(lib):
     assert verify(lib, abort_out=None) == NULL
     assert verify(lib, seq_lens=A + 2) == ALIGN
     assert verify(lib, batch=0, block_table=None) == OK       # nothing to do
+    # the split check's counters: one 64-bit word per request, only for rows
+    # longer than one 2,048-page chunk
+    assert lib.kv_verify_tags_workspace_bytes(3, 2048) == 0
+    assert lib.kv_verify_tags_workspace_bytes(3, 2049) == 24
+    assert lib.kv_verify_tags_workspace_bytes(0, 9000) == 0
+    assert verify(lib, bt_stride=5000, workspace=A, workspace_bytes=8) == WORKSPACE
+    assert verify(lib, bt_stride=5000, workspace=A + 4, workspace_bytes=16) == ALIGN
+    assert verify(lib, batch=4_000_000, bt_stride=2_000_000, workspace=A,
+                  workspace_bytes=1 << 40) == SHAPE       # 3.9e9 workgroups
 
 
 def append(lib, fp8=True, **kw):

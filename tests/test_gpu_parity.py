@@ -471,12 +471,16 @@ def test_maximum_partition_count(kv, cache):
     assert np.all(got[0] == 0) and np.all(got[1] == 0) and np.all(got[2] == 0)
 
 
-def test_verify_tags_long_rows(kv):
+@pytest.mark.parametrize("split", [False, True])
+def test_verify_tags_long_rows(kv, split):
     """Rows of up to 5,000 pages (80k tokens), more than one sweep of the
-    workgroup's 1,024 threads: a failing page anywhere (first, middle, last,
+    whole-row workgroup's 1,024 threads, or (split) three 2,048-page chunks
+    checked by three workgroups that combine through the counter workspace: a
+    failing page anywhere (first, middle, last, either side of a chunk edge,
     the one page of a last sweep) aborts exactly its request, pages past a
     request's length are ignored, and flags that held 1 or junk before the
-    call are overwritten with the oracle's 0 / 1."""
+    call are overwritten with the oracle's 0 / 1. The counters are back at
+    zero after every call."""
     rng = np.random.default_rng(23)
     num_pages, batch, width = 50_000, 12, 5_000
     tags = rng.integers(0, 2 ** 32, num_pages, dtype=np.uint64).astype(np.uint32)
@@ -491,17 +495,25 @@ def test_verify_tags_long_rows(kv):
     bt[4, 1_024] = num_pages           # a page id just outside the pool
     bt[8, 3_000] = -1                  # past request 8's pages: ignored
     exp[9, 2_048] ^= 1                 # likewise
+    exp[10, 2_047] ^= 1                # the last page of a first chunk
     bt[11, 1_499] = -7                 # last page of a 1500-page request
     want = paged.verify_tags(tags, bt, exp, lens, 16)
-    assert want.tolist() == [1, 1, 1, 1, 1, 0, 1, 1, 0, 0, 0, 1]
+    assert want.tolist() == [1, 1, 1, 1, 1, 0, 1, 1, 0, 0, 1, 1]
+    ws = None
+    if split:
+        n = kv.kv_verify_tags_workspace_bytes(batch, width)
+        assert n == 8 * batch
+        ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
     for fill in (0, 1, 0xA5):
         ab = torch.full((batch,), fill, dtype=torch.uint8, device=DEV)
         kv.kv_verify_tags(torch.from_numpy(tags.view(np.int32)).to(DEV),
                           torch.from_numpy(bt).to(DEV),
                           torch.from_numpy(exp.view(np.int32)).to(DEV),
-                          torch.from_numpy(lens).to(DEV), ab)
+                          torch.from_numpy(lens).to(DEV), ab, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(ab.cpu().numpy(), want), (fill, ab.cpu().numpy(), want)
+        if split:
+            assert int(ws.count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
