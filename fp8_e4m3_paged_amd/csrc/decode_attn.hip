@@ -604,9 +604,7 @@ __device__ __forceinline__ void merge_waves(float* sm, int wave, int lane, int g
 // meanwhile), and a ballot of the nonzero weights lists the slots to read,
 // whose outputs (two dims per lane, 512 B per slot) are loaded up to 8 at a
 // time before any is accumulated. Empty slots (weight 0) are never read.
-// The shared attention kernel runs this itself in the workgroup that
-// completes a (request, KV head); reduce_partials_kernel runs it for the
-// persistent kernel's partials.
+// Rows of at most kShortRow slots take a single round trip instead.
 constexpr int kReduceWaves = 4;
 constexpr int kReduceBatch = 8;             // slot outputs in flight per wavefront (16 requests
                                             // up to 131k tokens: 7.3 us; 4: 8.3, 16: 7.9, 32: 10.9)
@@ -625,34 +623,9 @@ constexpr f32x2 kEmptySlot = {-INFINITY, 0.f};
 // Rows of at most this many slots are combined in one round trip.
 constexpr int kShortRow = 16;
 
-// Partials exchanged between the workgroups of one launch are written and
-// read with agent-scope atomic accesses: the stores write through to the
-// point where every XCD's L2 sees them and the loads fetch from there, so
-// no cache-wide writeback or invalidate (what a device-scope fence costs on
-// this chip) is needed around the counter that publishes them.
-__device__ __forceinline__ void store_shared_f32x2(float* p, f32x2 v) {
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_shared_f32x4(float* p, const f32x4& v) {
-    store_shared_f32x2(p, f32x2{v[0], v[1]});
-    store_shared_f32x2(p + 2, f32x2{v[2], v[3]});
-}
-template <bool SHARED>
-__device__ __forceinline__ f32x2 load_f32x2(const f32x2* p) {
-    if constexpr (SHARED) {
-        return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
-                                                           __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
-    } else {
-        return *p;
-    }
-}
-
 // First pass over this wavefront's slots c0 + lane, c0 + lane + cstep, ...
 // (< np) of one row's (max, sum) pairs: the lane's maximum and whether any
 // slot carries the invalid-page mark. Four loads in flight per lane.
-template <bool SHARED>
 __device__ __forceinline__ void row_slot_max(const f32x2* __restrict__ ml, int np, int c0, int cstep,
                                              int lane, float& mx, bool& bad) {
     mx = -INFINITY;
@@ -661,7 +634,7 @@ __device__ __forceinline__ void row_slot_max(const f32x2* __restrict__ ml, int n
         f32x2 e[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            e[k] = i0 + cstep * k < np ? load_f32x2<SHARED>(ml + i0 + cstep * k) : kEmptySlot;
+            e[k] = i0 + cstep * k < np ? ml[i0 + cstep * k] : kEmptySlot;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             bad |= e[k][1] < 0.f;
@@ -673,17 +646,16 @@ __device__ __forceinline__ void row_slot_max(const f32x2* __restrict__ ml, int n
 // Second pass over the 64-slot chunks c0, c0 + cstep, ... (< np): the lane's
 // share of sum_p w_p l_p and its two dims of sum_p w_p acc_p, with
 // w_p = 2^(m_p - M_use). acc points at the row's outputs plus 2 * lane.
-template <bool SHARED>
 __device__ __forceinline__ void row_slot_accumulate(const f32x2* __restrict__ ml,
                                                     const float* __restrict__ acc, int np, int c0,
                                                     int cstep, int lane, float M_use, float& lsum,
                                                     f32x2& num) {
     lsum = 0.f;
     num = f32x2{0.f, 0.f};
-    f32x2 e_next = c0 + lane < np ? load_f32x2<SHARED>(ml + c0 + lane) : kEmptySlot;
+    f32x2 e_next = c0 + lane < np ? ml[c0 + lane] : kEmptySlot;
     for (int c = c0; c < np; c += cstep) {
         const f32x2 e = e_next;                               // the next chunk's pairs load
-        e_next = c + cstep + lane < np ? load_f32x2<SHARED>(ml + c + cstep + lane)
+        e_next = c + cstep + lane < np ? ml[c + cstep + lane]
                                        : kEmptySlot;          // under this one's reads
         const float w = exp2f(e[0] - M_use);                  // 0 for an empty slot
         lsum += w * e[1];
@@ -696,8 +668,8 @@ __device__ __forceinline__ void row_slot_accumulate(const f32x2* __restrict__ ml
                 sl[k] = mask != 0 ? __builtin_ctzll(mask) : -1;    // wave-uniform
                 mask &= mask - 1;
                 if (sl[k] >= 0)
-                    v[k] = load_f32x2<SHARED>(reinterpret_cast<const f32x2*>(
-                        acc + static_cast<size_t>(c + sl[k]) * kDim));
+                    v[k] = *reinterpret_cast<const f32x2*>(
+                        acc + static_cast<size_t>(c + sl[k]) * kDim);
             }
 #pragma unroll
             for (int k = 0; k < kReduceBatch; ++k) {
@@ -709,21 +681,19 @@ __device__ __forceinline__ void row_slot_accumulate(const f32x2* __restrict__ ml
 }
 
 // One wavefront reduces one whole row (slots [0, np)) and writes its two
-// dims per lane of the output o (already offset by the lane). SHARED: the
-// partials were written by other workgroups of the same launch.
-template <bool SHARED>
+// dims per lane of the output o (already offset by the lane).
 __device__ __forceinline__ void reduce_row_wave(const f32x2* __restrict__ ml,
                                                 const float* __restrict__ acc, int np, float vs,
                                                 f32x2* o, int lane) {
     if (np <= kShortRow) {
         // one round trip: every (max, sum) pair and every slot's two dims
         // are requested before any is used
-        const f32x2 e = lane < np ? load_f32x2<SHARED>(ml + lane) : kEmptySlot;
+        const f32x2 e = lane < np ? ml[lane] : kEmptySlot;
         f32x2 v[kShortRow];
 #pragma unroll
         for (int k = 0; k < kShortRow; ++k)              // slots past np re-read the last one
-            v[k] = load_f32x2<SHARED>(reinterpret_cast<const f32x2*>(
-                acc + static_cast<size_t>(min(k, np - 1)) * kDim));
+            v[k] = *reinterpret_cast<const f32x2*>(
+                acc + static_cast<size_t>(min(k, np - 1)) * kDim);
         if (__builtin_amdgcn_ballot_w64(e[1] < 0.f) != 0) {  // an invalid-page mark
             *o = f32x2{0.f, 0.f};
             return;
@@ -742,7 +712,7 @@ __device__ __forceinline__ void reduce_row_wave(const f32x2* __restrict__ ml,
     }
     float mx;
     bool bad;
-    row_slot_max<SHARED>(ml, np, 0, 64, lane, mx, bad);
+    row_slot_max(ml, np, 0, 64, lane, mx, bad);
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {              // uniform per row
         *o = f32x2{0.f, 0.f};
         return;
@@ -750,7 +720,7 @@ __device__ __forceinline__ void reduce_row_wave(const f32x2* __restrict__ ml,
     const float M = wave_max(mx);
     float lsum;
     f32x2 num;
-    row_slot_accumulate<SHARED>(ml, acc, np, 0, 64, lane, M == -INFINITY ? 0.f : M, lsum, num);
+    row_slot_accumulate(ml, acc, np, 0, 64, lane, M == -INFINITY ? 0.f : M, lsum, num);
     const float lt = wave_sum(lsum);
     *o = lt > 0.f ? num * (vs / lt) : f32x2{0.f, 0.f};
 }
@@ -760,16 +730,16 @@ __device__ __forceinline__ void reduce_row_wave(const f32x2* __restrict__ ml,
 // w + NW, ...) and merge in LDS. NW = 4, or 8 when the grid has at most one
 // workgroup per CU (e.g. 32 requests x 8 KV heads), so each CU still streams
 // with 8 wavefronts and no split-K reduction is needed.
-// With several partitions each workgroup writes its partial, then counts it
-// on the (b, g)'s counter; the workgroup whose increment completes the count
-// combines the (b, g)'s partials itself, one wavefront per query head, and
-// sets the counter back to zero, so no second launch is needed. The counters
-// start at zero (a zero-filled workspace) and every call leaves them at zero.
+// With several partitions each workgroup writes its partial (m, l, acc) and
+// reduce_partials_kernel, launched next, combines them. (Combining them in
+// the last workgroup of each (b, g) of the same launch, behind device-scope
+// stores and a counter, measured 1-3% slower at 1 to 16 requests.)
 // Occupancy is pinned at 2 waves per SIMD: the register pipeline needs ~200
 // VGPRs, and without the cap the scheduler may trade the in-flight loads for a
 // third wave (sinking the prefetches next to their uses), which halves the
-// streaming rate.
-template <bool FP8, int NW, bool APPEND>
+// streaming rate. SPLIT: more than one partition (partials written); the
+// one-partition instance writes the output and carries no partial code.
+template <bool FP8, int NW, bool APPEND, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_partition_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
@@ -778,10 +748,9 @@ void attn_partition_kernel(
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const uint8_t* __restrict__ abort,
     float* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_acc,
-    uint32_t* __restrict__ counters, float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv,
-    int32_t num_pages, int32_t part_tokens, int32_t n_parts) {
+    float sm_scale_log2, int32_t batch, int32_t hq, int32_t hkv, int32_t num_pages,
+    int32_t part_tokens, int32_t n_parts) {
     extern __shared__ float smem[];
-    __shared__ int sm_last;
     constexpr int kThreads = NW * 64;
     const int group = hq / hkv;
     // LDS: the merge area, then the page ids of the partition
@@ -862,39 +831,16 @@ void attn_partition_kernel(
     const float vs = (FP8 && v_scale != nullptr) ? v_scale[g] : 1.0f;
     merge_waves<NW>(smem, wave, lane, group, m_run, l_tot, acc_o,
                     [&](int qh, int d, float M, float lt, const f32x4& o) {
-        if (n_parts == 1) {
+        if constexpr (!SPLIT) {
             f32x4 r = {0.f, 0.f, 0.f, 0.f};
             if (!bad && lt > 0.f) r = o * (vs / lt);
             *reinterpret_cast<f32x4*>(out + (q_row + qh) * kDim + d) = r;
         } else {
             const size_t pslot = (q_row + qh) * partial_slots(n_parts) + p;
-            store_shared_f32x4(part_acc + pslot * kDim + d, o);
-            if (d == 0) store_shared_f32x2(part_ml + 2 * pslot, f32x2{M, bad ? -1.f : lt});
+            *reinterpret_cast<f32x4*>(part_acc + pslot * kDim + d) = o;
+            if (d == 0) *reinterpret_cast<f32x2*>(part_ml + 2 * pslot) = f32x2{M, bad ? -1.f : lt};
         }
     });
-    if (n_parts == 1) return;
-
-    // ---- count this partition; the last one of (b, g) combines them ------
-    __builtin_amdgcn_s_waitcnt(0);    // this workgroup's partial stores have completed
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t np_b = static_cast<uint32_t>((L + part_tokens - 1) / part_tokens);
-        sm_last = __hip_atomic_fetch_add(counters + static_cast<size_t>(b) * hkv + g, 1u,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np_b - 1;
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    if (tid == 0)                     // ready for the next call
-        __hip_atomic_store(counters + static_cast<size_t>(b) * hkv + g, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    const int np_b = (L + part_tokens - 1) / part_tokens;
-    const int64_t n_slots = partial_slots(n_parts);
-    for (int qh = wave; qh < group; qh += NW) {
-        const size_t row = q_row + qh;
-        reduce_row_wave<true>(reinterpret_cast<const f32x2*>(part_ml) + row * n_slots,
-                        part_acc + row * n_slots * kDim + 2 * lane, np_b, vs,
-                        reinterpret_cast<f32x2*>(out + row * kDim) + lane, lane);
-    }
 }
 
 // Persistent kernel for short partitions (<= 2048 tokens), used when there
@@ -953,7 +899,7 @@ void attn_wave_kernel(
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table, int32_t bt_stride,
     const int32_t* __restrict__ seq_lens, int32_t max_seq_len, const uint8_t* __restrict__ abort,
     float* __restrict__ out, float* __restrict__ part_ml, float* __restrict__ part_acc,
-    uint32_t* __restrict__ /*counters*/, float sm_scale_log2, int32_t batch, int32_t hq,
+    float sm_scale_log2, int32_t batch, int32_t hq,
     int32_t hkv, int32_t num_pages, int32_t part_tokens, int32_t n_parts) {
     constexpr int kThreads = kWaves * 64;
     extern __shared__ float smem[];
@@ -1145,13 +1091,13 @@ __global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
     const float* acc = part_acc + bh * n_slots * kDim + 2 * lane;
     const float vs = v_scale != nullptr ? v_scale[h / (hq / hkv)] : 1.0f;
     if constexpr (!COOP) {
-        reduce_row_wave<false>(ml, acc, np, vs, o, lane);
+        reduce_row_wave(ml, acc, np, vs, o, lane);
     } else {
         // this wavefront's 64-slot chunks: 64 wave, 64 wave + 256, ...
         constexpr int cstep = 64 * kReduceWaves;
         float mx;
         bool bad;
-        row_slot_max<false>(ml, np, 64 * wave, cstep, lane, mx, bad);
+        row_slot_max(ml, np, 64 * wave, cstep, lane, mx, bad);
         const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
         float M = wave_max(mx);
         if (lane == 0) {
@@ -1170,8 +1116,8 @@ __global__ __launch_bounds__(kReduceWaves * 64) void reduce_partials_kernel(
         }
         float lsum;
         f32x2 num;
-        row_slot_accumulate<false>(ml, acc, np, 64 * wave, cstep, lane,
-                                   M == -INFINITY ? 0.f : M, lsum, num);
+        row_slot_accumulate(ml, acc, np, 64 * wave, cstep, lane, M == -INFINITY ? 0.f : M, lsum,
+                            num);
         sm_num[wave][lane] = num;
         const float ls = wave_sum(lsum);
         if (lane == 0) sm_sum[wave] = ls;
@@ -1221,7 +1167,7 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
 #define KVFP8_ARGS                                                                               \
     a.q, a.k_new, a.v_new, static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool),    \
         fp8 ? a.k_scale : nullptr, fp8 ? a.v_scale : nullptr, a.block_table, a.bt_stride,        \
-        a.seq_lens, a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, a.counters, sm_log2,   \
+        a.seq_lens, a.max_seq_len, a.abort, a.out, a.part_ml, a.part_acc, sm_log2,              \
         a.batch, a.num_q_heads, a.num_kv_heads, a.num_pages, a.partition_tokens, a.num_partitions
     if (use_wave_partitions(a)) {
         // persistent: at most 2 workgroups per CU, each streams its range of pages
@@ -1242,13 +1188,19 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
         const size_t lds = sizeof(float) * merge_floats(nw, group) +
                            sizeof(int32_t) * static_cast<size_t>(a.partition_tokens / kPage);
         const dim3 grid(static_cast<uint32_t>(a.num_partitions * items));
-#define KVFP8_SHARED(F8, NW, AP)                                                                 \
-    hipLaunchKernelGGL((attn_partition_kernel<F8, NW, AP>), grid, dim3(NW * 64), lds, stream,   \
-                       KVFP8_ARGS)
+        const bool split = a.num_partitions > 1;
+#define KVFP8_SHARED(F8, NW, AP, MD)                                                             \
+    hipLaunchKernelGGL((attn_partition_kernel<F8, NW, AP, MD>), grid, dim3(NW * 64), lds,       \
+                       stream, KVFP8_ARGS)
+#define KVFP8_SHARED1(F8, NW, AP)                                 \
+    do {                                                          \
+        if (split) KVFP8_SHARED(F8, NW, AP, true);                \
+        else KVFP8_SHARED(F8, NW, AP, false);                     \
+    } while (0)
 #define KVFP8_SHARED2(F8, NW)                                     \
     do {                                                          \
-        if (append) KVFP8_SHARED(F8, NW, true);                   \
-        else KVFP8_SHARED(F8, NW, false);                         \
+        if (append) KVFP8_SHARED1(F8, NW, true);                  \
+        else KVFP8_SHARED1(F8, NW, false);                        \
     } while (0)
         if (fp8) {
             if (nw == kWavesWide) KVFP8_SHARED2(true, kWavesWide); else KVFP8_SHARED2(true, kWaves);
@@ -1256,15 +1208,16 @@ hipError_t launch_decode_attn(bool fp8, const AttnArgs& a, hipStream_t stream) {
             if (nw == kWavesWide) KVFP8_SHARED2(false, kWavesWide); else KVFP8_SHARED2(false, kWaves);
         }
 #undef KVFP8_SHARED2
+#undef KVFP8_SHARED1
 #undef KVFP8_SHARED
     }
 #undef KVFP8_ARGS
     hipError_t e = hipGetLastError();
-    // the shared kernel combines its own partitions; the persistent one leaves
-    // them to the reduction kernel
-    if (e != hipSuccess || a.num_partitions == 1 || !use_wave_partitions(a)) return e;
+    // with several partitions, either kernel leaves its partials to the reduction
+    const bool wave = use_wave_partitions(a);
+    if (e != hipSuccess || a.num_partitions == 1) return e;
     const int64_t rows = static_cast<int64_t>(a.batch) * a.num_q_heads;
-    const int extra = 1;            // the persistent kernel's slot after the last partition
+    const int extra = wave ? 1 : 0;  // the persistent kernel's slot after the last partition
 #define KVFP8_REDUCE(CO, WGS)                                                                    \
     hipLaunchKernelGGL(reduce_partials_kernel<CO>, dim3(static_cast<uint32_t>(WGS)),             \
                        dim3(kReduceWaves * 64), 0, stream, a.part_ml, a.part_acc, a.seq_lens,    \

@@ -48,7 +48,6 @@ struct AttnArgs {
     int32_t num_partitions;     // ceil(max_seq_len / partition_tokens), >= 1
     float* part_ml;             // [batch][Hq][partial_slots(num_partitions)][2], or null if 1 partition
     float* part_acc;            // [batch][Hq][partial_slots(num_partitions)][128]
-    uint32_t* counters;         // [batch][Hkv] partitions done, zero between calls (null if 1 partition)
 };
 
 // Split-K partial slots per (request, query head): one per partition, plus
@@ -59,23 +58,21 @@ __host__ __device__ constexpr int64_t partial_slots(int64_t num_partitions) {
 }
 
 // Workspace layout of the attention calls with more than one partition:
-// the per-(request, KV head) counters, then the (max, sum) pairs, then the
-// partial outputs, each part starting on a 256-byte boundary.
+// the (max, sum) pairs, then the partial outputs from the next 256-byte
+// boundary.
 struct WorkspaceLayout {
-    size_t counters;            // byte offsets
-    size_t ml;
+    size_t ml;                  // byte offsets
     size_t acc;
     size_t total;
 };
 
-inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,
+inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_q_heads,
                                         int64_t num_partitions) {
     const auto up = [](size_t n) { return (n + 255) / 256 * 256; };
     const size_t slots = static_cast<size_t>(batch) * num_q_heads * partial_slots(num_partitions);
     WorkspaceLayout w{};
-    w.counters = 0;
-    w.ml = up(static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t));
-    w.acc = w.ml + up(slots * 2 * sizeof(float));
+    w.ml = 0;
+    w.acc = up(slots * 2 * sizeof(float));
     w.total = w.acc + slots * 128 * sizeof(float);
     return w;
 }

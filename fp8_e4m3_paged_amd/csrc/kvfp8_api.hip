@@ -49,12 +49,15 @@ int check_append_common(const void* k_new, const void* v_new, const int32_t* tok
 // wavefronts streaming on every compute unit, and into at most 16 partitions
 // (the combine then takes one round trip: at one request of 9,193 tokens the
 // FP8 step went from 0.129 ms with 18 partitions to 0.107 ms with 12).
-// Partitions are equal shares of max_seq_len rounded up to whole page pairs
-// (32 tokens), at most the LDS page list's capacity, and hold at least
-// 192 KiB of K and V per KV head (768 FP8 or 384 BF16 tokens): below that
-// the wavefronts' pipeline start-up dominates. At that one request the FP8
-// step takes 0.107 ms with 12 partitions of 768 tokens and 0.125 ms with 16
-// of 576, while the BF16 step takes 0.143 ms with 16 and 0.168 ms with 12.
+// Partitions are equal shares of max_seq_len rounded up to 256 tokens (the
+// same number of page pairs for each of 8 wavefronts: at 8 requests 2,304
+// tokens ran 3% faster than 2,272), or to one page pair (32 tokens) where the
+// coarser rounding would drop partitions; at most the LDS page list's
+// capacity, and at least 192 KiB of K and V per KV head (768 FP8 or 384 BF16
+// tokens): below that the wavefronts' pipeline start-up dominates. At that
+// one request the FP8 step takes 0.107 ms with 12 partitions of 768 tokens
+// and 0.125 ms with 16 of 576, while the BF16 step takes 0.143 ms with 16
+// and 0.168 ms with 12.
 int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len, bool fp8) {
     const int64_t items = static_cast<int64_t>(batch) * num_kv_heads;
     int64_t parts;
@@ -62,8 +65,10 @@ int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
     else if (items <= 256 && 256 % items == 0) parts = 256 / items;
     else parts = (512 + items - 1) / items;
     if (parts > 16) parts = 16;
-    int64_t tokens = (static_cast<int64_t>(max_seq_len) + parts - 1) / parts;
-    tokens = ((tokens + 31) / 32) * 32;
+    const int64_t share = (static_cast<int64_t>(max_seq_len) + parts - 1) / parts;
+    int64_t tokens = ((share + 255) / 256) * 256;
+    if ((static_cast<int64_t>(max_seq_len) + tokens - 1) / tokens < parts)
+        tokens = ((share + 31) / 32) * 32;
     const int64_t min_tokens = (192 * 1024) / (2 * KV_HEAD_DIM * (fp8 ? 1 : 2));
     if (tokens < min_tokens) tokens = min_tokens;
     if (tokens > KV_MAX_PARTITION_TOKENS) tokens = KV_MAX_PARTITION_TOKENS;
@@ -78,9 +83,9 @@ int32_t auto_partition(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
 // object is loaded) until the process ends. Host code never uses the array's
 // name as an address: the first call on a device asks the runtime for that
 // device's copy (hipGetSymbolAddress, with that device current) and keeps the
-// pointer; kernels receive that pointer. The counters at its start are zero
-// on load and every call leaves them at zero; the rest is overwritten before
-// it is read. Calls that overlap on one GPU share the array and race.
+// pointer; kernels receive that pointer. Every call overwrites the partials
+// it reads, so no call needs the array cleared. Calls that overlap on one GPU
+// share the array and race.
 static __device__ __align__(256) uint8_t scratch[KV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
@@ -191,10 +196,8 @@ static int attn_impl(const void* q, const void* k_new, const void* v_new, int32_
     a.partition_tokens = pt;
     a.num_partitions = parts;
     if (parts > 1) {
-        const kvfp8::WorkspaceLayout w = kvfp8::workspace_layout(batch, num_q_heads, num_kv_heads,
-                                                                 parts);
+        const kvfp8::WorkspaceLayout w = kvfp8::workspace_layout(batch, num_q_heads, parts);
         char* base = static_cast<char*>(workspace);
-        a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
         a.part_ml = reinterpret_cast<float*>(base + w.ml);
         a.part_acc = reinterpret_cast<float*>(base + w.acc);
     }
@@ -312,8 +315,8 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
     if (pt <= 0) return 0;
     const int64_t parts = (static_cast<int64_t>(max_seq_len) + pt - 1) / pt;
     if (parts <= 1) return 0;
-    // [batch][Hkv] counters, [slots][2] (max, sum), then [slots][head_dim] outputs
-    return kvfp8::workspace_layout(batch, num_q_heads, num_kv_heads, parts).total;
+    // [slots][2] (max, sum), then [slots][head_dim] outputs
+    return kvfp8::workspace_layout(batch, num_q_heads, parts).total;
 }
 
 int paged_decode_attn(const void* q, int32_t cache_dtype, const void* k_pool, const void* v_pool,

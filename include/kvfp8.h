@@ -206,15 +206,14 @@ int32_t paged_decode_attn_partition_tokens(int32_t batch, int32_t num_kv_heads,
 
 /*
  * Bytes of device workspace paged_decode_attn needs for these sizes (0 when a
- * single partition covers max_seq_len). The workspace holds one counter per
- * (request, KV head) and the split-K softmax partials (running max,
- * normaliser, unnormalised output), one slot per partition of each (request,
- * query head) plus one more, that the cross-partition reduction combines.
- * Zero-fill it once before its first use: the counters must start at zero,
- * and every call leaves them at zero again (the rest is overwritten before
- * it is read), so one buffer serves any later calls and sizes that fit it.
- * The partition count, and so the size, depends on cache_dtype when
- * partition_tokens is 0. Returns 0 for unsupported arguments.
+ * single partition covers max_seq_len). The workspace holds the split-K
+ * softmax partials (running max, normaliser, unnormalised output), one slot
+ * per partition of each (request, query head) plus one more, that the
+ * cross-partition reduction combines. Every call writes the slots it reads,
+ * so the contents on entry do not matter and one buffer serves any later
+ * calls and sizes that fit it. The partition count, and so the size, depends
+ * on cache_dtype when partition_tokens is 0. Returns 0 for unsupported
+ * arguments.
  */
 size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
@@ -236,17 +235,16 @@ size_t paged_decode_attn_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * and out[b][h][:] = 0 for every other request (aborted, empty, too long,
  * or mapped to an invalid page). The sequence is split into partitions of
  * partition_tokens tokens (0 = automatic); each is reduced with an online
- * softmax, and with more than one partition the partials are merged, by the
- * last workgroup of each (request, KV head) or, for the persistent kernel of
- * short partitions, by a second kernel.
+ * softmax, and with more than one partition a second kernel merges the
+ * partials.
  *
  * sm_scale must be finite and >= 0 (usually 1/sqrt(head_dim)); the scales
  * must be positive and finite.
  * q: bf16 [batch][num_q_heads][head_dim]. out: fp32 [batch][num_q_heads]
  * [head_dim], fully written. k_scale/v_scale: fp32 [num_kv_heads] (may be
  * NULL for the BF16 cache). workspace: device memory of at least
- * paged_decode_attn_workspace_bytes(...) bytes, zero-filled before its first
- * use (may be NULL when that size is 0).
+ * paged_decode_attn_workspace_bytes(...) bytes (may be NULL when that size
+ * is 0).
  * Errors: KV_ERR_NULL, KV_ERR_SHAPE (also when partitions x batch x
  * num_kv_heads exceeds 8,388,607, or, with more than one partition, batch x
  * num_q_heads does), KV_ERR_UNSUPPORTED (also when

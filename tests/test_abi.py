@@ -265,15 +265,14 @@ def test_workspace_and_partition_sizing(real_lib):
     # one partition covers everything: no workspace
     assert k.paged_decode_attn_workspace_bytes(64, 64, 8, 8000, 8192) == 0
     # 16 requests, 64 heads, up to 131073 tokens at 512 -> 257 partitions, and
-    # one more partial slot per (request, query head) for the wave-mode kernel;
-    # after 16 x 8 counters (512 bytes)
+    # one more partial slot per (request, query head) for the wave-mode kernel:
+    # the (max, sum) pairs, then the outputs from the next 256-byte boundary
     n = 16 * 64 * (257 + 1)
     ml = -(-(n * 2 * 4) // 256) * 256
-    assert k.paged_decode_attn_workspace_bytes(16, 64, 8, 131073, 512) == 512 + ml + n * 128 * 4
-    # counters rounded up to 256 bytes: 3 requests x 2 KV heads
+    assert k.paged_decode_attn_workspace_bytes(16, 64, 8, 131073, 512) == ml + n * 128 * 4
     n = 3 * 4 * (3 + 1)
     assert k.paged_decode_attn_workspace_bytes(3, 4, 2, 3 * 1024, 1024) == \
-        256 + -(-(n * 2 * 4) // 256) * 256 + n * 128 * 4
+        -(-(n * 2 * 4) // 256) * 256 + n * 128 * 4
     for cd in (k.KV_CACHE_FP8_E4M3, k.KV_CACHE_BF16):
         for b, h, L in [(64, 8, 9193), (1, 1, 256), (16, 8, 131073), (8, 8, 8192)]:
             pt = k.paged_decode_attn_partition_tokens(b, h, L, 0, cd)
@@ -281,16 +280,19 @@ def test_workspace_and_partition_sizing(real_lib):
         assert k.paged_decode_attn_partition_tokens(64, 8, 9193, 512, cd) == 512
         with pytest.raises(k.KvError):
             k.paged_decode_attn_partition_tokens(64, 8, 9193, 24, cd)
-    # automatic: at most 16 equal shares in whole page pairs, each at least
-    # 192 KiB of K and V per KV head (768 FP8 tokens, 384 BF16 tokens)
+    # automatic: at most 16 equal shares rounded up to 256 tokens (to a page
+    # pair where that would drop partitions), each at least 192 KiB of K and V
+    # per KV head (768 FP8 tokens, 384 BF16 tokens)
     assert k.paged_decode_attn_partition_tokens(1, 8, 9193, 0, k.KV_CACHE_FP8_E4M3) == 768
     assert k.paged_decode_attn_partition_tokens(1, 8, 9193, 0, k.KV_CACHE_BF16) == 576
     assert k.paged_decode_attn_partition_tokens(8, 8, 9193, 0, k.KV_CACHE_BF16) == 2304
+    assert k.paged_decode_attn_partition_tokens(8, 8, 9082, 0, k.KV_CACHE_FP8_E4M3) == 2304
+    assert k.paged_decode_attn_partition_tokens(4, 8, 8797, 0, k.KV_CACHE_FP8_E4M3) == 1120
     assert k.paged_decode_attn_partition_tokens(64, 8, 9193, 0, k.KV_CACHE_FP8_E4M3) == 9216
     # the BF16 size at one request: 16 partitions (+1 slot) per (request, query head)
     n = 1 * 64 * (16 + 1)
     assert k.paged_decode_attn_workspace_bytes(1, 64, 8, 9193, 0, cache_dtype=k.KV_CACHE_BF16) \
-        == 256 + -(-(n * 2 * 4) // 256) * 256 + n * 128 * 4
+        == -(-(n * 2 * 4) // 256) * 256 + n * 128 * 4
     with pytest.raises(k.KvError):
         k.paged_decode_attn_partition_tokens(1, 8, 9193, 0, 7)
     assert k.paged_decode_attn_workspace_bytes(1, 64, 8, 9193, 0, cache_dtype=7) == 0
