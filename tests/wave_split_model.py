@@ -19,8 +19,8 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 PAGE = 16
-PENALTY = 8            # kPiecePenalty
-RUN_PAGES = 512        # kCoopRunPages
+PENALTY = 64           # kPiecePenalty
+RUN_PAGES = 1024       # kCoopRunPages
 WAVES = 4              # kWaves
 NUM_CUS = 256          # kNumCUs
 MAX_TOKENS = 2048      # kWaveModeMaxTokens
