@@ -652,8 +652,8 @@ def main():
     measure_noop = args.verify == "on" and args.verify_cost == "on"
     # timed passes of --steps steps each: the step itself (no per-kernel events,
     # which would add gaps), the attention calls bracketed by events, and
-    # optionally the no-op tracker
-    total_steps = args.warmup + args.steps * (3 if measure_noop else 2)
+    # optionally the no-op tracker followed by the checked step once more
+    total_steps = args.warmup + args.steps * (4 if measure_noop else 2)
     make = {"uniform32": synth.uniform_32req, "batch64": synth.batch64_ctx8k, "skewed16": synth.skewed_16req}[args.config]
     wl = make(max_steps=total_steps)
     pt = wl.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
@@ -792,34 +792,45 @@ def main():
 
     noop = None
     if measure_noop:
-        # the same number of steps with the no-op tracker: no tag check, abort = NULL
-        a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        base3 = args.warmup + 2 * args.steps
-        graphs3 = None
-        if args.graph == "on":                   # timed the same way as pass 1
-            graphs3 = []
+        def timed_pass(base, check):
+            """--steps steps from step index `base`, timed the same way as pass 1."""
+            a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gs = None
+            if args.graph == "on":
+                gs = []
+                for i in range(args.steps):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        run_step(base + i, check=check, stream=torch.cuda.current_stream())
+                    gs.append(g)
+            torch.cuda.synchronize()
+            a2.record(stream)
             for i in range(args.steps):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    run_step(base3 + i, check=False, stream=torch.cuda.current_stream())
-                graphs3.append(g)
-        torch.cuda.synchronize()
-        a2.record(stream)
-        for i in range(args.steps):
-            if graphs3 is not None:
-                graphs3[i].replay()
-            else:
-                run_step(base3 + i, check=False)
-        b2.record(stream)
-        torch.cuda.synchronize()
-        off_ms = a2.elapsed_time(b2)
-        by_off = [step_bytes(wl, wl.seq_lens_at(base3 + i), cache, False)
-                  for i in range(args.steps)]
+                if gs is not None:
+                    gs[i].replay()
+                else:
+                    run_step(base + i, check=check)
+            b2.record(stream)
+            torch.cuda.synchronize()
+            return a2.elapsed_time(b2)
+
+        def kv_bytes(base):
+            return sum(step_bytes(wl, wl.seq_lens_at(base + i), cache, False)["kv_per_layer"]
+                       for i in range(args.steps))
+
+        # the no-op tracker (no tag check, abort = NULL), then the checked step
+        # again, so drift between passes does not favour either: the checked
+        # rate is the mean of the passes before and after the no-op one
+        base3 = args.warmup + 2 * args.steps
+        base4 = args.warmup + 3 * args.steps
+        off_ms = timed_pass(base3, False)
+        on2_ms = timed_pass(base4, True)
         kv_on = sum(b["kv_per_layer"] for b in by)
-        kv_off = sum(b["kv_per_layer"] for b in by_off)
         # per KV byte, so the tokens the contexts grew in between do not count
-        overhead = (elapsed_ms / kv_on) / (off_ms / kv_off) - 1.0
+        on_rate = 0.5 * (elapsed_ms / kv_on + on2_ms / kv_bytes(base4))
+        overhead = on_rate / (off_ms / kv_bytes(base3)) - 1.0
         noop = {"ms_per_step": round(off_ms / args.steps, 4),
+                "checked_after_ms_per_step": round(on2_ms / args.steps, 4),
                 "tag_check_overhead_pct": round(100.0 * overhead, 2)}
         log(args, f"no-op tracker: {off_ms / args.steps:.3f} ms/step; tag check costs "
                   f"{100 * overhead:.2f}%")
