@@ -388,6 +388,27 @@ def test_edge_abort_bad_ids_and_overlong(kv, cache):
     assert np.all(got[3] == 0)
 
 
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_automatic_split_of_one_long_request(kv, cache):
+    """A request of 9,193 tokens and one of 17 pages, 64 query / 8 KV heads,
+    automatic partitions: FP8 gets 12 of 768 tokens and BF16 16 of 576 (at
+    least 192 KiB of K and V per partition), which the reduction combines in
+    one round trip (rows of up to 16 slots). Every row against the oracle, and
+    again with explicit 512-token partitions (18 slots: the two-pass path)."""
+    lens = [9193, 17 * 16]
+    need = sum(max(1, -(-L // 16)) for L in lens)
+    e = _edge_state(kv, cache, 64, 8, lens, pool_pages=need + 8)
+    cd = kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16
+    pt = kv.paged_decode_attn_partition_tokens(len(lens), 8, max(lens), 0, cd)
+    assert pt == (768 if cache == "fp8" else 576)
+    assert -(-max(lens) // pt) <= 16
+    want = _edge_oracle(e, cache, lens)
+    got = _edge_run(kv, e, cache)
+    helpers.check_attention(got, want, label=f"automatic split {cache}")
+    got512 = _edge_run(kv, e, cache, partition_tokens=512)
+    helpers.check_attention(got512, want, label=f"512-token partitions {cache}")
+
+
 def _uses_persistent_kernel(batch, hkv, max_len, pt):
     """Whether the library picks its persistent kernel
     (short partitions and enough of them to give every CU a 4-wave group)."""
