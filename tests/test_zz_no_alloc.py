@@ -28,11 +28,12 @@ def kv():
     return k
 
 
-def _pair(kv, wl, rows, partition_tokens, step=0):
+def _pair(kv, wl, rows, partition_tokens, step=0, cache="fp8"):
     """One fused call through each entry point on twin states; the requests
     ``rows`` only (a smaller batch reads a prefix of the tables)."""
-    a = DeviceState(wl, kv, device=DEV, layers=[0])
-    b = DeviceState(wl, kv, device=DEV, layers=[0])
+    a = DeviceState(wl, kv, cache=cache, device=DEV, layers=[0])
+    b = DeviceState(wl, kv, cache=cache, device=DEV, layers=[0])
+    cd = kv.KV_CACHE_FP8_E4M3 if cache == "fp8" else kv.KV_CACHE_BF16
     n = len(rows)
     q, kn, vn = a.step_layer_inputs(0, step)
     q, kn, vn = q[:n].contiguous(), kn[:n].contiguous(), vn[:n].contiguous()
@@ -46,15 +47,16 @@ def _pair(kv, wl, rows, partition_tokens, step=0):
         if noalloc:
             kv.paged_decode_attn_append_noalloc(q, kn, vn, st.k_pool[0], st.v_pool[0],
                                                 st.k_scale[0], st.v_scale[0], bt, seq, msl, out,
-                                                sm, partition_tokens=partition_tokens)
+                                                sm, partition_tokens=partition_tokens,
+                                                cache_dtype=cd)
         else:
             nb = kv.paged_decode_attn_workspace_bytes(n, wl.num_q_heads, wl.num_kv_heads, msl,
-                                                      partition_tokens)
+                                                      partition_tokens, cache_dtype=cd)
             assert nb > 0, "the case must use a workspace"
             ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
             kv.paged_decode_attn_append(q, kn, vn, st.k_pool[0], st.v_pool[0], st.k_scale[0],
                                         st.v_scale[0], bt, seq, msl, out, sm, workspace=ws,
-                                        partition_tokens=partition_tokens)
+                                        partition_tokens=partition_tokens, cache_dtype=cd)
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]), "outputs differ from the workspace entry point"
@@ -75,6 +77,16 @@ def test_noalloc_two_calls_second_smaller(kv):
     _pair(kv, wl, list(range(8)), 0)
     say("noalloc: call 2, 3 requests, 512-token partitions")
     _pair(kv, wl, [0, 1, 2], 512)
+
+
+def test_noalloc_bf16_cache_two_calls_second_smaller(kv):
+    """The BF16-cache variant of the no-alloc call: automatic partitions
+    (sized for 2-byte elements), then a smaller call with 256-token ones."""
+    wl = synth.mixed_8req(max_steps=1)
+    say("noalloc bf16: call 1, 8 requests, automatic partitions")
+    _pair(kv, wl, list(range(8)), 0, cache="bf16")
+    say("noalloc bf16: call 2, 4 requests, 256-token partitions")
+    _pair(kv, wl, [0, 1, 2, 3], 256, cache="bf16")
 
 
 def test_noalloc_persistent_kernel_then_shared(kv):
