@@ -15,10 +15,12 @@
 //    weights its B operand, so a lane's four results are four tokens of one
 //    weight row and the 16 lanes of a token add to 16 consecutive outputs
 //    (one 64-byte line per atomic instruction and token group);
-//  * integer codes (sign-magnitude, |q| <= 7) become bf16 exactly through an
-//    e4m3 lookup and the hardware decode, e4m3 codes through the decode
-//    alone; the MFMA sums one group in fp32 and the group's row scale
-//    multiplies that partial (the products themselves are exact);
+//  * integer codes (|q| <= 7) are sign-magnitude fields placed so that one
+//    mask (values 0..3) or a rotate and a mask (values 4..7) leaves, in each
+//    byte, an e4m3 subnormal of q * 2^-9; the hardware decode with scale 2^9
+//    then gives q in bf16 exactly. e4m3 codes go through the decode alone;
+//    the MFMA sums one group in fp32 and the group's row scale multiplies
+//    that partial (the products themselves are exact);
 //  * grid: a workgroup = 4 wavefronts = 4 consecutive 16-row tiles over one
 //    range of input groups; ranges are split so the grid fills the chip, and
 //    partial sums are added to y with hardware fp32 atomics (y must hold
@@ -83,12 +85,17 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const uint16_t* __restrict
             for (int i = 0; i < 8; ++i) {
                 const uint32_t bits = (raw[c][i / 2] >> (16 * (i % 2))) & 0xFFFFu;
                 // round-to-odd quotient, then half-to-even to an integer: exact (24 >= 4 + 2);
-                // |w / s| <= amax / fp32(amax / 7) < 7.5, so -8 never occurs and the clamp
-                // to [-7, 7] changes nothing
+                // |w / s| <= amax / fp32(amax / 7) < 7.5, so the clamp to [-7, 7] changes
+                // nothing and three magnitude bits suffice
                 const float qf = rintf(div_round_odd(bf16_bits_to_float(bits), s));
                 const float qc = fminf(fmaxf(qf, -7.0f), 7.0f);
-                const uint32_t nib = (qc < 0.0f ? 8u : 0u) | static_cast<uint32_t>(fabsf(qc));
-                word |= nib << (8 * (i % 4) + 4 * (i / 4));       // sign-magnitude nibble
+                const uint32_t mag = static_cast<uint32_t>(fabsf(qc));
+                const uint32_t neg = qc < 0.0f ? 1u : 0u;
+                const int j = i % 4;
+                if (i < 4)      // byte j: magnitude in bits 0..2, sign in bit 7
+                    word |= (mag << (8 * j)) | (neg << (8 * j + 7));
+                else            // magnitude in bits 4..6 of byte j, sign in bit 3 of byte j + 1 (mod 4)
+                    word |= (mag << (8 * j + 4)) | (neg << (8 * ((j + 1) % 4) + 3));
             }
             d[c] = word;
         }
@@ -115,22 +122,19 @@ __global__ __launch_bounds__(256) void wq_pack_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 // GEMV
 // ---------------------------------------------------------------------------
-// One packed dword of 8 sign-magnitude nibbles (value i in byte i % 4, low
-// nibble for i < 4) -> 8 bf16, exactly. A byte permute looks up the e4m3
-// codes of the magnitudes 0..7 (8-entry table in two registers), the sign
-// bits are ORed into bit 7, and the hardware decode turns the e4m3 codes into
-// bf16 (integers up to 7 are exact in both). About 1.5 VALU instructions per
-// weight, against 2.5 for bit-field extract, int-to-float and pack.
+// One packed dword of 8 INT4 codes -> 8 bf16, exactly. Value i < 4 has its
+// magnitude in bits 0..2 and its sign in bit 7 of byte i, so w & 0x87878787 is
+// four e4m3 subnormals (+-|q| * 2^-9); value i + 4 has its magnitude in bits
+// 4..6 of byte i and its sign in bit 3 of byte i + 1 (mod 4), so a rotate
+// right by 4 and the same mask give the other four. The hardware decode with
+// scale 2^9 returns q: ~0.9 VALU instructions per weight.
 __device__ __forceinline__ bf16x8 int4x8_to_bf16(uint32_t w) {
-    constexpr uint32_t kCodes0123 = 0x44403800u;     // e4m3 of 3, 2, 1, 0 (bytes 3..0)
-    constexpr uint32_t kCodes4567 = 0x4E4C4A48u;     // e4m3 of 7, 6, 5, 4
-    const uint32_t lo = __builtin_amdgcn_perm(kCodes4567, kCodes0123, w & 0x07070707u) |
-                        ((w << 4) & 0x80808080u);    // values 0..3
-    const uint32_t hi = __builtin_amdgcn_perm(kCodes4567, kCodes0123, (w >> 4) & 0x07070707u) |
-                        (w & 0x80808080u);           // values 4..7
-    bf16x2 p0, p1, p2, p3;
-    decode4_bf16(lo, p0, p1);
-    decode4_bf16(hi, p2, p3);
+    const uint32_t lo = w & 0x87878787u;                                  // values 0..3
+    const uint32_t hi = __builtin_amdgcn_alignbit(w, w, 4) & 0x87878787u;  // values 4..7
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
     return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 

@@ -391,8 +391,7 @@ int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
  * only "four-bit integer"): weights W [n][k] in bf16 are quantized per row and
  * per group of 128 inputs with one fp32 scale s:
  *   WQ_INT4:      q = RNE(w / s) of the exact quotient, s = amax / 7, so
- *                 |q| <= 7 (|w / s| <= amax / fp32(amax / 7) < 7.5: the
- *                 fourth bit is free for a sign-magnitude code)
+ *                 |q| <= 7 (|w / s| <= amax / fp32(amax / 7) < 7.5)
  *   WQ_FP8_E4M3:  q = E4M3(w / s) (the KV encoder), s = amax / 448
  * (s = 1.0 for an all-zero group; weights must be finite), and the product is
  *   y[m][n] += sum_k x[m][k] * q[n][k] * s[n][k / 128]
@@ -402,9 +401,11 @@ int kv_ingest_prefill(const void* k_rows, const void* v_rows, int64_t n_rows,
  * inputs 128 g .. 128 g + 127, blocks ordered nt-major: block index
  * b = nt * (k / 128) + g. Element (row 16 nt + r, input 128 g + 32 c + 8 j + i),
  * r < 16, c < 4, j < 4, i < 8, with lane l = 16 j + r:
- *   WQ_INT4:     byte 1024 b + 16 l + 4 c + i % 4, low nibble for i < 4,
- *                high nibble for i >= 4; sign-magnitude (bit 3 = sign,
- *                bits 0..2 = |q|, zero always positive);
+ *   WQ_INT4:     dword 256 b + 4 l + c (bytes 4 x that), sign-magnitude
+ *                fields: for i < 4, |q| in bits 0..2 and the sign in bit 7
+ *                of byte i % 4; for i >= 4, |q| in bits 4..6 of byte i % 4
+ *                and the sign in bit 3 of byte (i + 1) % 4 (bytes of the
+ *                dword; zero is always positive);
  *   WQ_FP8_E4M3: byte 2048 b + 1024 (c / 2) + 16 l + 8 (c % 2) + i.
  * Scales: fp32 [n / 16][k / 128][16], element (b, r) = s of row 16 nt + r.
  */

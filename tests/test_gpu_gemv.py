@@ -26,7 +26,8 @@ def kv():
 
 
 def _index_maps(n, k, fmt):
-    """Byte offset (and nibble) of every element (row, input), from the header's formulas."""
+    """Byte offset of every element (row, input), from the header's formulas; INT4:
+    the offset of its dword and the value index i within it."""
     rows = np.arange(n)[:, None]
     cols = np.arange(k)[None, :]
     nt, r = rows // 16, rows % 16
@@ -35,18 +36,22 @@ def _index_maps(n, k, fmt):
     b = nt * (k // G) + g
     lane = 16 * j + r
     if fmt == 0:
-        return 1024 * b + 16 * lane + 4 * c + i % 4, i // 4
+        return 1024 * b + 16 * lane + 4 * c, i
     return 2048 * b + 1024 * (c // 2) + 16 * lane + 8 * (c % 2) + i, None
 
 
 def _unpack(packed, n, k, fmt):
-    off, nib = _index_maps(n, k, fmt)
-    byte = packed[off]
+    off, i = _index_maps(n, k, fmt)
     if fmt == 0:
-        v = (byte >> (4 * nib)) & 0xF
-        assert not np.any(v == 8), "negative zero code"
-        return np.where(v >= 8, -(v & 7), v).astype(np.int8)
-    return byte
+        # the header's fields: i < 4: |q| in bits 0..2, sign in bit 7 of byte i;
+        # i >= 4: |q| in bits 4..6 of byte i % 4, sign in bit 3 of byte (i + 1) % 4
+        word = packed.view(np.uint32)[off // 4].astype(np.int64)
+        j = i % 4
+        mag = np.where(i < 4, word >> (8 * j), word >> (8 * j + 4)) & 7
+        neg = np.where(i < 4, word >> (8 * j + 7), word >> (8 * ((j + 1) % 4) + 3)) & 1
+        assert not np.any((neg == 1) & (mag == 0)), "negative zero code"
+        return np.where(neg == 1, -mag, mag).astype(np.int8)
+    return packed[off]
 
 
 def _weights(rng, n, k):

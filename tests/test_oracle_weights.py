@@ -110,9 +110,10 @@ def test_one_hot_activation_reads_a_column(fmt):
 
 def test_int4_codes_never_reach_minus_8():
     """|w / s| <= amax / fp32(amax / 7) < 7.5 for every finite bf16 amax, so
-    the INT4 codes stay in [-7, 7] and the fourth bit is free for a sign
-    (the packed format is sign-magnitude). Exhaustive over the amax patterns;
-    then groups whose most negative value is -amax, quantized by the oracle."""
+    the INT4 codes stay in [-7, 7] and three magnitude bits and a sign bit
+    hold every code (the packed format is sign-magnitude). Exhaustive over the
+    amax patterns; then groups whose most negative value is -amax, quantized
+    by the oracle."""
     a_bits = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)     # every positive finite
     amax = e4m3.bf16_bits_to_f64(a_bits)
     s = (amax / 7.0).astype(np.float32).astype(np.float64)
