@@ -59,8 +59,8 @@ INGEST_COUNTER_TRAFFIC = {
 }
 GEMV_COUNTER_TRAFFIC = {
     "sources": ("gemv.hip", "kv_device.h"),
-    "source_sha": "fec999b66cdac863",
-    "read_bytes": 1.24997e8,
+    "source_sha": "37ca3d3f20bb1a07",
+    "read_bytes": 1.24994e8,
     "write_bytes": 5.734e5,
 }
 
