@@ -111,6 +111,42 @@ def test_gemv_against_oracle(kv, fmt, m, n, k):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("m", [1, 4, 64])
+def test_one_hot_inputs_read_every_code_position(kv, fmt, m):
+    """Token t of a call has x = 1.0 at one input j_t and zeros elsewhere, and
+    the calls run j over every input of a 32 x 256 matrix, so each output is a
+    single product: y[t] must equal fp32(q[:, j_t] * s) bit for bit. INT4
+    weights are q * 2^-6 with q = (3 row + input) % 15 - 7, so every code value
+    sits at every position of the packed words and each group's scale is
+    exactly 2^-6; FP8 weights are random. 1 and 4 tokens take the small-batch
+    kernel, 64 the chunked one."""
+    n, k = 32, 2 * G
+    if fmt == 0:
+        q = ((3 * np.arange(n)[:, None] + np.arange(k)[None, :]) % 15 - 7).astype(np.float32)
+        wb = ((q * 2.0 ** -6).view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        wb = _weights(np.random.default_rng(11), n, k)
+    packed, scales = _pack(kv, wb, fmt)
+    q_o, s_o = weights.quantize_int4(wb) if fmt == 0 else weights.quantize_fp8(wb)
+    if fmt == 0:
+        assert np.array_equal(q_o, q.astype(q_o.dtype)) and np.all(s_o == 2.0 ** -6)
+    assert np.array_equal(_unpack(packed.cpu().numpy(), n, k, fmt), q_o)
+    wd = weights.dequant_int4(q_o, s_o) if fmt == 0 else weights.dequant_fp8(q_o, s_o)
+    want_cols = wd.astype(np.float32)            # one exact product, rounded once to fp32
+    for j0 in range(0, k, m):
+        cols = (j0 + np.arange(m)) % k
+        xb = np.zeros((m, k), np.uint16)
+        xb[np.arange(m), cols] = 0x3F80                                 # bf16 1.0
+        y = torch.zeros((m, n), dtype=torch.float32, device=DEV)
+        kv.wq_gemv(torch.from_numpy(xb.view(np.int16)).to(DEV), packed, scales, y, n, fmt)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        want = want_cols[:, cols].T
+        assert np.array_equal(got, want), f"fmt {fmt} m {m} inputs {cols[:4]}..: " \
+            f"{np.argwhere(got != want)[:4].tolist()}"
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("m", [1, 16])
 def test_gemv_full_size_sampled_rows(kv, fmt, m):
     """8192 x 8192 weights, 1 token (the small-batch kernel) and 16 tokens,
