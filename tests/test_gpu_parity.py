@@ -537,6 +537,49 @@ def test_verify_tags_long_rows(kv, split):
             assert int(ws.count_nonzero()) == 0
 
 
+def test_split_verify_captured_in_a_graph_replays_fresh(kv):
+    """The split tag check (5,000-page rows over three workgroups per request,
+    combining through the counter workspace) captured in a HIP graph and
+    replayed with the expected tags changed between replays: every replay
+    gives the oracle's mask for the tags it read, overwrites junk flags, and
+    leaves the counters at zero for the next replay."""
+    rng = np.random.default_rng(29)
+    num_pages, batch, width = 40_000, 6, 5_000
+    tags = rng.integers(0, 2 ** 32, num_pages, dtype=np.uint64).astype(np.uint32)
+    bt = rng.integers(0, num_pages, (batch, width)).astype(np.int32)
+    exp = tags[bt].copy()
+    lens = np.array([16 * 5_000, 16 * 4_500, 16 * 3_000, 16 * 2_049, 16 * 5_000, 16 * 100],
+                    np.int32)
+    exp[1, 4_200] ^= 1                                       # request 1 fails throughout
+    d_tags = torch.from_numpy(tags.view(np.int32)).to(DEV)
+    d_bt = torch.from_numpy(bt).to(DEV)
+    d_exp = torch.from_numpy(exp.view(np.int32)).to(DEV)
+    d_lens = torch.from_numpy(lens).to(DEV)
+    ws = torch.zeros(kv.kv_verify_tags_workspace_bytes(batch, width), dtype=torch.uint8,
+                     device=DEV)
+    ab = torch.zeros(batch, dtype=torch.uint8, device=DEV)
+    kv.kv_verify_tags(d_tags, d_bt, d_exp, d_lens, ab, workspace=ws)   # warm-up, eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kv.kv_verify_tags(d_tags, d_bt, d_exp, d_lens, ab, workspace=ws)
+    torch.cuda.synchronize()
+    # per replay, one more page to flip: a chunk edge, a last page, an ignored page
+    flips = [(0, 2_048), (4, 4_999), (3, 2_048), (5, 100), (2, 2_999)]
+    for r, (b, pg) in enumerate(flips):
+        cur = exp.copy()
+        cur[b, pg] ^= 1 << (r + 3)
+        d_exp.copy_(torch.from_numpy(cur.view(np.int32)))
+        ab.fill_(0xA5 if r % 2 else 1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = paged.verify_tags(tags, bt, cur, lens, 16)
+        assert np.array_equal(ab.cpu().numpy(), want), (r, ab.cpu().numpy(), want)
+        assert int(ws.count_nonzero()) == 0, f"replay {r}: counters not reset"
+    say("split tag check: 5 graph replays with changed tags match the oracle")
+
+
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
 def test_wave_mode_even_page_split_long_partitions(kv, cache):
     """Partitions of 256 to 2048 tokens in the wave-mode kernel, which splits
