@@ -5,8 +5,9 @@ Two calls in a row share the library's static scratch, the second with a
 smaller input (fewer requests, other partitions), each compared with the
 workspace call on identical copies of the state: outputs and pools bit for
 bit, and the outputs within the attention tolerance of the oracle. Also the
-persistent kernel's path (short partitions, separate reduction) and the
-refusal of a size whose workspace exceeds the scratch.
+persistent kernel's path (short partitions, separate reduction), the call
+captured in a HIP graph and replayed with new queries, and the refusal of a
+size whose workspace exceeds the scratch.
 """
 
 import numpy as np
@@ -97,6 +98,54 @@ def test_noalloc_persistent_kernel_then_shared(kv):
     assert ws.uses_wave_kernel(8, 8, wl.max_seq_len, 64)
     _pair(kv, wl, list(range(8)), 64)
     _pair(kv, wl, [0, 1], 1024)
+
+
+def test_noalloc_call_captured_in_a_graph_replays_like_eager(kv):
+    """A caller under graph capture: the no-alloc call (FP8, 512-token
+    partitions, so the split partials live in the static scratch) captured
+    once and replayed with new queries written between replays, each replay
+    against the workspace entry point run eagerly on the same inputs: outputs
+    bit for bit, pools equal. (The first call on the device, which looks up
+    the scratch address, runs before the capture.)"""
+    wl = synth.mixed_8req(max_steps=1)
+    a = DeviceState(wl, kv, device=DEV, layers=[0])
+    b = DeviceState(wl, kv, device=DEV, layers=[0])
+    q, kn, vn = a.step_layer_inputs(0, 0)
+    msl, sm, pt = wl.max_seq_len, sm_scale_for(wl), 512
+    shape = (wl.batch, wl.num_q_heads, wl.head_dim)
+    nb = kv.paged_decode_attn_workspace_bytes(wl.batch, wl.num_q_heads, wl.num_kv_heads, msl, pt)
+    assert nb > 0, "the case must use the scratch"
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    seq_a, seq_b = a.seq_lens(0), b.seq_lens(0)
+    qg = q.clone()
+    out_g = torch.full(shape, float("nan"), device=DEV)
+
+    def call_noalloc():
+        kv.paged_decode_attn_append_noalloc(qg, kn, vn, b.k_pool[0], b.v_pool[0], b.k_scale[0],
+                                            b.v_scale[0], b.block_table, seq_b, msl, out_g, sm,
+                                            partition_tokens=pt)
+
+    call_noalloc()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call_noalloc()
+    torch.cuda.synchronize()
+    out_e = torch.full(shape, float("nan"), device=DEV)
+    for r in range(3):
+        qr = (q.float() * (1.0 + 0.25 * r)).to(torch.bfloat16)
+        qg.copy_(qr)
+        out_g.fill_(float("nan"))
+        out_e.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        kv.paged_decode_attn_append(qr, kn, vn, a.k_pool[0], a.v_pool[0], a.k_scale[0],
+                                    a.v_scale[0], a.block_table, seq_a, msl, out_e, sm,
+                                    workspace=ws, partition_tokens=pt)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {r}: output differs from the eager call"
+        assert torch.equal(a.k_pool[0], b.k_pool[0]) and torch.equal(a.v_pool[0], b.v_pool[0])
+    say("noalloc: 3 graph replays with new queries equal the workspace entry point")
 
 
 def test_noalloc_refuses_a_workspace_beyond_its_scratch(kv):
