@@ -382,7 +382,25 @@ __device__ __forceinline__ void apply_new_token(u32x4 (&K)[PairTiles<FP8>::N],
 // `proc_end` processes the pairs of the FP8 epilogue, which always include
 // the wave's last pair (the only one the fused append ever patches), so the
 // steady-state loop carries no patch logic.
-template <bool FP8, int DEPTH, typename Issue, typename Proc, typename ProcEnd, typename Hook>
+//
+// PRIO: the wave's scheduling priority follows its own progress through its
+// pairs (3 in the first quarter, then 2, 1, 0). Two 4-wave workgroups share a
+// CU; without it the one that started first finishes well before the other
+// (a per-workgroup timing probe saw ~95-110 against up to ~175 us at 64
+// requests), which then streams alone. Ranked by progress, the later one
+// catches up and the CU stays loaded to the end: at 64 requests x ~8.7k
+// tokens the launch went 180 -> 178 us. With one 8-wave workgroup per CU
+// (32 requests) it measured 0.5-1% slower, so only the 4-wave kernel uses it.
+__device__ __forceinline__ void progress_priority(int i, int n) {
+    const int quarter = (4 * i) / n;                      // 0 <= i < n
+    if (quarter <= 0) __builtin_amdgcn_s_setprio(3);
+    else if (quarter == 1) __builtin_amdgcn_s_setprio(2);
+    else if (quarter == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
+template <bool FP8, int DEPTH, bool PRIO, typename Issue, typename Proc, typename ProcEnd,
+          typename Hook>
 __device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc, ProcEnd&& proc_end,
                                                Hook&& after_issue) {
     if (n <= 0) return;
@@ -395,6 +413,7 @@ __device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc
         after_issue();     // runs while the first tiles are in flight
         int i = 0;
         for (; i + 7 < n; i += 4) {
+            if constexpr (PRIO) progress_priority(i, n);
             proc(t0, i);
             issue(t0, i + 4);
             proc(t1, i + 1);
@@ -424,6 +443,7 @@ __device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc
         after_issue();     // runs while the first tiles are in flight
         int i = 0;
         for (; i + 5 < n; i += 3) {
+            if constexpr (PRIO) progress_priority(i, n);
             proc(t0, i);
             issue(t0, i + 3);
             proc(t1, i + 1);
@@ -482,7 +502,7 @@ __device__ __forceinline__ void load_q_operand(bf16x8 (&qop)[4], const uint16_t*
 // slot in the pair's registers when it gets there, and stores the codes to
 // the pool after its last load. Nothing in the launch reads those codes back
 // from memory, so no fence or barrier is involved.
-template <bool FP8, bool APPEND, int DEPTH, typename TileOf>
+template <bool FP8, bool APPEND, int DEPTH, bool PRIO, typename TileOf>
 __device__ __forceinline__ void stream_share(
     TileOf&& tile_of, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int npg,
     int pg0, int first, int stride, int t_begin, int t_end, int L, int lane, int jgrp,
@@ -526,7 +546,7 @@ __device__ __forceinline__ void stream_share(
         process_pair<FP8>(t, (pg0 + 2 * pr) * kPage, t_end, jgrp, s_scale, qop, m_run, l_run,
                           acc_o);
     };
-    pipeline_pairs<FP8, DEPTH>(n_w, issue, proc, proc_end, prepare);
+    pipeline_pairs<FP8, DEPTH, PRIO>(n_w, issue, proc, proc_end, prepare);
     if constexpr (APPEND) {
         if (owns_new) {
             const size_t tile = tile_of(t_new / kPage - pg0);
@@ -819,7 +839,7 @@ void attn_partition_kernel(
             return static_cast<size_t>(id) * hkv + g;
         };
         const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
-        stream_share<FP8, APPEND, kSharedDepth>(
+        stream_share<FP8, APPEND, kSharedDepth, NW == 4>(
             tile_of, k_pool, v_pool, npg, pg0, wave, NW, t_begin, t_end, L, lane, jgrp, s_scale,
             qop, k_new + new_row, v_new + new_row, k_scale + g, v_scale + g, m_run, l_run, acc_o);
     }
@@ -1019,10 +1039,10 @@ void attn_wave_kernel(
                 return static_cast<size_t>(id) * hkv + g;
             };
             const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
-            stream_share<FP8, APPEND, 3>(tile_of, k_pool, v_pool, npg, k0, wave, kWaves, t_begin,
-                                      t_end, L, lane, jgrp, s_scale, qop, k_new + new_row,
-                                      v_new + new_row, k_scale + g, v_scale + g, m_run, l_run,
-                                      acc_o);
+            stream_share<FP8, APPEND, 3, false>(tile_of, k_pool, v_pool, npg, k0, wave, kWaves,
+                                                t_begin, t_end, L, lane, jgrp, s_scale, qop,
+                                                k_new + new_row, v_new + new_row, k_scale + g,
+                                                v_scale + g, m_run, l_run, acc_o);
         }
         float l_tot = l_run + __shfl_xor(l_run, 16);
         l_tot += __shfl_xor(l_tot, 32);
