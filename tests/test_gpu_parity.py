@@ -357,8 +357,12 @@ def _edge_oracle(e, cache, lens, abort=None, bt=None):
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
 @pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2), (4, 4), (32, 2), (4, 2), (6, 2), (12, 3),
-                                     (24, 4), (24, 2), (10, 2), (14, 1)])
+                                     (24, 4), (24, 2), (10, 2), (14, 1), (7, 1), (18, 2),
+                                     (20, 2), (11, 1), (26, 2), (15, 1)])
 def test_edge_lengths_groups_and_garbage_slots(kv, cache, hq, hkv):
+    """Every GQA group size from 1 to 16 (G = hq / hkv), lengths around page and
+    page-pair edges, an empty request, and slots past each length holding
+    garbage, at the automatic and three short partition sizes."""
     lens = [1, 2, 15, 16, 17, 31, 33, 100, 0, 47]
     e = _edge_state(kv, cache, hq, hkv, lens)
     for pt in (0, 16, 32, 64):
