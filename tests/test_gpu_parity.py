@@ -421,9 +421,11 @@ def _uses_persistent_kernel(batch, hkv, max_len, pt):
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
-@pytest.mark.parametrize("hq", [16, 24, 32, 48, 64, 96, 128])
+@pytest.mark.parametrize("hq", [8, 16, 24, 32, 40, 48, 56, 64, 72, 80, 88, 96, 104, 112, 120,
+                                128])
 def test_wave_mode_edges_aborts_and_bad_ids(kv, cache, hq):
-    """A batch large enough for the persistent kernel, with ragged
+    """Every GQA group size from 1 to 16 (8 KV heads). A batch large enough for
+    the persistent kernel, with ragged
     lengths (1 token, page and partition boundaries, empty requests) and
     aborted and badly mapped requests between valid ones, so the kernel's
     per-request numbering of its work items has to skip them."""
