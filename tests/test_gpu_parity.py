@@ -374,6 +374,56 @@ def test_edge_lengths_groups_and_garbage_slots(kv, cache, hq, hkv):
 
 
 @pytest.mark.parametrize("cache", ["fp8", "bf16"])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (12, 4), (20, 4), (32, 2)])
+@pytest.mark.parametrize("pt", [0, 32])
+def test_fused_append_equals_separate_calls_any_group(kv, cache, hq, hkv, pt):
+    """The fused append + attention call against kv_append_* followed by
+    paged_decode_attn on a twin state, at group sizes 1, 3, 5 and 16 and two
+    partition sizes: outputs and pools bit for bit, and the output within the
+    oracle's tolerance. The new tokens land first in a page, last in a page,
+    mid-page and in requests that had none."""
+    lens = [1, 2, 15, 16, 17, 31, 33, 100, 0, 47]          # tokens before the step
+    plus = [L + 1 for L in lens]                              # after it
+    a = _edge_state(kv, cache, hq, hkv, plus)
+    b = _edge_state(kv, cache, hq, hkv, plus)
+    rng = np.random.default_rng(5)
+    batch = len(lens)
+    kb = synth._f32_to_bf16_bits(rng.normal(0, 1, (batch, hkv, 128)).astype(np.float32))
+    vb = synth._f32_to_bf16_bits(rng.normal(0, 0.5, (batch, hkv, 128)).astype(np.float32))
+    kn = torch.from_numpy(kb.view(np.int16)).to(DEV)
+    vn = torch.from_numpy(vb.view(np.int16)).to(DEV)
+    seq = torch.from_numpy(np.array(plus, np.int32)).to(DEV)
+    msl = max(plus)
+    q = torch.from_numpy(a["q"].view(np.int16)).to(DEV)
+    fp8 = cache == "fp8"
+    cd = kv.KV_CACHE_FP8_E4M3 if fp8 else kv.KV_CACHE_BF16
+    n = kv.paged_decode_attn_workspace_bytes(batch, hq, hkv, msl, pt, cache_dtype=cd)
+    ws_a = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
+    ws_b = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
+    out_f = torch.full((batch, hq, 128), float("nan"), device=DEV)
+    out_s = torch.full((batch, hq, 128), float("nan"), device=DEV)
+    sm = 0.0883883
+    kv.paged_decode_attn_append(q, kn, vn, a["kp"], a["vp"], a["kst"] if fp8 else None,
+                                a["vst"] if fp8 else None, a["btt"], seq, msl, out_f, sm,
+                                workspace=ws_a, partition_tokens=pt, cache_dtype=cd)
+    tok_seq = torch.arange(batch, dtype=torch.int32, device=DEV)
+    tok_pos = seq - 1
+    if fp8:
+        kv.kv_append_quant(kn, vn, tok_seq, tok_pos, b["btt"], b["kst"], b["vst"], b["kp"],
+                           b["vp"])
+    else:
+        kv.kv_append_bf16(kn, vn, tok_seq, tok_pos, b["btt"], b["kp"], b["vp"])
+    kv.paged_decode_attn(q, b["kp"], b["vp"], b["kst"] if fp8 else None,
+                         b["vst"] if fp8 else None, b["btt"], seq, msl, out_s, sm,
+                         workspace=ws_b, partition_tokens=pt, cache_dtype=cd)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_s), "fused output differs from the separate calls"
+    assert torch.equal(a["kp"], b["kp"]) and torch.equal(a["vp"], b["vp"])
+    want = _edge_oracle(b, cache, plus)
+    helpers.check_attention(out_f.cpu().numpy(), want, label=f"fused {cache} G={hq // hkv} p{pt}")
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
 def test_edge_abort_bad_ids_and_overlong(kv, cache):
     lens = [20, 40, 5, 64, 16]
     e = _edge_state(kv, cache, 8, 1, lens)
