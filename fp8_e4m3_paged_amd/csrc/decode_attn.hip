@@ -389,8 +389,9 @@ __device__ __forceinline__ void apply_new_token(u32x4 (&K)[PairTiles<FP8>::N],
 // (a per-workgroup timing probe saw ~95-110 against up to ~175 us at 64
 // requests), which then streams alone. Ranked by progress, the later one
 // catches up and the CU stays loaded to the end: at 64 requests x ~8.7k
-// tokens the launch went 180 -> 178 us. With one 8-wave workgroup per CU
-// (32 requests) it measured 0.5-1% slower, so only the 4-wave kernel uses it.
+// tokens the launch went 180 -> 178 us (FP8) and 355 -> 350 us (BF16). With
+// one 8-wave workgroup per CU (32 requests) it measured 0.5-1% slower, so
+// only the 4-wave kernel uses it.
 __device__ __forceinline__ void progress_priority(int i, int n) {
     const int quarter = (4 * i) / n;                      // 0 <= i < n
     if (quarter <= 0) __builtin_amdgcn_s_setprio(3);
@@ -468,6 +469,7 @@ __device__ __forceinline__ void pipeline_pairs(int n, Issue&& issue, Proc&& proc
         issue(t1, 1);
         after_issue();
         for (int i = 0; i < n; i += 2) {
+            if constexpr (PRIO) progress_priority(i, n);
             proc_end(t0, i);
             issue(t0, i + 2);
             if (i + 1 < n) proc_end(t1, i + 1);
