@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # for the kernel sources they were taken on (sha256 prefix of decode_attn.hip
 # + kv_device.h + kv_launch.h). See profiles/attn_partition_kernel_batch64_ctx8k_hbm_counters.md.
 COUNTER_TRAFFIC = {
-    "source_sha": "9a705b059e97a00e",
+    "source_sha": "7563e0198cdbc69e",
     "workload": "batch64_ctx8k",
     "read_bytes": 1.14390e9,
     "write_bytes": 2.490e6,

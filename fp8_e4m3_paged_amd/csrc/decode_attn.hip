@@ -389,9 +389,11 @@ __device__ __forceinline__ void apply_new_token(u32x4 (&K)[PairTiles<FP8>::N],
 // (a per-workgroup timing probe saw ~95-110 against up to ~175 us at 64
 // requests), which then streams alone. Ranked by progress, the later one
 // catches up and the CU stays loaded to the end: at 64 requests x ~8.7k
-// tokens the launch went 180 -> 178 us (FP8) and 355 -> 350 us (BF16). With
-// one 8-wave workgroup per CU (32 requests) it measured 0.5-1% slower, so
-// only the 4-wave kernel uses it.
+// tokens the launch went 180 -> 178 us (FP8) and 355 -> 350 us (BF16), and
+// the persistent kernel (two 4-wave workgroups per CU, progress counted per
+// piece) on 16 requests of up to 131k tokens 186-188 -> 184 us. With one
+// 8-wave workgroup per CU (32 requests) it measured 0.5-1% slower, so the
+// 8-wave instance does not use it.
 __device__ __forceinline__ void progress_priority(int i, int n) {
     const int quarter = (4 * i) / n;                      // 0 <= i < n
     if (quarter <= 0) __builtin_amdgcn_s_setprio(3);
@@ -1041,7 +1043,7 @@ void attn_wave_kernel(
                 return static_cast<size_t>(id) * hkv + g;
             };
             const size_t new_row = (static_cast<size_t>(b) * hkv + g) * kDim;
-            stream_share<FP8, APPEND, 3, false>(tile_of, k_pool, v_pool, npg, k0, wave, kWaves,
+            stream_share<FP8, APPEND, 3, true>(tile_of, k_pool, v_pool, npg, k0, wave, kWaves,
                                                 t_begin, t_end, L, lane, jgrp, s_scale, qop,
                                                 k_new + new_row, v_new + new_row, k_scale + g,
                                                 v_scale + g, m_run, l_run, acc_o);
