@@ -84,7 +84,9 @@ def counter_traffic(entry):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for --config skewed16, whose one-layer "
+                         "step is ~0.19 ms)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="batch64", choices=["uniform32", "batch64", "skewed16"])
     ap.add_argument("--cache", default="fp8", choices=["fp8", "bf16"])
@@ -113,7 +115,10 @@ def parse():
     ap.add_argument("--sweep-caches", default="bf16,fp8", help="sweep mode: the caches to run")
     ap.add_argument("--gemv-tokens", default="1,8,16,32,64",
                     help="--mode gemv: comma-separated token counts (the roofline needs 1)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 200 if args.mode == "step" and args.config == "skewed16" else 20
+    return args
 
 
 def log(args, msg):
