@@ -59,7 +59,7 @@ INGEST_COUNTER_TRAFFIC = {
 }
 GEMV_COUNTER_TRAFFIC = {
     "sources": ("gemv.hip", "kv_device.h"),
-    "source_sha": "60e9b81a922550e5",
+    "source_sha": "7706fea6e8b160f5",
     "read_bytes": 1.25000e8,
     "write_bytes": 5.734e5,
 }

@@ -430,7 +430,7 @@ void wq_gemv_small_kernel(const uint16_t* __restrict__ x, int32_t m_rows,
     // 2, 1, 0), so the workgroups resident on a CU finish closer together:
     // 2.4-3.3% off an INT4 layer at 1-4 tokens, while FP8 weights measured the
     // same or 0.3% slower with it (and the chunked kernel, ranked by chunk,
-    // -2% to +2% by token count).
+    // between 2% faster and 6% slower by token count and format).
     int i = 0;
     for (; i + 5 < ng; i += 3) {
         if constexpr (INT4) {
