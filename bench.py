@@ -753,16 +753,24 @@ def main():
     # cost is not counted once per launch); separate calls: a pair per attention call
     ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps * (1 if fused else wl.num_layers))]
+    # and one pair around each step's tag check, whose time is taken out of the
+    # timed pass's step to give the fused launches' share of it
+    ev_check = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
 
     # counters of the split tag check (rows longer than one 2,048-page chunk)
     vws_n = kv.kv_verify_tags_workspace_bytes(wl.batch, st.block_table.shape[1])
     vws = torch.zeros(vws_n, dtype=torch.uint8, device=dev) if vws_n else None
 
-    def run_step(s, timed_slot=None, check=verify, stream=stream):
+    def run_step(s, timed_slot=None, check=verify, stream=stream, check_slot=None):
         abort = st.abort if check else None
         if check:
+            if check_slot is not None:
+                ev_check[check_slot][0].record(stream)
             kv.kv_verify_tags(st.pool_tags, st.block_table, st.expected_tags, seq_lens[s],
                               st.abort, stream=stream, workspace=vws)
+            if check_slot is not None:
+                ev_check[check_slot][1].record(stream)
         for layer in range(wl.num_layers):
             q, kn, vn = inputs[s][layer]
             if fused:
@@ -830,18 +838,27 @@ def main():
     base2 = args.warmup + args.steps
     torch.cuda.synchronize()
     for i in range(args.steps):
-        run_step(base2 + i, timed_slot=i if fused else i * wl.num_layers)
+        run_step(base2 + i, timed_slot=i if fused else i * wl.num_layers, check_slot=i)
     torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) / (wl.num_layers if fused else 1) for a, b in ev_attn]
-    attn_avg_ms = float(np.mean(attn_ms))
+    attn_events_ms = float(np.mean(attn_ms))
+    # median: a pair of events around one short kernel now and then also holds a
+    # stray delay of tens of microseconds
+    check_ms = float(np.median([a.elapsed_time(b) for a, b in ev_check])) if verify else 0.0
 
     by = [step_bytes(wl, wl.seq_lens_at(args.warmup + i), cache, verify)
           for i in range(args.steps)]
     by2 = [step_bytes(wl, wl.seq_lens_at(base2 + i), cache, verify) for i in range(args.steps)]
     total_bytes = sum(b["total"] for b in by)
     gbs = total_bytes / (elapsed_ms * 1e-3) / 1e9
-    attn_bytes = float(np.mean([b["attn_per_layer"] + (b["append_per_layer"] if fused else 0)
-                                for b in by2]))
+    if fused:
+        # the timed pass itself: its step, less the tag check's share, over the
+        # back-to-back layer launches (the kernels run with no gap between them)
+        attn_avg_ms = (ms_per_step - check_ms) / wl.num_layers
+        attn_bytes = float(np.mean([b["attn_per_layer"] + b["append_per_layer"] for b in by]))
+    else:
+        attn_avg_ms = attn_events_ms
+        attn_bytes = float(np.mean([b["attn_per_layer"] for b in by2]))
     attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     seq_steps = wl.batch * args.steps / (elapsed_ms * 1e-3)
     log(args, f"{ms_per_step:.3f} ms/step, {gbs:.0f} GB/s, attention call {attn_avg_ms*1e3:.1f} us "
@@ -943,6 +960,8 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(attn_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": int(attn_bytes),
+            "avg_launch_us_events_pass": round(attn_events_ms * 1e3, 2),
+            "tag_check_us": round(check_ms * 1e3, 2),
         },
         "cpu_baseline": cpu,
         "no_op_tracker": noop,
