@@ -26,8 +26,10 @@
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers, allocated and owned by the
- *     caller. The library allocates nothing, keeps no state and no handles,
- *     and is safe to call from several host threads.
+ *     caller. The library allocates nothing, keeps no handles and no state
+ *     beyond one exception (paged_decode_attn_append_noalloc's static device
+ *     scratch, one per GPU for the life of the process, and its address
+ *     cached per device), and is safe to call from several host threads.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously on it; nothing synchronises the host.
  *   - Arguments are validated before anything is enqueued. On invalid
