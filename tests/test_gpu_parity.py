@@ -696,3 +696,62 @@ def test_wave_mode_even_page_split_long_partitions(kv, cache):
     e2 = dict(e, kp=kp_b, vp=vp_b)
     helpers.check_attention(out_b.cpu().numpy(), _edge_oracle(e2, cache, lens), zero_rows=zero,
                             label=f"page split fused {cache}")
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_large_batches_at_the_kernel_limits(kv, cache):
+    """Thousands of short requests (GQA 8/1): 4,096, the largest batch the
+    persistent kernel takes (its per-request prefix fills the most LDS), and
+    4,097, one past it, where the shared kernel runs the same 16-token
+    partitions and the reduce covers 32,776 rows; then 20,000 requests in one
+    partition each. Ragged lengths from 1 to 96 tokens with empty and aborted
+    requests scattered through; every row against the oracle."""
+    hq, hkv = 8, 1
+    rng = np.random.default_rng(4097)
+    lens = rng.integers(1, 97, 4097)
+    lens[::511] = 0
+    lens = lens.tolist()
+    need = sum(max(1, -(-L // 16)) for L in lens)
+    e = _edge_state(kv, cache, hq, hkv, lens, pool_pages=need + 16)
+    abort = np.zeros(len(lens), np.uint8)
+    abort[7::613] = 1
+    for batch in (4096, 4097):
+        sub = dict(e, q=e["q"][:batch], bt=e["bt"][:batch], btt=e["btt"][:batch],
+                   lens=e["lens"][:batch])
+        ln = lens[:batch]
+        ab = abort[:batch]
+        assert _uses_persistent_kernel(batch, hkv, max(ln), 16) == (batch <= 4096)
+        zero = sorted({b for b, L in enumerate(ln) if L == 0} | set(np.flatnonzero(ab).tolist()))
+        want = _edge_oracle(sub, cache, ln, abort=ab)
+        got = _edge_run(kv, sub, cache, abort=ab, partition_tokens=16)
+        helpers.check_attention(got, want, zero_rows=zero, label=f"batch {batch} {cache} p16")
+    if cache == "bf16":
+        return
+    # 20,000 requests, one partition each (the shared kernel's grid of 20,000
+    # workgroups, no reduce), and the batched tag check over all of them
+    big = 20_000
+    lens2 = rng.integers(1, 49, big)
+    lens2[::997] = 0
+    lens2 = lens2.tolist()
+    need2 = sum(max(1, -(-L // 16)) for L in lens2)
+    e2 = _edge_state(kv, cache, hq, hkv, lens2, pool_pages=need2 + 16)
+    zero2 = [b for b, L in enumerate(lens2) if L == 0]
+    assert kv.paged_decode_attn_partition_tokens(big, hkv, max(lens2), 0) >= max(lens2)
+    want2 = _edge_oracle(e2, cache, lens2)
+    got2 = _edge_run(kv, e2, cache)
+    helpers.check_attention(got2, want2, zero_rows=zero2, label=f"batch {big} {cache}")
+    tags = rng.integers(0, 2 ** 32, need2 + 16, dtype=np.uint64).astype(np.uint32)
+    bt2 = e2["bt"]
+    exp = tags[np.clip(bt2, 0, None)]
+    stale = rng.choice(big, 5, replace=False)
+    for b in stale:
+        if lens2[b] > 0:
+            exp[b, 0] ^= 1
+    want_ab = paged.verify_tags(tags, bt2, exp, np.array(lens2, np.int32), 16)
+    ab = torch.full((big,), 0xA5, dtype=torch.uint8, device=DEV)
+    kv.kv_verify_tags(torch.from_numpy(tags.view(np.int32)).to(DEV), e2["btt"],
+                      torch.from_numpy(exp.view(np.int32)).to(DEV),
+                      torch.from_numpy(np.array(lens2, np.int32)).to(DEV), ab)
+    torch.cuda.synchronize()
+    assert np.array_equal(ab.cpu().numpy(), want_ab)
+    assert sorted(np.flatnonzero(want_ab).tolist()) == sorted(int(b) for b in stale if lens2[b] > 0)
