@@ -5,12 +5,18 @@ KV-head group) at a time from the seeded generator.
 For each sample: the request's pool codes (its pages, read back from the GPU
 and mapped through the documented tile layout) are compared bit-exactly with
 the oracle's codes, then the attention output of that request is compared
-within the tolerance. Abort masks are compared whole.
+within the tolerance. Abort masks are compared whole. One layer of the
+headline batch and one of the skewed batch are also checked whole: every
+output against the oracle over the pools the launch left.
 """
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import synth
 from oracle import e4m3, paged
@@ -136,3 +142,59 @@ def test_skewed_16req_split_k_and_churn(kv):
     ok = [b for b in range(wl.batch) if b not in stale]
     for b, g in [(ok[0], 0), (ok[-1], 4)]:
         _check_group(st, 0, b, g, 1, inputs1[0][0], outs1[0], "skewed16 step 1")
+
+
+def _threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _logical_threaded(tiles, kind):
+    """tiles_to_logical over a whole layer's pool, in page chunks on threads."""
+    out = np.empty(tiles.shape[:-1] + (16, 128), tiles.dtype)
+    bounds = np.linspace(0, tiles.shape[0], 65).astype(np.int64)
+
+    def conv(i):
+        a, b = bounds[i], bounds[i + 1]
+        out[a:b] = helpers.tiles_to_logical(tiles[a:b], kind, "fp8")
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(conv, range(64)))
+    return out
+
+
+@pytest.mark.parametrize("config", ["batch64", "skewed16"])
+def test_every_output_of_a_full_size_layer(kv, config):
+    """Every output of one full-size layer, not a sample: the headline batch
+    (64 requests, one partition each, as benchmarked) and the skewed batch
+    (512-token partitions in the persistent kernel, then the reduce), each as
+    one fused append + attention launch after the tag check. The whole layer's
+    pools are read back after the launch, and the oracle attends every
+    request over them (the same dequantized inputs, the token appended by the
+    launch included; one request per thread, BLAS on one thread each); each
+    (request, query head) row must meet the tolerance. The appended token's
+    codes are the oracle's encoding of its bf16 row."""
+    make = {"batch64": synth.batch64_ctx8k, "skewed16": synth.skewed_16req}[config]
+    wl = make(max_steps=1)
+    st = DeviceState(wl, kv, cache="fp8", device=DEV, layers=[0])
+    pt = 0 if config == "batch64" else wl.partition_tokens
+    ab, outs, inputs = gpu_step(st, 0, partition_tokens=pt, fused=True)
+    assert not ab.any()
+    q_bits, kn, vn = inputs[0]
+    kl = _logical_threaded(st.k_pool[0].cpu().numpy(), "k")
+    vl = _logical_threaded(st.v_pool[0].cpu().numpy(), "v")
+    L = wl.seq_lens_at(0).astype(np.int32)
+    ks, vs = st.k_scale_host[0], st.v_scale_host[0]
+    # the token each request appended this step (position L - 1)
+    for b in range(wl.batch):
+        t = int(L[b]) - 1
+        page = int(wl.block_table[b, t // 16])
+        assert np.array_equal(kl[page, :, t % 16], e4m3.quantize(kn[b], ks[:, None])), f"K row {b}"
+        assert np.array_equal(vl[page, :, t % 16], e4m3.quantize(vn[b], vs[:, None])), f"V row {b}"
+    sm = sm_scale_for(wl)
+    with threadpool_limits(1), ThreadPoolExecutor(_threads()) as ex:
+        want = np.stack(list(ex.map(
+            lambda b: paged.decode_attn_request(b, q_bits, kl, vl, ks, vs, wl.block_table, L,
+                                                sm, "fp8"), range(wl.batch))))
+    rel, mx = helpers.check_attention(outs[0], want, label=f"{config} every output")
+    say(f"{config}: all {wl.batch} x {wl.num_q_heads} rows of layer 0, worst rel_l2={rel:.2e} "
+        f"max_abs={mx:.2e}")
