@@ -148,53 +148,60 @@ def _threads():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def _logical_threaded(tiles, kind):
+def _logical_threaded(tiles, kind, cache):
     """tiles_to_logical over a whole layer's pool, in page chunks on threads."""
     out = np.empty(tiles.shape[:-1] + (16, 128), tiles.dtype)
     bounds = np.linspace(0, tiles.shape[0], 65).astype(np.int64)
 
     def conv(i):
         a, b = bounds[i], bounds[i + 1]
-        out[a:b] = helpers.tiles_to_logical(tiles[a:b], kind, "fp8")
+        out[a:b] = helpers.tiles_to_logical(tiles[a:b], kind, cache)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(conv, range(64)))
     return out
 
 
-@pytest.mark.parametrize("config", ["batch64", "skewed16"])
-def test_every_output_of_a_full_size_layer(kv, config):
+@pytest.mark.parametrize("config,cache", [("batch64", "fp8"), ("skewed16", "fp8"),
+                                          ("uniform32", "fp8"), ("uniform32", "bf16")])
+def test_every_output_of_a_full_size_layer(kv, config, cache):
     """Every output of one full-size layer, not a sample: the headline batch
-    (64 requests, one partition each, as benchmarked) and the skewed batch
-    (512-token partitions in the persistent kernel, then the reduce), each as
-    one fused append + attention launch after the tag check. The whole layer's
-    pools are read back after the launch, and the oracle attends every
-    request over them (the same dequantized inputs, the token appended by the
-    launch included; one request per thread, BLAS on one thread each); each
+    (64 requests, one partition each, as benchmarked), the skewed batch
+    (512-token partitions in the persistent kernel, then the reduce) and the
+    32-request batch with either cache (8-wave workgroups), each as one fused
+    append + attention launch after the tag check. The whole layer's pools
+    are read back after the launch, and the oracle attends every request over
+    them (the same dequantized inputs, the token appended by the launch
+    included; one request per thread, BLAS on one thread each); each
     (request, query head) row must meet the tolerance. The appended token's
-    codes are the oracle's encoding of its bf16 row."""
-    make = {"batch64": synth.batch64_ctx8k, "skewed16": synth.skewed_16req}[config]
+    codes are the oracle's encoding of its bf16 row (BF16 cache: the row)."""
+    make = {"batch64": synth.batch64_ctx8k, "skewed16": synth.skewed_16req,
+            "uniform32": synth.uniform_32req}[config]
     wl = make(max_steps=1)
-    st = DeviceState(wl, kv, cache="fp8", device=DEV, layers=[0])
-    pt = 0 if config == "batch64" else wl.partition_tokens
+    st = DeviceState(wl, kv, cache=cache, device=DEV, layers=[0])
+    pt = wl.partition_tokens if config == "skewed16" else 0
     ab, outs, inputs = gpu_step(st, 0, partition_tokens=pt, fused=True)
     assert not ab.any()
     q_bits, kn, vn = inputs[0]
-    kl = _logical_threaded(st.k_pool[0].cpu().numpy(), "k")
-    vl = _logical_threaded(st.v_pool[0].cpu().numpy(), "v")
+    kt, vt = st.k_pool[0].cpu().numpy(), st.v_pool[0].cpu().numpy()
+    if cache == "bf16":
+        kt, vt = kt.view(np.uint16), vt.view(np.uint16)
+    kl, vl = _logical_threaded(kt, "k", cache), _logical_threaded(vt, "v", cache)
     L = wl.seq_lens_at(0).astype(np.int32)
     ks, vs = st.k_scale_host[0], st.v_scale_host[0]
     # the token each request appended this step (position L - 1)
     for b in range(wl.batch):
         t = int(L[b]) - 1
         page = int(wl.block_table[b, t // 16])
-        assert np.array_equal(kl[page, :, t % 16], e4m3.quantize(kn[b], ks[:, None])), f"K row {b}"
-        assert np.array_equal(vl[page, :, t % 16], e4m3.quantize(vn[b], vs[:, None])), f"V row {b}"
+        want_k = e4m3.quantize(kn[b], ks[:, None]) if cache == "fp8" else kn[b]
+        want_v = e4m3.quantize(vn[b], vs[:, None]) if cache == "fp8" else vn[b]
+        assert np.array_equal(kl[page, :, t % 16], want_k), f"K row {b}"
+        assert np.array_equal(vl[page, :, t % 16], want_v), f"V row {b}"
     sm = sm_scale_for(wl)
     with threadpool_limits(1), ThreadPoolExecutor(_threads()) as ex:
         want = np.stack(list(ex.map(
             lambda b: paged.decode_attn_request(b, q_bits, kl, vl, ks, vs, wl.block_table, L,
-                                                sm, "fp8"), range(wl.batch))))
-    rel, mx = helpers.check_attention(outs[0], want, label=f"{config} every output")
-    say(f"{config}: all {wl.batch} x {wl.num_q_heads} rows of layer 0, worst rel_l2={rel:.2e} "
+                                                sm, cache), range(wl.batch))))
+    rel, mx = helpers.check_attention(outs[0], want, label=f"{config} {cache} every output")
+    say(f"{config} {cache}: all {wl.batch} x {wl.num_q_heads} rows of layer 0, worst rel_l2={rel:.2e} "
         f"max_abs={mx:.2e}")
