@@ -6,8 +6,9 @@ For each sample: the request's pool codes (its pages, read back from the GPU
 and mapped through the documented tile layout) are compared bit-exactly with
 the oracle's codes, then the attention output of that request is compared
 within the tolerance. Abort masks are compared whole. One layer of the
-headline batch and one of the skewed batch are also checked whole: every
-output against the oracle over the pools the launch left.
+headline, skewed and 32-request batches (both caches) are also checked
+whole: every code of the pools the launch left, and every output against the
+oracle over those pools.
 """
 
 import os
@@ -173,8 +174,10 @@ def test_every_output_of_a_full_size_layer(kv, config, cache):
     are read back after the launch, and the oracle attends every request over
     them (the same dequantized inputs, the token appended by the launch
     included; one request per thread, BLAS on one thread each); each
-    (request, query head) row must meet the tolerance. The appended token's
-    codes are the oracle's encoding of its bf16 row (BF16 cache: the row)."""
+    (request, query head) row must meet the tolerance. Every code of every
+    request's tokens, the initial fill and the appended token, is the oracle's
+    encoding of its seeded bf16 row (BF16 cache: the row itself), so the pages
+    the attention read are checked whole too."""
     make = {"batch64": synth.batch64_ctx8k, "skewed16": synth.skewed_16req,
             "uniform32": synth.uniform_32req}[config]
     wl = make(max_steps=1)
@@ -197,6 +200,24 @@ def test_every_output_of_a_full_size_layer(kv, config, cache):
         want_v = e4m3.quantize(vn[b], vs[:, None]) if cache == "fp8" else vn[b]
         assert np.array_equal(kl[page, :, t % 16], want_k), f"K row {b}"
         assert np.array_equal(vl[page, :, t % 16], want_v), f"V row {b}"
+
+    # every code of every request's tokens (the initial fill and the appended
+    # token) against the oracle's encoding of the seeded bf16 rows
+    def codes_ok(bg):
+        b, g = bg
+        n = int(L[b])
+        ids = wl.block_table[b, :-(-n // 16)]
+        for kind, pool, sc in (("k", kl, ks), ("v", vl, vs)):
+            bits = wl.kv_bits_head(0, kind, b, g, 0, n)
+            want_c = e4m3.quantize(bits, sc[g]) if cache == "fp8" else bits
+            if not np.array_equal(pool[ids, g].reshape(-1, 128)[:n], want_c):
+                return (b, g, kind)
+        return None
+
+    groups = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    with threadpool_limits(1), ThreadPoolExecutor(_threads()) as ex:
+        bad = [r for r in ex.map(codes_ok, groups) if r is not None]
+    assert not bad, f"{config} {cache}: codes differ for (request, head, K|V) {bad[:8]}"
     sm = sm_scale_for(wl)
     with threadpool_limits(1), ThreadPoolExecutor(_threads()) as ex:
         want = np.stack(list(ex.map(
