@@ -146,27 +146,40 @@ def test_one_hot_inputs_read_every_code_position(kv, fmt, m):
             f"{np.argwhere(got != want)[:4].tolist()}"
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("m", [1, 16])
-def test_gemv_full_size_sampled_rows(kv, fmt, m):
-    """8192 x 8192 weights, 1 token (the small-batch kernel) and 16 tokens,
-    in the launch configurations the benchmark times; rows sampled for the
-    oracle (codes checked for them)."""
-    n = k = 8192
-    rng = np.random.default_rng(7 + fmt)
+def _full_size_check(kv, fmt, m, n, k, seed):
+    """Every code, scale and output of an n x k product at m tokens, in the
+    launch configuration the benchmark times, against the oracle."""
+    rng = np.random.default_rng(seed)
     wb = _weights(rng, n, k)
     packed, scales = _pack(kv, wb, fmt)
     xb = (rng.normal(0, 1, size=(m, k)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     y = torch.zeros((m, n), dtype=torch.float32, device=DEV)
     kv.wq_gemv(torch.from_numpy(xb.view(np.int16)).to(DEV), packed, scales, y, n, fmt)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 17, 4095, 8191] + rng.integers(0, n, 11).tolist())
-    q_o, s_o = weights.quantize_int4(wb[rows]) if fmt == 0 else weights.quantize_fp8(wb[rows])
+    q_o, s_o = weights.quantize_int4(wb) if fmt == 0 else weights.quantize_fp8(wb)
+    assert np.array_equal(_unpack(packed.cpu().numpy(), n, k, fmt), q_o), "codes"
+    got_s = scales.cpu().numpy().reshape(n // 16, k // G, 16).transpose(0, 2, 1).reshape(n, k // G)
+    assert np.array_equal(got_s.view(np.uint32), s_o.view(np.uint32)), "scales"
+    del wb, packed, scales
     wd = weights.dequant_int4(q_o, s_o) if fmt == 0 else weights.dequant_fp8(q_o, s_o)
     want = weights.gemv(xb, wd)
-    got = y.cpu().numpy()[:, rows].astype(np.float64)
-    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
-    assert rel <= REL_TOL
-    allq = _unpack(packed.cpu().numpy(), n, k, fmt)
-    assert np.array_equal(allq[rows], q_o)
-    say(f"gemv fmt {fmt} 8192x8192 m={m}: sampled rows rel_l2 {rel:.2e}")
+    got = y.cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
+    assert np.all(rel <= REL_TOL), rel
+    say(f"gemv fmt {fmt} {n}x{k} m={m}: every code, scale and output; worst token rel_l2 "
+        f"{rel.max():.2e}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("m", [1, 16])
+def test_gemv_full_size_every_output(kv, fmt, m):
+    """8192 x 8192 weights, 1 token (the small-batch kernel) and 16 tokens
+    (the chunked kernel): every code and scale bit for bit, every output
+    within the tolerance (per token)."""
+    _full_size_check(kv, fmt, m, 8192, 8192, 7 + fmt)
+
+
+def test_gemv_largest_product_every_output(kv):
+    """The 28672 x 8192 INT4 product at one token, the roofline launch: every
+    code, scale and output against the oracle."""
+    _full_size_check(kv, 0, 1, 28672, 8192, 11)
