@@ -226,3 +226,58 @@ def test_every_output_of_a_full_size_layer(kv, config, cache):
     rel, mx = helpers.check_attention(outs[0], want, label=f"{config} {cache} every output")
     say(f"{config} {cache}: all {wl.batch} x {wl.num_q_heads} rows of layer 0, worst rel_l2={rel:.2e} "
         f"max_abs={mx:.2e}")
+
+
+def test_every_output_after_churn(kv):
+    """The skewed batch's second step after the churn (10% of pages freed
+    and reallocated with tag bumps; two requests keep stale mappings), as one
+    fused launch after the tag check: the mask is exactly the two stale
+    requests, their rows are zero and their append slots untouched, every
+    other request's appended codes are the oracle's, and every output of the
+    others is within the tolerance of the oracle over the pools the launch
+    left."""
+    wl = synth.skewed_16req(max_steps=2)
+    stale = wl.notes["churn_stale"]
+    st = DeviceState(wl, kv, cache="fp8", device=DEV, layers=[0])
+    pt = wl.partition_tokens
+    ab0, _, _ = gpu_step(st, 0, partition_tokens=pt, fused=True)
+    assert not ab0.any()
+    wl.notes["churn_step"] = 1
+    wl.apply_churn(np.random.default_rng(wl.notes["churn_rng_seed"]), 0.10, stale)
+    st.upload_tags()
+    L = wl.seq_lens_at(1).astype(np.int32)
+    # the stale requests' target slots before the step
+    before = {}
+    for b in stale:
+        t = int(L[b]) - 1
+        page = int(wl.block_table[b, t // 16])
+        before[b] = (page, st.k_pool[0][page].cpu().numpy().copy(),
+                     st.v_pool[0][page].cpu().numpy().copy())
+    ab, outs, inputs = gpu_step(st, 1, partition_tokens=pt, fused=True)
+    assert sorted(np.flatnonzero(ab).tolist()) == sorted(stale)
+    for b in stale:
+        page, k0, v0 = before[b]
+        assert np.array_equal(st.k_pool[0][page].cpu().numpy(), k0), f"stale {b} wrote K"
+        assert np.array_equal(st.v_pool[0][page].cpu().numpy(), v0), f"stale {b} wrote V"
+    q_bits, kn, vn = inputs[0]
+    kl = _logical_threaded(st.k_pool[0].cpu().numpy(), "k", "fp8")
+    vl = _logical_threaded(st.v_pool[0].cpu().numpy(), "v", "fp8")
+    ks, vs = st.k_scale_host[0], st.v_scale_host[0]
+    for b in range(wl.batch):
+        if b in stale:
+            continue
+        t = int(L[b]) - 1
+        page = int(wl.block_table[b, t // 16])
+        assert np.array_equal(kl[page, :, t % 16], e4m3.quantize(kn[b], ks[:, None])), f"K row {b}"
+        assert np.array_equal(vl[page, :, t % 16], e4m3.quantize(vn[b], vs[:, None])), f"V row {b}"
+    abort = np.zeros(wl.batch, np.uint8)
+    abort[list(stale)] = 1
+    sm = sm_scale_for(wl)
+    with threadpool_limits(1), ThreadPoolExecutor(_threads()) as ex:
+        want = np.stack(list(ex.map(
+            lambda b: paged.decode_attn_request(b, q_bits, kl, vl, ks, vs, wl.block_table, L,
+                                                sm, "fp8", abort), range(wl.batch))))
+    rel, mx = helpers.check_attention(outs[0], want, zero_rows=list(stale),
+                                      label="skewed16 after churn, every output")
+    say(f"skewed16 after churn: stale {sorted(stale)} zero and unwritten; the other "
+        f"{wl.batch - len(stale)} x {wl.num_q_heads} rows worst rel_l2={rel:.2e} max_abs={mx:.2e}")
