@@ -163,13 +163,15 @@ def _logical_threaded(tiles, kind, cache):
     return out
 
 
-@pytest.mark.parametrize("config,cache", [("batch64", "fp8"), ("skewed16", "fp8"),
+@pytest.mark.parametrize("config,cache", [("batch64", "fp8"), ("batch64", "bf16"),
+                                          ("skewed16", "fp8"), ("skewed16", "bf16"),
                                           ("uniform32", "fp8"), ("uniform32", "bf16")])
 def test_every_output_of_a_full_size_layer(kv, config, cache):
-    """Every output of one full-size layer, not a sample: the headline batch
-    (64 requests, one partition each, as benchmarked), the skewed batch
-    (512-token partitions in the persistent kernel, then the reduce) and the
-    32-request batch with either cache (8-wave workgroups), each as one fused
+    """Every output of one full-size layer, not a sample, with either cache:
+    the headline batch (64 requests, one partition each in 4-wave
+    workgroups, as benchmarked), the skewed batch (512-token partitions in
+    the persistent kernel, then the reduce) and the 32-request batch (8-wave
+    workgroups), each as one fused
     append + attention launch after the tag check. The whole layer's pools
     are read back after the launch, and the oracle attends every request over
     them (the same dequantized inputs, the token appended by the launch
