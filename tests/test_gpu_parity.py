@@ -755,3 +755,106 @@ def test_large_batches_at_the_kernel_limits(kv, cache):
     torch.cuda.synchronize()
     assert np.array_equal(ab.cpu().numpy(), want_ab)
     assert sorted(np.flatnonzero(want_ab).tolist()) == sorted(int(b) for b in stale if lens2[b] > 0)
+
+
+@pytest.mark.parametrize("cache", ["fp8", "bf16"])
+def test_pools_larger_than_4gib(kv, cache):
+    """A 330,000-page pool (5.4 GB per K or V array with FP8 tiles, 10.8 GB
+    with BF16) whose requests live in its top 30,000 pages, so every tile
+    offset lies beyond 2^32 bytes (one request at the bottom for contrast):
+    the prompts calibrated and ingested there, then one fused append +
+    attention step in the shared kernel (automatic split) and in the
+    persistent kernel (64-token partitions), after the tag check. Scales,
+    every code of every request and every output against the oracle."""
+    from oracle import ingest
+    hq, hkv, num_pages = 64, 8, 330_000
+    rng = np.random.default_rng(4242)
+    lens = [1, 17, 1000, 4096, 9000, 20000]
+    batch = len(lens)
+    need = [-(-L // 16) for L in lens]
+    top = rng.permutation(np.arange(num_pages - 30_000, num_pages))
+    ids, off = [np.array([3])], 0
+    for n in need[1:]:
+        ids.append(top[off:off + n])
+        off += n
+    bt = np.full((batch, max(need)), -1, np.int32)
+    for b in range(batch):
+        bt[b, :need[b]] = ids[b]
+    assert bt[1:].max() >= num_pages - 30_000 and (num_pages - 30_000) * hkv * 2048 > 2 ** 32
+    prompt = [L - 1 for L in lens]                      # the last token comes with the step
+    rows_k = synth._f32_to_bf16_bits(rng.normal(0, 1, (sum(prompt), hkv, 128)).astype(np.float32))
+    rows_v = synth._f32_to_bf16_bits(rng.normal(0, 0.5, (sum(prompt), hkv, 128)).astype(np.float32))
+    start = np.concatenate([[0], np.cumsum(prompt)[:-1]]).astype(np.int32)
+    new_k = synth._f32_to_bf16_bits(rng.normal(0, 1, (batch, hkv, 128)).astype(np.float32))
+    new_v = synth._f32_to_bf16_bits(rng.normal(0, 0.5, (batch, hkv, 128)).astype(np.float32))
+    q = synth._f32_to_bf16_bits(rng.normal(0, 1, (batch, hq, 128)).astype(np.float32))
+    fp8 = cache == "fp8"
+    cd = kv.KV_CACHE_FP8_E4M3 if fp8 else kv.KV_CACHE_BF16
+    dt = torch.uint8 if fp8 else torch.int16
+    fill = 0x7F if fp8 else 0x7FC0                      # NaN everywhere no request writes
+    btt = torch.from_numpy(bt).to(DEV)
+    tags = rng.integers(0, 2 ** 32, num_pages, dtype=np.uint64).astype(np.uint32)
+    exp = tags[np.clip(bt, 0, None)]
+    d_tags = torch.from_numpy(tags.view(np.int32)).to(DEV)
+    d_exp = torch.from_numpy(exp.view(np.int32)).to(DEV)
+    d_lens = torch.from_numpy(np.array(lens, np.int32)).to(DEV)
+    for pt in (0, 64):
+        kp = torch.full((num_pages, hkv, 2048), fill, dtype=dt, device=DEV)
+        vp = torch.full((num_pages, hkv, 2048), fill, dtype=dt, device=DEV)
+        ks = torch.ones(hkv, dtype=torch.float32, device=DEV)
+        vs = torch.ones(hkv, dtype=torch.float32, device=DEV)
+        kv.ingest_layer(torch.from_numpy(rows_k.view(np.int16)).to(DEV),
+                        torch.from_numpy(rows_v.view(np.int16)).to(DEV),
+                        torch.from_numpy(start).to(DEV),
+                        torch.from_numpy(np.array(prompt, np.int32)).to(DEV), btt, kp, vp,
+                        max(lens), ks if fp8 else None, vs if fp8 else None, cache_dtype=cd)
+        ab = torch.full((batch,), 0xA5, dtype=torch.uint8, device=DEV)
+        kv.kv_verify_tags(d_tags, btt, d_exp, d_lens, ab)
+        out = torch.full((batch, hq, 128), float("nan"), device=DEV)
+        n = kv.paged_decode_attn_workspace_bytes(batch, hq, hkv, max(lens), pt, cache_dtype=cd)
+        ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
+        kv.paged_decode_attn_append(torch.from_numpy(q.view(np.int16)).to(DEV),
+                                    torch.from_numpy(new_k.view(np.int16)).to(DEV),
+                                    torch.from_numpy(new_v.view(np.int16)).to(DEV), kp, vp,
+                                    ks if fp8 else None, vs if fp8 else None, btt, d_lens,
+                                    max(lens), out, 0.0883883, workspace=ws, abort=ab,
+                                    partition_tokens=pt, cache_dtype=cd)
+        torch.cuda.synchronize()
+        assert not ab.any().item()
+        used = np.concatenate(ids)
+        sel = torch.from_numpy(used.astype(np.int64)).to(DEV)
+        kt, vt = kp[sel].cpu().numpy(), vp[sel].cpu().numpy()
+        del kp, vp
+        torch.cuda.empty_cache()
+        if not fp8:
+            kt, vt = kt.view(np.uint16), vt.view(np.uint16)
+        kl, vl = helpers.tiles_to_logical(kt, "k", cache), helpers.tiles_to_logical(vt, "v", cache)
+        if fp8:
+            ks_o = ingest.scales_from_amax(ingest.amax_finite(rows_k))
+            vs_o = ingest.scales_from_amax(ingest.amax_finite(rows_v))
+            assert np.array_equal(ks.cpu().numpy().view(np.uint32), ks_o.view(np.uint32))
+            assert np.array_equal(vs.cpu().numpy().view(np.uint32), vs_o.view(np.uint32))
+        else:
+            ks_o = vs_o = np.ones(hkv, np.float32)
+        # the compact pool: request b's pages in order, its table remapped
+        bt_c = np.full_like(bt, -1)
+        pos = 0
+        for b in range(batch):
+            bt_c[b, :need[b]] = np.arange(pos, pos + need[b])
+            pos += need[b]
+            for pool, rows, new, sc in ((kl, rows_k, new_k, ks_o), (vl, rows_v, new_v, vs_o)):
+                toks = np.concatenate([rows[start[b]:start[b] + prompt[b]], new[b][None]])
+                want = e4m3.quantize(toks, sc[None, :, None]) if fp8 else toks
+                got = pool[bt_c[b, :need[b]]].transpose(0, 2, 1, 3).reshape(-1, hkv, 128)
+                assert np.array_equal(got[:lens[b]], want), f"{cache} p{pt}: codes of request {b}"
+                # past the end: the ingest's zeros where it wrote the last page; the
+                # fill where only the appended token reached it
+                tail = 0 if -(-prompt[b] // 16) == need[b] else fill
+                assert np.all(got[lens[b]:] == tail), \
+                    f"{cache} p{pt}: tail of request {b}"
+        want = paged.decode_attn(q, kl, vl, ks_o, vs_o, bt_c, np.array(lens, np.int32),
+                                 0.0883883, cache)
+        rel, mx = helpers.check_attention(out.cpu().numpy(), want,
+                                          label=f"pool beyond 4 GiB {cache} p{pt}")
+        say(f"pool of {num_pages} pages ({cache}, partitions {pt or 'auto'}): codes exact, "
+            f"worst row rel_l2={rel:.2e}")
