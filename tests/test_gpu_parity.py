@@ -858,3 +858,89 @@ def test_pools_larger_than_4gib(kv, cache):
                                           label=f"pool beyond 4 GiB {cache} p{pt}")
         say(f"pool of {num_pages} pages ({cache}, partitions {pt or 'auto'}): codes exact, "
             f"worst row rel_l2={rel:.2e}")
+
+
+def test_one_million_token_request(kv):
+    """One request of 1,000,000 tokens (62,500 pages per KV head, 1 GB per
+    FP8 array), filled through the bulk append: the tag check splits its row
+    over 31 workgroups (all matching -> 0; its last page's expected tag wrong
+    -> 1 and an all-zero output), then one fused append + attention step in
+    the shared kernel (62 automatic partitions of 16,384 tokens) and in the
+    persistent kernel (1,954 partitions of 512). Each KV head's 8 query
+    heads against the oracle over that head's codes as the launch left them;
+    the appended token's codes are the oracle's."""
+    hq, hkv, L = 64, 8, 1_000_000
+    npg = -(-L // 16)
+    num_pages = npg + 100
+    rng = np.random.default_rng(1_000_000)
+    bt = rng.permutation(num_pages)[:npg].astype(np.int32)[None]
+    btt = torch.from_numpy(bt).to(DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    kp = torch.zeros((num_pages, hkv, 2048), dtype=torch.uint8, device=DEV)
+    vp = torch.zeros_like(kp)
+    k_rows = (torch.randn((L - 1, hkv, 128), generator=gen, device=DEV)).to(torch.bfloat16)
+    v_rows = (torch.randn((L - 1, hkv, 128), generator=gen, device=DEV) * 0.5).to(torch.bfloat16)
+    ks = (k_rows.abs().amax(dim=(0, 2)).float() / 448.0).contiguous()
+    vs = (v_rows.abs().amax(dim=(0, 2)).float() / 448.0).contiguous()
+    chunk = 1 << 16
+    for t0 in range(0, L - 1, chunk):
+        t1 = min(L - 1, t0 + chunk)
+        pos = torch.arange(t0, t1, dtype=torch.int32, device=DEV)
+        kv.kv_append_quant(k_rows[t0:t1].view(torch.int16), v_rows[t0:t1].view(torch.int16),
+                           torch.zeros_like(pos), pos, btt, ks, vs, kp, vp)
+    del k_rows, v_rows
+    new_k = synth._f32_to_bf16_bits(rng.normal(0, 1, (1, hkv, 128)).astype(np.float32))
+    new_v = synth._f32_to_bf16_bits(rng.normal(0, 0.5, (1, hkv, 128)).astype(np.float32))
+    q = synth._f32_to_bf16_bits(rng.normal(0, 1, (1, hq, 128)).astype(np.float32))
+    tags = rng.integers(0, 2 ** 32, num_pages, dtype=np.uint64).astype(np.uint32)
+    exp = tags[bt].copy()
+    d_tags = torch.from_numpy(tags.view(np.int32)).to(DEV)
+    d_lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+    ws_v = torch.zeros(kv.kv_verify_tags_workspace_bytes(1, npg), dtype=torch.uint8, device=DEV)
+    bad = exp.copy()
+    bad[0, npg - 1] ^= 1
+    ab = torch.full((1,), 0xA5, dtype=torch.uint8, device=DEV)
+    kv.kv_verify_tags(d_tags, btt, torch.from_numpy(bad.view(np.int32)).to(DEV), d_lens, ab,
+                      workspace=ws_v)
+    torch.cuda.synchronize()
+    assert ab.item() == 1 and int(ws_v.count_nonzero()) == 0
+    ks_h, vs_h = ks.cpu().numpy(), vs.cpu().numpy()
+    qt = torch.from_numpy(q.view(np.int16)).to(DEV)
+    knt = torch.from_numpy(new_k.view(np.int16)).to(DEV)
+    vnt = torch.from_numpy(new_v.view(np.int16)).to(DEV)
+    out = torch.full((1, hq, 128), float("nan"), device=DEV)
+    kp0, vp0 = kp.clone(), vp.clone()          # the aborted step must leave the pools as they are
+    ws = torch.zeros(kv.paged_decode_attn_workspace_bytes(1, hq, hkv, L, 512), dtype=torch.uint8,
+                     device=DEV)
+    kv.paged_decode_attn_append(qt, knt, vnt, kp, vp, ks, vs, btt, d_lens, L, out, 0.0883883,
+                                workspace=ws, abort=ab, partition_tokens=512)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0).item() and torch.equal(kp, kp0) and torch.equal(vp, vp0)
+    del kp0, vp0
+    kv.kv_verify_tags(d_tags, btt, torch.from_numpy(exp.view(np.int32)).to(DEV), d_lens, ab,
+                      workspace=ws_v)
+    torch.cuda.synchronize()
+    assert ab.item() == 0
+    sel = torch.from_numpy(bt[0].astype(np.int64)).to(DEV)
+    for pt in (0, 512):
+        assert kv.paged_decode_attn_partition_tokens(1, hkv, L, pt) == (16384 if pt == 0 else 512)
+        assert _uses_persistent_kernel(1, hkv, L, 16384 if pt == 0 else 512) == (pt == 512)
+        out = torch.full((1, hq, 128), float("nan"), device=DEV)
+        kv.paged_decode_attn_append(qt, knt, vnt, kp, vp, ks, vs, btt, d_lens, L, out, 0.0883883,
+                                    workspace=ws, abort=ab, partition_tokens=pt)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        worst = 0.0
+        for g in range(hkv):
+            kc = helpers.tiles_to_logical(kp[sel, g].cpu().numpy(), "k", "fp8").reshape(-1, 128)[:L]
+            vc = helpers.tiles_to_logical(vp[sel, g].cpu().numpy(), "v", "fp8").reshape(-1, 128)[:L]
+            assert np.array_equal(kc[L - 1], e4m3.quantize(new_k[0, g], ks_h[g]))
+            assert np.array_equal(vc[L - 1], e4m3.quantize(new_v[0, g], vs_h[g]))
+            want = paged.attend_request(q[0, g * 8:(g + 1) * 8],
+                                        e4m3.dequantize(kc, ks_h[g])[None],
+                                        e4m3.dequantize(vc, vs_h[g])[None], 0.0883883)
+            rel, _ = helpers.check_attention(got[:, g * 8:(g + 1) * 8], want[None],
+                                             label=f"1M tokens p{pt} head {g}")
+            worst = max(worst, rel)
+        say(f"1,000,000-token request, partitions {pt or 'auto'}: worst row rel_l2={worst:.2e}")
