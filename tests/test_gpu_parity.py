@@ -944,3 +944,73 @@ def test_one_million_token_request(kv):
                                              label=f"1M tokens p{pt} head {g}")
             worst = max(worst, rel)
         say(f"1,000,000-token request, partitions {pt or 'auto'}: worst row rel_l2={worst:.2e}")
+
+
+def test_two_streams_at_once_equal_each_alone(kv):
+    """The library keeps no state between calls beyond the caller's buffers:
+    two batches decoded at the same time on two side streams (default
+    priority), each with its own tag-check counters and split-K workspace,
+    one through the persistent kernel and one through the shared kernel,
+    give bit for bit what each gives alone on the default stream; three
+    rounds, so the counters come back to zero in between."""
+    rng = np.random.default_rng(31)
+    jobs = []
+    for lens, hq, pt in (((rng.integers(1, 3000, 40)).tolist(), 64, 64),
+                         ((rng.integers(1, 9000, 6)).tolist(), 32, 0)):
+        hkv = 8
+        need = sum(max(1, -(-L // 16)) for L in lens)
+        e = _edge_state(kv, "fp8", hq, hkv, lens, pool_pages=need + 8)
+        batch = len(lens)
+        width = max(3000, e["bt"].shape[1])              # rows wider than one check chunk
+        bt = np.full((batch, width), -1, np.int32)
+        bt[:, :e["bt"].shape[1]] = e["bt"]
+        tags = rng.integers(0, 2 ** 32, need + 8, dtype=np.uint64).astype(np.uint32)
+        exp = tags[np.clip(bt, 0, None)]
+        msl = max(lens)
+        n = kv.paged_decode_attn_workspace_bytes(batch, hq, hkv, msl, pt)
+        jobs.append(dict(
+            e=e, hq=hq, pt=pt, msl=msl, batch=batch,
+            btt=torch.from_numpy(bt).to(DEV), tags=torch.from_numpy(tags.view(np.int32)).to(DEV),
+            exp=torch.from_numpy(exp.view(np.int32)).to(DEV),
+            lens=torch.from_numpy(np.array(lens, np.int32)).to(DEV),
+            q=torch.from_numpy(e["q"].view(np.int16)).to(DEV),
+            ws=torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV),
+            vws=torch.zeros(kv.kv_verify_tags_workspace_bytes(batch, width), dtype=torch.uint8,
+                            device=DEV),
+            ab=torch.zeros(batch, dtype=torch.uint8, device=DEV),
+            out=torch.zeros((batch, hq, 128), dtype=torch.float32, device=DEV)))
+    assert _uses_persistent_kernel(jobs[0]["batch"], 8, jobs[0]["msl"], 64)
+    assert not _uses_persistent_kernel(jobs[1]["batch"], 8, jobs[1]["msl"],
+                                       kv.paged_decode_attn_partition_tokens(
+                                           jobs[1]["batch"], 8, jobs[1]["msl"], 0))
+
+    def run(j, stream=None):
+        kv.kv_verify_tags(j["tags"], j["btt"], j["exp"], j["lens"], j["ab"], workspace=j["vws"],
+                          stream=stream)
+        kv.paged_decode_attn(j["q"], j["e"]["kp"], j["e"]["vp"], j["e"]["kst"], j["e"]["vst"],
+                             j["btt"], j["lens"], j["msl"], j["out"], 0.0883883,
+                             workspace=j["ws"], abort=j["ab"], partition_tokens=j["pt"],
+                             stream=stream)
+
+    alone = []
+    for j in jobs:
+        run(j)
+        torch.cuda.synchronize()
+        assert not j["ab"].any().item()
+        alone.append(j["out"].clone())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rnd in range(3):
+        for j in jobs:
+            j["out"].fill_(float("nan"))
+            j["ab"].fill_(0xA5)
+        torch.cuda.synchronize()
+        for _ in range(4):                   # the two streams' launches interleave
+            for j, s in zip(jobs, streams):
+                run(j, stream=s)
+        torch.cuda.synchronize()
+        for j, ref in zip(jobs, alone):
+            assert not j["ab"].any().item()
+            assert torch.equal(j["out"], ref), f"round {rnd}: hq {j['hq']}"
+            assert int(j["vws"].count_nonzero()) == 0
+    want = _edge_oracle(jobs[0]["e"], "fp8", jobs[0]["e"]["lens"])
+    helpers.check_attention(alone[0].cpu().numpy(), want, label="two streams, job 0")
