@@ -189,7 +189,7 @@ def cpu_baseline(args, wl, scales, step_index):
         paged.append_fp8(kp2, vp2, kn, vn, np.array([0]), np.array([L - 1]), bt, ks, vs, ab)
         paged.decode_attn(q, kp2, vp2, ks, vs, bt, np.array([L], np.int32), sm, "fp8", ab)
 
-    # one thread per usable core (at most 16, the machine's CPU share), each with BLAS
+    # one thread per usable core (at most 16: a host's CPU share per GPU), each with BLAS
     # at one thread; numpy releases the GIL in the oracle's array work. Each
     # thread runs the sampled requests in turn for the same wall-clock window.
     try:
@@ -302,7 +302,7 @@ def _back_to_back_ms(fn, reps, per=8):
 
 
 def stream_read_peak(reps=10):
-    """Streaming-read rate of this box through the library's own grid-stride
+    """Streaming-read rate of this GPU through the library's own grid-stride
     read kernel (the prefill amax pass, 16-byte loads, no writes) over 2 GiB:
     the plain-read ceiling the paged kernels can be compared with (the
     roofline fraction itself stays against the published 8 TB/s)."""
